@@ -1,0 +1,397 @@
+/*
+ * SSTA CPU oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, sequential C for what the Selective and Sliding Tile Attention
+ * (SSTA) forward computes.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header or table with the GPU library.
+ *
+ * Sources (cited by page and section):
+ *   [TR]   "HunyuanVideo 1.5 Technical Report" summary page, section
+ *          "SSTA: Selective and Sliding Tile Attention": the attention
+ *          equation, Step 1 (3D block partition, block count B), Step 2
+ *          (Score_s, Score_r, Score_i, Topk, Indexes2mask), Step 3 (M_sta),
+ *          Step 4 (mask combination, flex_block_attention).
+ *   [BLOG] "HunyuanVideo-1.5: An 8.3B-Parameter Video Diffusion Model Built
+ *          for Consumer GPUs", section "Under the Hood: SSTA and Muon in
+ *          Detail": the importance_sampling code excerpt (cosine
+ *          normalisation, (x+1)/2 map, diagonal-excluded mean redundancy,
+ *          lambda = 0.9 with beta = 1 - lambda, top-k clamped to the block
+ *          count, unsorted top-k).
+ *
+ * Floating-point rules (the pages fix no order; these are the readings):
+ *   - scoring runs in fp32 with every operation written out: dot products
+ *     are fmaf chains over the channel index in ascending order starting at
+ *     0.0f; sqrtf and '/' are IEEE correctly rounded; nothing is contracted
+ *     (compile with -ffp-contract=off);
+ *   - tile means are fp32 sums over the in-tile token index in ascending
+ *     order, divided by the token count;
+ *   - attention uses the exact fp32 widening of the bf16 inputs, fp64
+ *     accumulation and a two-pass softmax (max, then sum).
+ *
+ * Parity pins: every function here is pinned by tests (closed forms,
+ * brute force, library special cases); see the tests for each.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+  int32_t batch, heads, head_dim;
+  int32_t T, H, W;
+  int32_t tile_t, tile_h, tile_w;
+} orc_geom;
+
+enum { ORC_COMBINE_AND = 1u << 0, ORC_TOPK_EXCLUDE_WINDOW = 1u << 1 };
+
+static float bf16_to_f32(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+static int64_t tiles_t(const orc_geom* g) { return g->T / g->tile_t; }
+static int64_t tiles_h(const orc_geom* g) { return g->H / g->tile_h; }
+static int64_t tiles_w(const orc_geom* g) { return g->W / g->tile_w; }
+
+/* [TR] Step 1: block count = (F/tile_t)(H/tile_h)(W/tile_w). */
+int64_t orc_n_tiles(const orc_geom* g) { return tiles_t(g) * tiles_h(g) * tiles_w(g); }
+
+int32_t orc_tile_tokens(const orc_geom* g) { return g->tile_t * g->tile_h * g->tile_w; }
+
+/*
+ * [TR] Step 1: tokens are grouped into contiguous 3D blocks.
+ * Reading: blocks are numbered row-major over the (t, h, w) block grid and
+ * tokens inside a block row-major over (t, h, w); token n = (t*H + y)*W + x.
+ */
+void orc_token_to_tile(const orc_geom* g, int64_t n, int64_t* tile, int32_t* r) {
+  const int64_t t = n / ((int64_t)g->H * g->W);
+  const int64_t y = (n / g->W) % g->H;
+  const int64_t x = n % g->W;
+  *tile = ((t / g->tile_t) * tiles_h(g) + (y / g->tile_h)) * tiles_w(g) + (x / g->tile_w);
+  *r = (int32_t)(((t % g->tile_t) * g->tile_h + (y % g->tile_h)) * g->tile_w + (x % g->tile_w));
+}
+
+/* Inverse map: the token index of in-tile position r of tile `tile`. */
+int64_t orc_tile_to_token(const orc_geom* g, int64_t tile, int32_t r) {
+  const int64_t bt = tile / (tiles_h(g) * tiles_w(g));
+  const int64_t by = (tile / tiles_w(g)) % tiles_h(g);
+  const int64_t bx = tile % tiles_w(g);
+  const int64_t it = r / (g->tile_h * g->tile_w);
+  const int64_t iy = (r / g->tile_w) % g->tile_h;
+  const int64_t ix = r % g->tile_w;
+  const int64_t t = bt * g->tile_t + it, y = by * g->tile_h + iy, x = bx * g->tile_w + ix;
+  return (t * g->H + y) * g->W + x;
+}
+
+/* Gather x[b,h,N,D] (bf16 bits) into tile-major x_t[b,h,n_tiles,tile_tokens,D]. */
+void orc_permute(const orc_geom* g, const uint16_t* x, uint16_t* x_t) {
+  const int64_t N = (int64_t)g->T * g->H * g->W, D = g->head_dim;
+  const int64_t BH = (int64_t)g->batch * g->heads;
+  for (int64_t bh = 0; bh < BH; ++bh)
+    for (int64_t n = 0; n < N; ++n) {
+      int64_t tile;
+      int32_t r;
+      orc_token_to_tile(g, n, &tile, &r);
+      memcpy(x_t + ((bh * orc_n_tiles(g) + tile) * orc_tile_tokens(g) + r) * D,
+             x + (bh * N + n) * D, (size_t)D * sizeof(uint16_t));
+    }
+}
+
+/*
+ * [TR] Step 2: pooled (average) block representation.
+ * pooled[b,h,i,d] = (sum over r = 0..tile_tokens-1, ascending, in fp32, of
+ * x[token(i, r), d]) / tile_tokens.
+ */
+void orc_pool(const orc_geom* g, const uint16_t* x, float* pooled) {
+  const int64_t N = (int64_t)g->T * g->H * g->W, D = g->head_dim;
+  const int64_t BH = (int64_t)g->batch * g->heads, NT = orc_n_tiles(g);
+  const int32_t R = orc_tile_tokens(g);
+#pragma omp parallel for schedule(static)
+  for (int64_t bhi = 0; bhi < BH * NT; ++bhi) {
+    const int64_t bh = bhi / NT, i = bhi % NT;
+    float s[1024];
+    for (int64_t d = 0; d < D; ++d) s[d] = 0.0f;
+    for (int32_t r = 0; r < R; ++r) {
+      const uint16_t* row = x + (bh * N + orc_tile_to_token(g, i, r)) * D;
+      for (int64_t d = 0; d < D; ++d) s[d] = s[d] + bf16_to_f32(row[d]);
+    }
+    for (int64_t d = 0; d < D; ++d) pooled[bhi * D + d] = s[d] / (float)R;
+  }
+}
+
+/*
+ * [BLOG] importance_sampling: each pooled vector is divided by its L2 norm.
+ * ss = fmaf chain of p[d]*p[d] over ascending d; nrm = sqrtf(ss);
+ * out[d] = p[d] / nrm.  Reading: a zero vector stays zero (the pages do
+ * not cover it; the excerpt would produce NaN).
+ */
+void orc_normalize(int64_t rows, int32_t D, const float* p, float* out) {
+  for (int64_t i = 0; i < rows; ++i) {
+    const float* v = p + i * D;
+    float ss = 0.0f;
+    for (int32_t d = 0; d < D; ++d) ss = fmaf(v[d], v[d], ss);
+    const float nrm = sqrtf(ss);
+    for (int32_t d = 0; d < D; ++d) out[i * D + d] = (nrm == 0.0f) ? 0.0f : v[d] / nrm;
+  }
+}
+
+static float dot_f32(const float* a, const float* b, int32_t D) {
+  float s = 0.0f;
+  for (int32_t d = 0; d < D; ++d) s = fmaf(a[d], b[d], s);
+  return s;
+}
+
+/*
+ * [TR] Step 2, Score_r; [BLOG] gate_unique with the diagonal removed and a
+ * mean over the remaining key blocks.
+ * u(i, j) = (khat_i . khat_j + 1) * 0.5;
+ * red[j] = (sum over i != j, ascending i, fp32, of u(i, j)) / (n - 1);
+ * red = 0 when n == 1.  Reading: the normaliser counts key blocks (n - 1);
+ * the summary page's "N - 1" reuses the letter it gave the block size.
+ */
+void orc_redundancy(int64_t BH, int64_t n, int32_t D, const float* khat, float* red) {
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t bhj = 0; bhj < BH * n; ++bhj) {
+    const int64_t bh = bhj / n, j = bhj % n;
+    const float* kb = khat + bh * n * D;
+    float s = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+      if (i == j) continue;
+      const float u = (dot_f32(kb + i * D, kb + j * D, D) + 1.0f) * 0.5f;
+      s = s + u;
+    }
+    red[bhj] = (n > 1) ? s / (float)(n - 1) : 0.0f;
+  }
+}
+
+/*
+ * [TR] Step 2, Score_s and Score_i; [BLOG] gate_similarity and
+ * importance_scores.
+ * g(i, j) = (qhat_i . khat_j + 1) * 0.5;
+ * score(i, j) = (lambda * g(i, j)) - (beta * red[j]), two rounded products
+ * and one rounded difference.
+ */
+void orc_scores(int64_t BH, int64_t n, int32_t D, const float* qhat, const float* khat,
+                const float* red, float lambda_, float beta, float* scores) {
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t bhi = 0; bhi < BH * n; ++bhi) {
+    const int64_t bh = bhi / n;
+    const float* q = qhat + bhi * D;
+    for (int64_t j = 0; j < n; ++j) {
+      const float gs = (dot_f32(q, khat + (bh * n + j) * D, D) + 1.0f) * 0.5f;
+      const float a = lambda_ * gs;
+      const float b = beta * red[bh * n + j];
+      scores[bhi * n + j] = a - b;
+    }
+  }
+}
+
+/* [TR] Step 3: the sliding-tile window.  WS = 2*half + 1 blocks per axis,
+ * centred on the query block.  Reading: clipped at the grid edge (no wrap,
+ * no shift).  Writes the window's block ids in ascending order; returns the
+ * count. */
+int32_t orc_window(const orc_geom* g, int32_t wt, int32_t wh, int32_t ww, int64_t i, int32_t* out) {
+  const int64_t nt = tiles_t(g), ny = tiles_h(g), nx = tiles_w(g);
+  const int64_t ti = i / (ny * nx), yi = (i / nx) % ny, xi = i % nx;
+  int32_t c = 0;
+  for (int64_t t = 0; t < nt; ++t) {
+    if (llabs(t - ti) > wt) continue;
+    for (int64_t y = 0; y < ny; ++y) {
+      if (llabs(y - yi) > wh) continue;
+      for (int64_t x = 0; x < nx; ++x) {
+        if (llabs(x - xi) > ww) continue;
+        out[c++] = (int32_t)((t * ny + y) * nx + x);
+      }
+    }
+  }
+  return c;
+}
+
+typedef struct { float s; int32_t j; } scored;
+
+/* Higher score first; equal scores (IEEE ==, so -0 == +0): lower block id first. */
+static int cmp_scored(const void* a, const void* b) {
+  const scored* x = (const scored*)a;
+  const scored* y = (const scored*)b;
+  if (x->s > y->s) return -1;
+  if (x->s < y->s) return 1;
+  return (x->j < y->j) ? -1 : (x->j > y->j);
+}
+
+static int cmp_i32(const void* a, const void* b) {
+  const int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return (x > y) - (x < y);
+}
+
+/*
+ * [TR] Step 2, Topk; [BLOG] topk clamped to the number of key blocks.
+ * For each query-block row: sort all n candidates by (score descending,
+ * block id ascending) and keep the first k_eff; output in ascending block
+ * id (the pages leave the order unspecified).  With exclude_window != 0,
+ * window blocks of the row (given per row by `geom`/win) are not
+ * candidates.  idx_out has room for k_out entries per row; rows with fewer
+ * candidates are padded with -1.  Returns 0, or -1 on a bad argument.
+ */
+int orc_topk(const orc_geom* g, int32_t wt, int32_t wh, int32_t ww, int32_t exclude_window,
+             int64_t BH, int64_t n, const float* scores, int32_t k, int32_t k_out,
+             int32_t* idx_out) {
+  if (k < 0 || k_out < 0) return -1;
+  int failed = 0;
+#pragma omp parallel
+  {
+    scored* buf = (scored*)malloc(sizeof(scored) * (size_t)(n > 0 ? n : 1));
+    int32_t* win = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+    char* inwin = (char*)calloc((size_t)(n > 0 ? n : 1), 1);
+    if (!buf || !win || !inwin) failed = 1;
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t row = 0; row < BH * n; ++row) {
+      if (failed) continue;
+      const int64_t i = row % n;
+      int32_t nw = 0;
+      if (exclude_window) {
+        nw = orc_window(g, wt, wh, ww, i, win);
+        for (int32_t a = 0; a < nw; ++a) inwin[win[a]] = 1;
+      }
+      int64_t m = 0;
+      for (int64_t j = 0; j < n; ++j) {
+        if (exclude_window && inwin[j]) continue;
+        buf[m].s = scores[row * n + j];
+        buf[m].j = (int32_t)j;
+        ++m;
+      }
+      if (exclude_window)
+        for (int32_t a = 0; a < nw; ++a) inwin[win[a]] = 0;
+      qsort(buf, (size_t)m, sizeof(scored), cmp_scored);
+      int64_t keep = k < m ? k : m;
+      if (keep > k_out) keep = k_out;
+      int32_t* o = idx_out + row * (int64_t)k_out;
+      for (int64_t a = 0; a < keep; ++a) o[a] = buf[a].j;
+      qsort(o, (size_t)keep, sizeof(int32_t), cmp_i32);
+      for (int64_t a = keep; a < k_out; ++a) o[a] = -1;
+    }
+    free(buf);
+    free(win);
+    free(inwin);
+  }
+  return failed ? -1 : 0;
+}
+
+/*
+ * [TR] Step 4: combine the per-head selected blocks with the shared window.
+ * Reading: union (ORC_COMBINE_AND gives the intersection that Algorithm 1
+ * prints).  kv_idx rows are ascending and padded with -1 to max_kept;
+ * kv_cnt holds the row length.  bitmask (nullable) gets bit j%32 of word
+ * j/32 set for every kept block j, words per row = ceil(n/32).
+ * Returns 0, or -1 if a row would exceed max_kept.
+ */
+int orc_build_lists(const orc_geom* g, int32_t wt, int32_t wh, int32_t ww, uint32_t flags,
+                    const int32_t* topk_idx, int32_t k_stride, int32_t max_kept,
+                    int32_t* kv_idx, int32_t* kv_cnt, uint32_t* bitmask) {
+  const int64_t n = orc_n_tiles(g), BH = (int64_t)g->batch * g->heads;
+  const int64_t words = (n + 31) / 32;
+  int bad = 0;
+  char* mark = (char*)calloc((size_t)n, 1);
+  char* wmark = (char*)calloc((size_t)n, 1);
+  int32_t* win = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+  if (!mark || !wmark || !win) { free(mark); free(wmark); free(win); return -1; }
+  for (int64_t row = 0; row < BH * n; ++row) {
+    const int64_t i = row % n;
+    const int32_t nw = orc_window(g, wt, wh, ww, i, win);
+    for (int32_t a = 0; a < nw; ++a) wmark[win[a]] = 1;
+    for (int32_t a = 0; a < k_stride; ++a) {
+      const int32_t j = topk_idx[row * k_stride + a];
+      if (j < 0) continue;
+      if (flags & ORC_COMBINE_AND) { if (wmark[j]) mark[j] = 1; }
+      else mark[j] = 1;
+    }
+    if (!(flags & ORC_COMBINE_AND))
+      for (int32_t a = 0; a < nw; ++a) mark[win[a]] = 1;
+    int32_t c = 0;
+    for (int64_t j = 0; j < n; ++j) {
+      if (!mark[j]) continue;
+      if (c >= max_kept) { bad = 1; break; }
+      kv_idx[row * max_kept + c++] = (int32_t)j;
+    }
+    for (int32_t a = c; a < max_kept; ++a) kv_idx[row * max_kept + a] = -1;
+    kv_cnt[row] = c;
+    if (bitmask) {
+      uint32_t* bm = bitmask + row * words;
+      for (int64_t w = 0; w < words; ++w) bm[w] = 0;
+      for (int64_t j = 0; j < n; ++j)
+        if (mark[j]) bm[j / 32] |= 1u << (j % 32);
+    }
+    for (int64_t j = 0; j < n; ++j) { mark[j] = 0; wmark[j] = 0; }
+    if (bad) break;
+  }
+  free(mark);
+  free(wmark);
+  free(win);
+  return bad ? -1 : 0;
+}
+
+/*
+ * [TR] the attention equation and Step 4 (flex_block_attention): softmax of
+ * scale * q.k over the keys of the kept blocks only, then the weighted sum
+ * of their values; full attention inside a kept block (Step 1).
+ * For each selected row (b*heads + h)*n_tiles + i, writes o[sel][r][d] for
+ * the query at in-tile position r (fp64) and lse[sel][r] = log sum exp.
+ * Inputs are token-major bf16 bits [b, h, N, D].  An empty kept list gives
+ * o = 0 and lse = -inf.
+ */
+void orc_attention(const orc_geom* g, double scale, const uint16_t* q, const uint16_t* k,
+                   const uint16_t* v, const int32_t* kv_idx, const int32_t* kv_cnt,
+                   int32_t max_kept, int64_t n_sel, const int64_t* sel_rows, double* o_out,
+                   double* lse_out) {
+  const int64_t N = (int64_t)g->T * g->H * g->W, D = g->head_dim, n = orc_n_tiles(g);
+  const int32_t R = orc_tile_tokens(g);
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)max_kept * R + 8);
+    double* qv = (double*)malloc(sizeof(double) * (size_t)D);
+    int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)max_kept * R + 8);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t a = 0; a < n_sel; ++a) {
+      const int64_t row = sel_rows[a], bh = row / n, i = row % n;
+      const int32_t cnt = kv_cnt[row];
+      int64_t m = 0;
+      for (int32_t c = 0; c < cnt; ++c) {
+        const int32_t j = kv_idx[row * max_kept + c];
+        for (int32_t rr = 0; rr < R; ++rr) keys[m++] = orc_tile_to_token(g, j, rr);
+      }
+      for (int32_t r = 0; r < R; ++r) {
+        const int64_t nq = orc_tile_to_token(g, i, r);
+        double* o = o_out + (a * R + r) * D;
+        for (int64_t d = 0; d < D; ++d) {
+          qv[d] = (double)bf16_to_f32(q[(bh * N + nq) * D + d]);
+          o[d] = 0.0;
+        }
+        if (m == 0) { lse_out[a * R + r] = -INFINITY; continue; }
+        double mx = -INFINITY;
+        for (int64_t t = 0; t < m; ++t) {
+          const uint16_t* kr = k + (bh * N + keys[t]) * D;
+          double acc = 0.0;
+          for (int64_t d = 0; d < D; ++d) acc += qv[d] * (double)bf16_to_f32(kr[d]);
+          s[t] = acc * scale;
+          if (s[t] > mx) mx = s[t];
+        }
+        double l = 0.0;
+        for (int64_t t = 0; t < m; ++t) {
+          s[t] = exp(s[t] - mx);
+          l += s[t];
+        }
+        for (int64_t t = 0; t < m; ++t) {
+          const uint16_t* vr = v + (bh * N + keys[t]) * D;
+          const double p = s[t] / l;
+          for (int64_t d = 0; d < D; ++d) o[d] += p * (double)bf16_to_f32(vr[d]);
+        }
+        lse_out[a * R + r] = mx + log(l);
+      }
+    }
+    free(s);
+    free(qv);
+    free(keys);
+  }
+}
