@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""SSTA forward benchmark on one MI355X.
+
+One step = the whole SSTA forward on one batch of synthetic inputs already
+resident in HBM: tile/pool Q, K, V -> scores + top-k -> window/union lists ->
+block-sparse attention -> unpermute O.  W untimed warm-up steps, then K timed
+steps between device synchronisations.  Prints one JSON line.
+
+  value  = effective TFLOP/s on kept blocks over the whole step
+           (kept (query block, key block) pairs x 4*128^3 FLOP / step time)
+  roofline: the attention kernel (the dominant kernel), achieved TFLOP/s from
+           HIP events recorded around its launches on the launch stream, vs the
+           dense bf16 MFMA peak of 2.5 PFLOP/s
+  speedup vs dense: the same pipeline with every block kept (dense attention)
+  cpu_baseline: the CPU oracle on a bounded sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SSTA fwd effective TFLOP/s on kept blocks (% bf16 MFMA peak) + speedup vs dense"
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+FLOP_PER_PAIR = 4 * 128 ** 3       # Q.K^T and P.V for one 128x128 block pair
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="720p-10s")
+    ap.add_argument("--dense-steps", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1800,
+                    help="query-block rows of head 0 in the CPU oracle sample")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM bytes per attention launch measured with rocprofv3 counters")
+    return ap.parse_args()
+
+
+def load_traffic(path, workload, kernel_hash):
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = t.get(workload)
+    if not ent or ent.get("kernel_source_sha256") != kernel_hash:
+        return None           # counters taken on another version of the kernel
+    return ent.get("attn_bytes_per_launch")
+
+
+def kernel_hash():
+    import hashlib
+    p = os.path.join(ROOT, "video_dit_block_tile_amd", "csrc", "k_attn.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def cpu_baseline(wl, q, k, v, rows_wanted):
+    """Oracle (as is) on a bounded sample: the selection for head 0 and the
+    attention of `rows_wanted` query blocks of head 0."""
+    import numpy as np
+    import oracle
+
+    wl1 = wl.with_(heads=1, batch=1)
+    q1, k1, v1 = (np.ascontiguousarray(x[:1, :1]) for x in (q, k, v))
+    t0 = time.perf_counter()
+    sel = oracle.select(wl1, q1, k1)
+    t_sel = time.perf_counter() - t0
+    n = wl1.n_tiles
+    rows = np.linspace(0, n - 1, num=min(rows_wanted, n)).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.attention(wl1, q1, k1, v1, sel["kv_idx"], sel["kv_cnt"], rows)
+    t_att = time.perf_counter() - t0
+    pairs = int(sel["kv_cnt"].reshape(-1)[rows].sum())
+    t = t_att + t_sel * len(rows) / n            # selection prorated to the sampled rows
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {
+        "value": pairs * FLOP_PER_PAIR / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": ("%s head 0: full selection (%.1f s, prorated to the sampled rows) + fp64 "
+                   "attention of %d of %d query blocks (%d kept pairs, %.1f s)"
+                   % (wl.name, t_sel, len(rows), n, pairs, t_att)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the SSTA forward shards by heads with no "
+              "communication inside it, so a multi-GPU figure is N independent copies; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synthetic_inputs as si
+    import video_dit_block_tile_amd as m
+
+    wl = si.ALL[args.workload]
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    q, k, v = si.make_qkv(wl)
+    gen_s = time.perf_counter() - t0
+    print("[bench] %s inputs generated in %.1f s" % (wl.name, gen_s), file=sys.stderr, flush=True)
+
+    def dev(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    g = m.make_geom(wl.batch, wl.heads, wl.T, wl.H, wl.W, tile=wl.tile)
+    p = m.make_params(win=wl.win, topk=wl.topk)
+    plan = m.SstaPlan(g, p)
+    stream = torch.cuda.current_stream()
+
+    phases = ("tile_pool", "select", "attention", "unpermute")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        plan.tile_pool(qd, kd, vd)
+        if ev is not None:
+            ev[1].record(stream)
+        plan.select()
+        if ev is not None:
+            ev[2].record(stream)
+        plan.attend()
+        if ev is not None:
+            ev[3].record(stream)
+        plan.unpermute()
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    phase_ms = {ph: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1])
+                                   for i in range(args.steps)]))
+                for j, ph in enumerate(phases)}
+    pairs = int(plan.kv_cnt.sum().item())
+    n = wl.n_tiles
+    total_pairs = wl.batch * wl.heads * n * n
+    flop = pairs * FLOP_PER_PAIR
+    value = flop / (ms_step * 1e-3) / 1e12
+    attn_tflops = flop / (phase_ms["attention"] * 1e-3) / 1e12
+    print("[bench] sparse step %.3f ms, attention %.3f ms (%.1f TFLOP/s)"
+          % (ms_step, phase_ms["attention"], attn_tflops), file=sys.stderr, flush=True)
+
+    # Dense reference: the same pipeline with every block kept.
+    dense_ms = dense_attn_ms = None
+    if args.dense_steps > 0:
+        dplan = m.SstaPlan(g, p, dense=True)
+        dplan.run(qd, kd, vd)
+        torch.cuda.synchronize()
+        de = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+              for _ in range(args.dense_steps)]
+        t0 = time.perf_counter()
+        for i in range(args.dense_steps):
+            dplan.tile_pool(qd, kd, vd)
+            de[i][0].record(stream)
+            dplan.attend()
+            de[i][1].record(stream)
+            dplan.unpermute()
+        torch.cuda.synchronize()
+        dense_ms = (time.perf_counter() - t0) * 1e3 / args.dense_steps
+        dense_attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in de]))
+        print("[bench] dense step %.1f ms, attention %.1f ms" % (dense_ms, dense_attn_ms),
+              file=sys.stderr, flush=True)
+
+    traffic = load_traffic(args.traffic_json, wl.name, kernel_hash())
+    roof = {
+        "kernel": "k_attn_fwd",
+        "bound": "mfma",
+        "achieved": round(attn_tflops, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "traffic": traffic,
+        "algorithmic_flop_per_launch": flop,
+        "avg_launch_ms": round(phase_ms["attention"], 4),
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, q, k, v, args.cpu_rows)
+
+    pool_bytes = 6 * wl.batch * wl.heads * wl.n_tokens * 128 * 2 + \
+        2 * wl.batch * wl.heads * n * 128 * 4
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "batch": wl.batch, "heads": wl.heads, "head_dim": wl.head_dim,
+            "grid": [wl.T, wl.H, wl.W], "tile": list(wl.tile), "window_half": list(wl.win),
+            "topk": wl.topk, "n_tiles": n, "seq_len": wl.n_tokens,
+            "input": "smooth 3D sinusoid field + N(0, 0.5^2) noise, bf16, seed %d" % wl.seed,
+        },
+        "pct_bf16_peak_step": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "attention_tflops": round(attn_tflops, 2),
+        "pct_bf16_peak_attention": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+        "kept_pairs": pairs,
+        "kept_fraction": round(pairs / total_pairs, 5),
+        "phase_ms": {kk: round(vv, 4) for kk, vv in phase_ms.items()},
+        "tile_pool_gbs": round(pool_bytes / (phase_ms["tile_pool"] * 1e-3) / 1e9, 1),
+        "dense_ms_per_step": None if dense_ms is None else round(dense_ms, 3),
+        "dense_attention_ms": None if dense_attn_ms is None else round(dense_attn_ms, 3),
+        "speedup_vs_dense_step": None if dense_ms is None else round(dense_ms / ms_step, 3),
+        "speedup_vs_dense_attention": (None if dense_attn_ms is None
+                                       else round(dense_attn_ms / phase_ms["attention"], 3)),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,186 @@
+/*
+ * ssta.h -- C ABI of the MI355X (gfx950) SSTA forward library, libssta.so.
+ *
+ * Selective and Sliding Tile Attention (SSTA) forward, as described on the
+ * "HunyuanVideo 1.5 Technical Report" summary page, section "SSTA: Selective
+ * and Sliding Tile Attention" (Steps 1-4), with the scoring details of the
+ * importance_sampling excerpt on the "HunyuanVideo-1.5: An 8.3B-Parameter
+ * Video Diffusion Model Built for Consumer GPUs" page, section "Under the
+ * Hood: SSTA and Muon in Detail".
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are device pointers, allocated and owned by the caller.  The
+ *     library never allocates, frees or keeps device memory between calls.
+ *   - Tensor pointers must be 16-byte aligned and densely packed in the
+ *     layout stated for them.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  All
+ *     device work is enqueued on it; no call synchronises the host.
+ *   - Every call returns an ssta_status (0 = success).  Arguments are
+ *     checked on the host before any HIP call, so a rejected call has
+ *     enqueued nothing.  Faults inside kernels surface at the caller's next
+ *     synchronisation.  There is no fallback path: if the current device is
+ *     missing or is not gfx950 the call fails with SSTA_ERR_NO_DEVICE or
+ *     SSTA_ERR_ARCH.
+ *   - Tokens of a clip are numbered n = (t*H + y)*W + x.  Blocks ("tiles")
+ *     are numbered row-major over the (T/tile_t, H/tile_h, W/tile_w) block
+ *     grid, and the tokens of one block row-major over (tile_t, tile_h,
+ *     tile_w).  n_tiles = (T/tile_t)(H/tile_h)(W/tile_w)  (Step 1).
+ *   - Current limits: head_dim == 128, tile_t*tile_h*tile_w == 128 tokens,
+ *     tile sizes divide T, H, W; ssta_score_select needs n_tiles <= 4096.
+ */
+#ifndef SSTA_H
+#define SSTA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ssta_status {
+  SSTA_OK = 0,
+  SSTA_ERR_ARG = -1,        /* null pointer, negative size, non-finite weight, unknown flag */
+  SSTA_ERR_SHAPE = -2,      /* unsupported geometry (see limits above) or size overflow */
+  SSTA_ERR_ALIGN = -3,      /* a tensor pointer is not 16-byte aligned */
+  SSTA_ERR_NO_DEVICE = -4,  /* no HIP device is usable */
+  SSTA_ERR_ARCH = -5,       /* the current device is not gfx950 */
+  SSTA_ERR_HIP = -6,        /* a HIP launch failed; see ssta_last_hip_error() */
+  SSTA_ERR_WORKSPACE = -7   /* workspace missing or smaller than ssta_workspace_bytes() */
+} ssta_status;
+
+/* Clip geometry.  All fields >= 1. */
+typedef struct ssta_geom {
+  int32_t batch, heads, head_dim;   /* head_dim must be 128 */
+  int32_t T, H, W;                  /* latent grid, tokens row-major (t, y, x) */
+  int32_t tile_t, tile_h, tile_w;   /* block size; divides the grid; product 128 */
+} ssta_geom_t;
+
+/* Selection and attention parameters. */
+typedef struct ssta_params {
+  int32_t win_t, win_h, win_w;  /* window half-widths in blocks (>= 0): a block j is in
+                                   the window of block i when its block coordinates differ
+                                   by at most these on every axis; clipped at the grid edge
+                                   (Step 3, window size 2*half+1 per axis) */
+  int32_t topk;                 /* >= 0; blocks selected per query block, clamped to the
+                                   number of candidates (Step 2, Topk) */
+  float lambda_, beta;          /* Score_i = lambda_*Score_s - beta*Score_r (Step 2);
+                                   the excerpt's defaults are 0.9f and 0.1f */
+  float scale;                  /* softmax scale, > 0; 1/sqrt(head_dim) in the attention
+                                   equation */
+  uint32_t flags;               /* SSTA_* flags below */
+} ssta_params_t;
+
+/* Step 4 prints the combination as a logical AND; the default is the union of
+ * window and selection.  With this flag the kept set is their intersection
+ * (a query block may then keep nothing: its output is 0 and its LSE -inf). */
+#define SSTA_COMBINE_AND (1u << 0)
+/* Select the top-k among the blocks outside the query block's window. */
+#define SSTA_TOPK_EXCLUDE_WINDOW (1u << 1)
+
+/* Layouts of a tiled tensor written by ssta_tile_pool. */
+#define SSTA_LAYOUT_TOKEN_MAJOR 0   /* [batch, heads, n_tiles, tile_tokens, head_dim] */
+#define SSTA_LAYOUT_DIM_MAJOR 1     /* [batch, heads, n_tiles, head_dim, tile_tokens] */
+
+/*
+ * Step 1 (3D block partition) and the block means of Step 2.
+ *   x       in : bf16 [batch, heads, T*H*W, head_dim], token-major.
+ *   x_tiled out: bf16, the same values gathered block by block in `layout`
+ *                (SSTA_LAYOUT_*); NULL to skip.
+ *   pooled  out: fp32 [batch, heads, n_tiles, head_dim], the mean of each
+ *                block's tokens: the fp32 sum over in-block tokens in
+ *                ascending order divided by the token count; NULL to skip.
+ * At least one of x_tiled and pooled must be non-NULL.
+ */
+int ssta_tile_pool(const ssta_geom_t* g, const void* x, void* x_tiled, int32_t layout,
+                   float* pooled, void* stream);
+
+/*
+ * Inverse of the token-major gather: x_tiled bf16 [batch, heads, n_tiles,
+ * tile_tokens, head_dim] -> x bf16 [batch, heads, T*H*W, head_dim].
+ */
+int ssta_tile_unpermute(const ssta_geom_t* g, const void* x_tiled, void* x, void* stream);
+
+/* Width of each row of topk_idx: min(topk, n_tiles), or with
+ * SSTA_TOPK_EXCLUDE_WINDOW min(topk, n_tiles - smallest window).  < 0 on a bad argument. */
+int32_t ssta_topk_width(const ssta_geom_t* g, const ssta_params_t* p);
+
+/* Row capacity of kv_idx: min(n_tiles, largest window + topk width), or with
+ * SSTA_COMBINE_AND min(largest window, topk width).  < 0 on a bad argument. */
+int32_t ssta_max_kept(const ssta_geom_t* g, const ssta_params_t* p);
+
+/* Device workspace bytes that ssta_score_select and ssta_scores need.  < 0 on a bad argument. */
+int64_t ssta_workspace_bytes(const ssta_geom_t* g, const ssta_params_t* p);
+
+/*
+ * Step 2 (selective mask): importance scores and per-query-block top-k.
+ *   q_pooled, k_pooled in: fp32 [batch, heads, n_tiles, head_dim] block means.
+ *   topk_idx out: int32 [batch, heads, n_tiles, ssta_topk_width()], the
+ *                 selected key blocks of every query block in ascending id,
+ *                 -1 padded when a row has fewer candidates than the width.
+ *   workspace: device scratch of ws_bytes >= ssta_workspace_bytes().
+ * Scores: qhat = q/|q|, khat = k/|k| (fp32, correctly rounded sqrt and
+ * division; a zero vector stays zero); Score_s(i,j) = (qhat_i.khat_j+1)/2;
+ * Score_r(j) = mean over key blocks i != j of (khat_i.khat_j+1)/2;
+ * Score_i = lambda_*Score_s - beta*Score_r.  Every dot product is an fp32
+ * fused-multiply-add chain in ascending channel order, the redundancy sum
+ * runs in ascending i, and nothing else is fused, so the selection is a
+ * deterministic function of the inputs.  Ties go to the lower block id.
+ */
+int ssta_score_select(const ssta_geom_t* g, const ssta_params_t* p, const float* q_pooled,
+                      const float* k_pooled, int32_t* topk_idx, void* workspace,
+                      size_t ws_bytes, void* stream);
+
+/*
+ * Inspection entry point for the same scoring: writes the full fp32
+ * Score_i matrix scores [batch, heads, n_tiles, n_tiles] (row = query block)
+ * and, if non-NULL, red [batch, heads, n_tiles] (Score_r).
+ */
+int ssta_scores(const ssta_geom_t* g, const ssta_params_t* p, const float* q_pooled,
+                const float* k_pooled, float* scores, float* red, void* workspace,
+                size_t ws_bytes, void* stream);
+
+/*
+ * Step 3 (sliding-tile window) and Step 4 (mask combination).
+ *   topk_idx in : int32 [batch, heads, n_tiles, ssta_topk_width()] as written by
+ *                 ssta_score_select (ascending, -1 padded).
+ *   kv_idx  out : int32 [batch, heads, n_tiles, ssta_max_kept()], the kept key
+ *                 blocks of each query block in ascending id, -1 padded.
+ *   kv_cnt  out : int32 [batch, heads, n_tiles], number of kept blocks.
+ *   bitmask out : uint32 [batch, heads, n_tiles, ceil(n_tiles/32)], bit j%32 of
+ *                 word j/32 set iff block j is kept; NULL to skip.
+ */
+int ssta_build_mask(const ssta_geom_t* g, const ssta_params_t* p, const int32_t* topk_idx,
+                    int32_t* kv_idx, int32_t* kv_cnt, uint32_t* bitmask, void* stream);
+
+/*
+ * Step 4 (block-sparse attention): for every query token of block i, softmax
+ * of scale*q.k over the tokens of the kept key blocks of i only, then the
+ * weighted sum of their values; full attention inside a kept block.
+ *   q_t, k_t in : bf16 [batch, heads, n_tiles, tile_tokens, head_dim] (token-major tiles).
+ *   v_t      in : bf16 [batch, heads, n_tiles, head_dim, tile_tokens] (dim-major tiles).
+ *   kv_idx, kv_cnt in: as written by ssta_build_mask; kv_idx row stride max_kept
+ *                 (>= 1).  Pass kv_idx = kv_cnt = NULL and max_kept = 0 for dense
+ *                 attention (every block kept).
+ *   o_t     out : bf16 [batch, heads, n_tiles, tile_tokens, head_dim] (token-major tiles).
+ *   lse     out : fp32 [batch, heads, n_tiles, tile_tokens], natural-log
+ *                 log-sum-exp of the scaled scores; NULL to skip.
+ * Arithmetic: bf16 products on the matrix cores, fp32 accumulation, fp32
+ * online softmax.  A row with no kept block yields o = 0, lse = -inf.
+ */
+int ssta_attention_fwd(const ssta_geom_t* g, const ssta_params_t* p, const void* q_t,
+                       const void* k_t, const void* v_t, const int32_t* kv_idx,
+                       const int32_t* kv_cnt, int32_t max_kept, void* o_t, float* lse,
+                       void* stream);
+
+/* Static text for a status code. */
+const char* ssta_status_string(int status);
+
+/* The hipError_t of the last SSTA_ERR_HIP on this thread (0 if none). */
+int ssta_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSTA_H */

@@ -1,0 +1,138 @@
+"""The C ABI on the host: libssta.so loads, exports every function that
+include/ssta.h declares, and rejects bad arguments before any HIP call.
+No kernel is launched here (the pointers passed are never valid buffers, and
+every call is built to fail validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import video_dit_block_tile_amd as m
+from video_dit_block_tile_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+ARG, SHAPE, ALIGN, NO_DEV, WS = -1, -2, -3, -4, -7
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "ssta.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssta_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = m.load()
+    names = _declared()
+    assert "ssta_attention_fwd" in names and len(names) >= 10
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(L.SIGNATURES)
+
+
+def test_status_strings():
+    lib = m.load()
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert lib.ssta_status_string(code)
+    assert lib.ssta_status_string(99) == b"unknown status"
+
+
+def _g(**kw):
+    base = dict(batch=1, heads=2, T=4, H=16, W=16, tile=(2, 8, 8))
+    base.update(kw)
+    return m.make_geom(base["batch"], base["heads"], base["T"], base["H"], base["W"],
+                       tile=base["tile"], head_dim=base.get("head_dim", 128))
+
+
+def test_geometry_validation():
+    lib = m.load()
+    good = 16
+    cases = [
+        (_g(head_dim=64), SHAPE),
+        (_g(tile=(4, 8, 8)), SHAPE),          # 256 tokens per block
+        (_g(tile=(3, 8, 8)), SHAPE),          # does not divide T
+        (_g(T=0), ARG),
+        (_g(batch=-1), ARG),
+        (_g(tile=(0, 8, 8)), ARG),
+    ]
+    for g, want in cases:
+        assert lib.ssta_tile_pool(ctypes.byref(g), good, good, 0, None, None) == want
+    assert lib.ssta_tile_pool(None, good, good, 0, None, None) == ARG
+
+
+def test_pointer_validation():
+    lib = m.load()
+    g = _g()
+    assert lib.ssta_tile_pool(ctypes.byref(g), None, 16, 0, None, None) == ARG
+    assert lib.ssta_tile_pool(ctypes.byref(g), 17, 16, 0, None, None) == ALIGN
+    assert lib.ssta_tile_pool(ctypes.byref(g), 16, 24, 0, None, None) == ALIGN
+    assert lib.ssta_tile_pool(ctypes.byref(g), 16, None, 0, None, None) == ARG
+    assert lib.ssta_tile_pool(ctypes.byref(g), 16, 32, 5, None, None) == ARG   # layout
+    assert lib.ssta_tile_unpermute(ctypes.byref(g), 16, 8, None) == ALIGN
+
+
+def test_params_validation():
+    lib = m.load()
+    g = _g()
+    for kw in (dict(win=(-1, 0, 0)), dict(topk=-3), dict(scale=0.0), dict(scale=float("inf")),
+               dict(lambda_=float("nan")), dict(flags=1 << 5)):
+        p = m.make_params(**kw)
+        assert lib.ssta_max_kept(ctypes.byref(g), ctypes.byref(p)) == ARG
+        assert lib.ssta_build_mask(ctypes.byref(g), ctypes.byref(p), 16, 16, 16, None,
+                                   None) == ARG
+
+
+def test_widths_and_capacity():
+    g = m.make_geom(1, 16, 60, 48, 80)                  # 30 x 6 x 10 blocks
+    p = m.make_params(topk=48)
+    assert m.ssta_topk_width(g, p) == 48
+    assert m.ssta_max_kept(g, p) == 27 + 48
+    p = m.make_params(topk=5000)
+    assert m.ssta_topk_width(g, p) == 1800 and m.ssta_max_kept(g, p) == 1800
+    p = m.make_params(topk=48, flags=m.COMBINE_AND)
+    assert m.ssta_max_kept(g, p) == 27
+    p = m.make_params(win=(0, 0, 0), topk=2000, flags=m.TOPK_EXCLUDE_WINDOW)
+    assert m.ssta_topk_width(g, p) == 1799
+    gt = m.make_geom(1, 2, 4, 16, 16)                   # 2 x 2 x 2 blocks
+    assert m.ssta_max_kept(gt, m.make_params(topk=2)) == 8
+    ws = m.ssta_workspace_bytes(g, m.make_params(topk=48))
+    assert ws >= 16 * 1800 * 1800 * 4 + 2 * 16 * 1800 * 128 * 4
+
+
+def test_workspace_and_score_validation():
+    lib = m.load()
+    g = _g()
+    p = m.make_params(topk=2)
+    need = m.ssta_workspace_bytes(g, p)
+    assert lib.ssta_score_select(ctypes.byref(g), ctypes.byref(p), 16, 16, 16, None, need,
+                                 None) == WS
+    assert lib.ssta_score_select(ctypes.byref(g), ctypes.byref(p), 16, 16, 16, 16, need - 1,
+                                 None) == WS
+    big = m.make_geom(1, 1, 80, 64, 128)                # 40 x 8 x 16 = 5120 blocks
+    assert lib.ssta_score_select(ctypes.byref(big), ctypes.byref(p), 16, 16, 16, 16, 1 << 40,
+                                 None) == SHAPE
+
+
+def test_attention_argument_rules():
+    lib = m.load()
+    g = _g()
+    p = m.make_params(topk=2)
+    # dense takes neither list; a list needs its count array
+    assert lib.ssta_attention_fwd(ctypes.byref(g), ctypes.byref(p), 16, 16, 16, 16, None, 0,
+                                  16, None, None) == ARG
+    assert lib.ssta_attention_fwd(ctypes.byref(g), ctypes.byref(p), 16, 16, 16, None, None, 3,
+                                  16, None, None) == ARG
+    assert lib.ssta_attention_fwd(ctypes.byref(g), ctypes.byref(p), 16, 16, 16, 16, 16, 9,
+                                  16, None, None) == ARG          # max_kept > n_tiles
+
+
+def test_no_device_is_an_error_not_a_fallback():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; this checks the no-device path")
+    lib = m.load()
+    g = _g()
+    assert lib.ssta_tile_pool(ctypes.byref(g), 16, 32, 0, None, None) == NO_DEV
+    with pytest.raises(m.SstaError):
+        L._call("ssta_tile_pool", ctypes.byref(g), 16, 32, 0, None, None)

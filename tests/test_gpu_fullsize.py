@@ -1,0 +1,76 @@
+"""GPU parity at the five measured shapes (tiny, 480p-short, 480p-5s, 720p-5s,
+720p-10s) in the launch configuration the benchmark times (one SstaPlan.run).
+
+Block means, top-k ids, kept lists and counts are compared in full, bit for
+bit.  The attention output is compared on a deterministic sample of rows that
+includes every corner and edge block, against the fp64 oracle.  Dense
+attention (every block kept) is checked on the 480p shapes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+from _helpers import (LSE_ABS, O_MAX_ABS, O_MEAN_ABS, bits, compare_o, geom_of, params_of,
+                      sample_rows, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["tiny", "480p-short", "480p-5s", "720p-5s", "720p-10s"])
+def test_full_shape(name):
+    import video_dit_block_tile_amd as m
+    wl = si.CONFIGS[name]
+    q, k, v = si.make_qkv(wl)
+    print("[%s] inputs ready" % name, flush=True)
+    plan = m.SstaPlan(geom_of(wl), params_of(wl))
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    plan.run(qd, kd, vd)
+    torch.cuda.synchronize()
+    print("[%s] gpu done" % name, flush=True)
+    sel = oracle.select(wl, q, k)
+    print("[%s] oracle selection done" % name, flush=True)
+    assert np.array_equal(plan.q_pooled.cpu().numpy().view(np.uint32),
+                          sel["q_pooled"].view(np.uint32))
+    assert np.array_equal(plan.k_pooled.cpu().numpy().view(np.uint32),
+                          sel["k_pooled"].view(np.uint32))
+    assert np.array_equal(plan.topk_idx.cpu().numpy(), sel["topk"])
+    assert np.array_equal(plan.kv_cnt.cpu().numpy(), sel["kv_cnt"])
+    assert np.array_equal(plan.kv_idx.cpu().numpy(), sel["kv_idx"])
+    rows = sample_rows(wl, 16, seed=1)
+    o_ref, lse_ref = oracle.attention(wl, q, k, v, sel["kv_idx"], sel["kv_cnt"], rows)
+    o_t = plan.o_t.float().cpu().numpy().reshape(-1, 128, 128)[rows]
+    mx, mean = compare_o(o_t, o_ref)
+    print("[%s] O max-abs %.3e mean-abs %.3e" % (name, mx, mean), flush=True)
+    assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS
+    lse = plan.lse.cpu().numpy().reshape(-1, 128)[rows]
+    assert np.max(np.abs(lse - lse_ref)) <= LSE_ABS
+    # final token-major output
+    o_tok = bits(plan.o).reshape(wl.batch * wl.heads, wl.n_tokens, 128)
+    o_til = bits(plan.o_t).reshape(-1, 128, 128)
+    for row in rows[:4]:
+        bh, i = divmod(int(row), wl.n_tiles)
+        toks = [oracle.tile_to_token(wl, i, r) for r in range(128)]
+        assert np.array_equal(o_tok[bh][toks], o_til[row])
+
+
+@pytest.mark.parametrize("name", ["480p-short", "480p-5s"])
+def test_dense_shape(name):
+    import video_dit_block_tile_amd as m
+    wl = si.CONFIGS[name]
+    q, k, v = si.make_qkv(wl)
+    plan = m.SstaPlan(geom_of(wl), params_of(wl), dense=True)
+    plan.run(to_dev(q), to_dev(k), to_dev(v))
+    torch.cuda.synchronize()
+    n = wl.n_tiles
+    kv_idx = np.broadcast_to(np.arange(n, dtype=np.int32), (wl.batch, wl.heads, n, n)).copy()
+    kv_cnt = np.full((wl.batch, wl.heads, n), n, dtype=np.int32)
+    rows = sample_rows(wl, 4, seed=2)[:12]
+    o_ref, lse_ref = oracle.attention(wl, q, k, v, kv_idx, kv_cnt, rows)
+    o_t = plan.o_t.float().cpu().numpy().reshape(-1, 128, 128)[rows]
+    mx, mean = compare_o(o_t, o_ref)
+    print("[%s dense] O max-abs %.3e mean-abs %.3e" % (name, mx, mean), flush=True)
+    assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS
+    lse = plan.lse.cpu().numpy().reshape(-1, 128)[rows]
+    assert np.max(np.abs(lse - lse_ref)) <= LSE_ABS

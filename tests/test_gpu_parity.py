@@ -1,0 +1,208 @@
+"""GPU parity of every step of the SSTA forward against the CPU oracle, through
+the C ABI, on small workloads that span several blocks, odd block grids,
+batch > 1, exact score ties, window 0, k = 0 and k above the block count.
+
+Bit-exact: tile copies (both layouts), block means, Score_r, Score_i, top-k
+ids, kept lists, bitmasks.  Within tolerance (tests/_helpers.py): the bf16
+attention output and its LSE.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+from _helpers import (LSE_ABS, O_MAX_ABS, O_MEAN_ABS, bits, compare_o, geom_of, params_of,
+                      sample_rows, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["tiny", "grid32-w1-k2", "grid32-w0-k3", "grid32-w0-k0", "dup-ties", "ragged", "wide-k"]
+_cache = {}
+
+
+def _case(name, flags=0):
+    key = (name, flags)
+    if key not in _cache:
+        wl = si.ALL[name]
+        q, k, v = si.make_qkv(wl)
+        sel = oracle.select(wl, q, k, flags)
+        _cache[key] = (wl, q, k, v, sel)
+    return _cache[key]
+
+
+def _plan(wl, flags=0, bitmask=True, dense=False):
+    import video_dit_block_tile_amd as m
+    return m.SstaPlan(geom_of(wl), params_of(wl, flags), bitmask=bitmask, dense=dense)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_tile_pool_bit_exact(name):
+    import video_dit_block_tile_amd as m
+    wl, q, k, v, sel = _case(name)
+    g = geom_of(wl)
+    for x in (q, v):
+        xd = to_dev(x)
+        tok = torch.empty(wl.batch, wl.heads, wl.n_tiles, 128, 128, dtype=torch.bfloat16,
+                          device="cuda")
+        dim = torch.empty_like(tok)
+        pooled = torch.empty(wl.batch, wl.heads, wl.n_tiles, 128, dtype=torch.float32,
+                             device="cuda")
+        m.ssta_tile_pool(g, xd, tok, m.LAYOUT_TOKEN_MAJOR, pooled)
+        m.ssta_tile_pool(g, xd, dim, m.LAYOUT_DIM_MAJOR, None)
+        torch.cuda.synchronize()
+        ref = oracle.permute(wl, x)
+        assert np.array_equal(bits(tok), ref)
+        assert np.array_equal(bits(dim), np.swapaxes(ref, -1, -2))
+        assert np.array_equal(pooled.cpu().numpy().view(np.uint32),
+                              oracle.pool(wl, x).view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged"])
+def test_unpermute_inverts(name):
+    import video_dit_block_tile_amd as m
+    wl, q, k, v, sel = _case(name)
+    g = geom_of(wl)
+    xt = to_dev(oracle.permute(wl, k))
+    out = torch.empty(wl.batch, wl.heads, wl.n_tokens, 128, dtype=torch.bfloat16, device="cuda")
+    m.ssta_tile_unpermute(g, xt, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), k)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_scores_bit_exact(name):
+    import video_dit_block_tile_amd as m
+    wl, q, k, v, sel = _case(name)
+    g, p = geom_of(wl), params_of(wl)
+    qp = torch.from_numpy(sel["q_pooled"]).cuda()
+    kp = torch.from_numpy(sel["k_pooled"]).cuda()
+    sc = torch.empty(wl.batch, wl.heads, wl.n_tiles, wl.n_tiles, dtype=torch.float32,
+                     device="cuda")
+    red = torch.empty(wl.batch, wl.heads, wl.n_tiles, dtype=torch.float32, device="cuda")
+    ws = torch.empty(m.ssta_workspace_bytes(g, p), dtype=torch.uint8, device="cuda")
+    m.ssta_scores(g, p, qp, kp, sc, red, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(red.cpu().numpy().view(np.uint32), sel["red"].view(np.uint32))
+    got = sc.cpu().numpy().view(np.uint32)
+    want = sel["scores"].view(np.uint32)
+    bad = np.count_nonzero(got != want)
+    assert bad == 0, "%d of %d scores differ" % (bad, got.size)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_selection_and_lists_bit_exact(name):
+    wl, q, k, v, sel = _case(name)
+    plan = _plan(wl)
+    plan.tile_pool(to_dev(q), to_dev(k), to_dev(v))
+    plan.select()
+    torch.cuda.synchronize()
+    assert np.array_equal(plan.topk_idx.cpu().numpy(), sel["topk"])
+    assert np.array_equal(plan.kv_cnt.cpu().numpy(), sel["kv_cnt"])
+    assert np.array_equal(plan.kv_idx.cpu().numpy(), sel["kv_idx"])
+    assert np.array_equal(plan.bitmask.cpu().numpy().view(np.uint32), sel["bitmask"])
+
+
+def _check_attention(wl, q, k, v, sel, plan, rows):
+    o_ref, lse_ref = oracle.attention(wl, q, k, v, sel["kv_idx"], sel["kv_cnt"], rows)
+    o_t = plan.o_t.float().cpu().numpy().reshape(-1, 128, 128)[rows]
+    mx, mean = compare_o(o_t, o_ref)
+    assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS, (mx, mean)
+    lse = plan.lse.cpu().numpy().reshape(-1, 128)[rows]
+    assert np.max(np.abs(lse - lse_ref)) <= LSE_ABS
+    # the token-major output holds the same values at the tokens' positions
+    o_tok = bits(plan.o).reshape(wl.batch * wl.heads, wl.n_tokens, 128)
+    o_til = bits(plan.o_t).reshape(-1, 128, 128)
+    n = wl.n_tiles
+    for row in rows[:8]:
+        bh, i = divmod(int(row), n)
+        toks = [oracle.tile_to_token(wl, i, r) for r in range(128)]
+        assert np.array_equal(o_tok[bh][toks], o_til[row])
+    return mx, mean
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_attention_vs_oracle(name):
+    wl, q, k, v, sel = _case(name)
+    plan = _plan(wl)
+    plan.run(to_dev(q), to_dev(k), to_dev(v))
+    torch.cuda.synchronize()
+    rows = sample_rows(wl, 48)
+    _check_attention(wl, q, k, v, sel, plan, rows)
+
+
+def test_attention_unit_values():
+    wl, q, k, v, sel = _case("ragged")
+    plan = _plan(wl)
+    ones = np.full_like(v, 0x3F80)
+    plan.run(to_dev(q), to_dev(k), to_dev(ones))
+    torch.cuda.synchronize()
+    o = plan.o.float().cpu().numpy()
+    assert np.max(np.abs(o - 1.0)) <= 1e-2
+
+
+def test_dense_equals_all_kept():
+    wl, q, k, v, sel = _case("wide-k")            # top-k clamps to every block
+    assert np.all(sel["kv_cnt"] == wl.n_tiles)
+    sparse = _plan(wl)
+    dense = _plan(wl, dense=True)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    sparse.run(qd, kd, vd)
+    dense.run(qd, kd, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(sparse.o_t, dense.o_t)
+    assert torch.equal(sparse.lse, dense.lse)
+
+
+def test_deterministic():
+    wl, q, k, v, sel = _case("dup-ties")
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    a = _plan(wl)
+    b = _plan(wl)
+    a.run(qd, kd, vd)
+    b.run(qd, kd, vd)
+    torch.cuda.synchronize()
+    for x, y in ((a.o, b.o), (a.lse, b.lse), (a.kv_idx, b.kv_idx), (a.topk_idx, b.topk_idx)):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("flags", [oracle.COMBINE_AND, oracle.TOPK_EXCLUDE_WINDOW,
+                                   oracle.COMBINE_AND | oracle.TOPK_EXCLUDE_WINDOW])
+def test_flag_variants(flags):
+    name = "grid32-w1-k2"
+    wl, q, k, v, sel = _case(name, flags)
+    plan = _plan(wl, flags)
+    plan.run(to_dev(q), to_dev(k), to_dev(v))
+    torch.cuda.synchronize()
+    assert np.array_equal(plan.topk_idx.cpu().numpy(), sel["topk"])
+    assert np.array_equal(plan.kv_cnt.cpu().numpy(), sel["kv_cnt"])
+    assert np.array_equal(plan.kv_idx.cpu().numpy(), sel["kv_idx"])
+    rows = np.arange(wl.batch * wl.heads * wl.n_tiles)
+    o_ref, lse_ref = oracle.attention(wl, q, k, v, sel["kv_idx"], sel["kv_cnt"], rows)
+    o_t = plan.o_t.float().cpu().numpy().reshape(-1, 128, 128)
+    mx, mean = compare_o(o_t, o_ref)
+    assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS
+    lse = plan.lse.cpu().numpy().reshape(-1, 128)
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse), empty)
+    if (~empty).any():
+        assert np.max(np.abs(lse[~empty] - lse_ref[~empty])) <= LSE_ABS
+    if flags == oracle.COMBINE_AND | oracle.TOPK_EXCLUDE_WINDOW:
+        # selection outside the window intersected with the window: nothing is kept
+        assert np.all(sel["kv_cnt"] == 0) and np.all(o_t == 0)
+
+
+def test_device_argument_errors():
+    import video_dit_block_tile_amd as m
+    wl = si.ALL["tiny"]
+    g = geom_of(wl)
+    x = torch.zeros(wl.batch, wl.heads, wl.n_tokens, 128, dtype=torch.bfloat16, device="cuda")
+    pooled = torch.empty(wl.batch * wl.heads * wl.n_tiles * 128 + 1, dtype=torch.float32,
+                         device="cuda")
+    lib = m.load()
+    import ctypes
+    rc = lib.ssta_tile_pool(ctypes.byref(g), x.data_ptr(), None, 0, pooled.data_ptr() + 4, None)
+    assert rc == -3                                   # SSTA_ERR_ALIGN, nothing launched
+    rc = lib.ssta_tile_pool(ctypes.byref(g), x.data_ptr(), None, 0, None, None)
+    assert rc == -1                                   # no output requested
+    torch.cuda.synchronize()

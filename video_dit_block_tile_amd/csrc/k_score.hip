@@ -1,0 +1,285 @@
+// Step 2 of SSTA (selective mask generation): block-level cosine similarity
+// Score_s, key-key redundancy Score_r, importance Score_i and the per-query
+// top-k ("HunyuanVideo 1.5 Technical Report" summary page, section "SSTA:
+// Selective and Sliding Tile Attention", Step 2; the importance_sampling
+// excerpt on the "HunyuanVideo-1.5: An 8.3B-Parameter Video Diffusion Model
+// Built for Consumer GPUs" page, section "Under the Hood: SSTA and Muon in
+// Detail").
+//
+// The selection is an integer decided by fp32 arithmetic, so every score is
+// computed in one fixed order that any implementation can repeat:
+//   * dot products are fmaf chains over the channel index 0..127 ascending,
+//     starting at 0.0f (an LDS-tiled fp32 VALU GEMM whose inner loop runs
+//     over channels in order: no split-K, no matrix cores, whose internal
+//     accumulation order is not sequential);
+//   * sqrt and division are IEEE correctly rounded;
+//   * the redundancy sum runs over key blocks in ascending order;
+//   * nothing is contracted (this file is built with -ffp-contract=off).
+// Work: 2 * n^2 * 128 FMAs per (batch, head) for Q.K and K.K; the kernels are
+// bound by the fp32 vector ALU, not by HBM.
+#include "ssta_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace ssta {
+namespace {
+
+constexpr int kBlk = 64;   // GEMM tile: 64 rows x 64 columns per workgroup
+
+// One thread per vector: x / |x| with a sequential fmaf sum of squares.
+__global__ __launch_bounds__(256) void k_normalize(const float* __restrict__ p,
+                                                   float* __restrict__ out, int64_t rows) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows) return;
+  const float4* v = reinterpret_cast<const float4*>(p + i * kHeadDim);
+  float ss = 0.0f;
+#pragma unroll 8
+  for (int c = 0; c < kHeadDim / 4; ++c) {
+    const float4 a = v[c];
+    ss = __builtin_fmaf(a.x, a.x, ss);
+    ss = __builtin_fmaf(a.y, a.y, ss);
+    ss = __builtin_fmaf(a.z, a.z, ss);
+    ss = __builtin_fmaf(a.w, a.w, ss);
+  }
+  const float nrm = __builtin_sqrtf(ss);
+  float4* o = reinterpret_cast<float4*>(out + i * kHeadDim);
+#pragma unroll 8
+  for (int c = 0; c < kHeadDim / 4; ++c) {
+    const float4 a = v[c];
+    float4 r;
+    if (nrm == 0.0f) {
+      r = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    } else {
+      r.x = a.x / nrm;
+      r.y = a.y / nrm;
+      r.z = a.z / nrm;
+      r.w = a.w / nrm;
+    }
+    o[c] = r;
+  }
+}
+
+// Loads rows [row0, row0+64) of a [n][128] fp32 matrix into LDS transposed,
+// dst[d][row] (rows past n are zero).
+__device__ __forceinline__ void load_block_t(float (*dst)[kBlk], const float* __restrict__ src,
+                                             int64_t row0, int64_t n) {
+  const int t = threadIdx.x;
+  const int r = t & 63;
+  const int64_t gr = row0 + r;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int d = ((t >> 6) + 4 * q) * 4;
+    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (gr < n) a = *reinterpret_cast<const float4*>(src + gr * kHeadDim + d);
+    dst[d + 0][r] = a.x;
+    dst[d + 1][r] = a.y;
+    dst[d + 2][r] = a.z;
+    dst[d + 3][r] = a.w;
+  }
+}
+
+// acc[a][b] = fmaf chain over d ascending of A[d][4*ti+a] * B[d][4*tj+b].
+__device__ __forceinline__ void block_dots(const float (*A)[kBlk], const float (*B)[kBlk],
+                                           int ti, int tj, float acc[4][4]) {
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
+#pragma unroll 4
+  for (int d = 0; d < kHeadDim; ++d) {
+    const float4 x = *reinterpret_cast<const float4*>(&A[d][4 * ti]);
+    const float4 y = *reinterpret_cast<const float4*>(&B[d][4 * tj]);
+    const float xa[4] = {x.x, x.y, x.z, x.w};
+    const float yb[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_fmaf(xa[a], yb[b], acc[a][b]);
+  }
+}
+
+// Score_r: one workgroup owns 64 key columns j and walks the key blocks i in
+// ascending order, 64 at a time, adding u(i, j) = (khat_i.khat_j + 1) * 0.5
+// for i != j into one running fp32 sum per column.
+__global__ __launch_bounds__(256) void k_redundancy(const float* __restrict__ khat,
+                                                    float* __restrict__ red, int64_t n) {
+  __shared__ __attribute__((aligned(16))) float kj[kHeadDim][kBlk];
+  __shared__ __attribute__((aligned(16))) float ki[kHeadDim][kBlk];   // reused for u
+  const int64_t bh = blockIdx.y;
+  const int64_t j0 = (int64_t)blockIdx.x * kBlk;
+  const float* kb = khat + bh * n * kHeadDim;
+  const int t = threadIdx.x;
+  const int ti = t >> 4, tj = t & 15;
+  load_block_t(kj, kb, j0, n);
+  float s = 0.0f;                                   // running sum of column j0 + t (t < 64)
+  float (*u)[kBlk + 1] = reinterpret_cast<float (*)[kBlk + 1]>(&ki[0][0]);
+  for (int64_t i0 = 0; i0 < n; i0 += kBlk) {
+    __syncthreads();                                // ki/u free
+    load_block_t(ki, kb, i0, n);
+    __syncthreads();
+    float acc[4][4];
+    block_dots(ki, kj, ti, tj, acc);
+    __syncthreads();                                // everyone done reading ki
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) u[4 * ti + a][4 * tj + b] = (acc[a][b] + 1.0f) * 0.5f;
+    __syncthreads();
+    if (t < kBlk) {
+      const int64_t j = j0 + t;
+      const int lim = (int)((n - i0) < kBlk ? (n - i0) : kBlk);
+      for (int r = 0; r < lim; ++r)
+        if (i0 + r != j) s = s + u[r][t];
+    }
+  }
+  if (t < kBlk && j0 + t < n) red[bh * n + j0 + t] = (n > 1) ? s / (float)(n - 1) : 0.0f;
+}
+
+// Score_i = (lambda * (qhat_i.khat_j + 1) * 0.5) - (beta * red_j), one 64x64 tile per workgroup.
+__global__ __launch_bounds__(256) void k_score_matrix(const float* __restrict__ qhat,
+                                                      const float* __restrict__ khat,
+                                                      const float* __restrict__ red,
+                                                      float* __restrict__ scores, int64_t n,
+                                                      float lambda_, float beta) {
+  __shared__ __attribute__((aligned(16))) float qi[kHeadDim][kBlk];
+  __shared__ __attribute__((aligned(16))) float kj[kHeadDim][kBlk];
+  const int64_t bh = blockIdx.z;
+  const int64_t i0 = (int64_t)blockIdx.y * kBlk, j0 = (int64_t)blockIdx.x * kBlk;
+  const int t = threadIdx.x;
+  const int ti = t >> 4, tj = t & 15;
+  load_block_t(qi, qhat + bh * n * kHeadDim, i0, n);
+  load_block_t(kj, khat + bh * n * kHeadDim, j0, n);
+  __syncthreads();
+  float acc[4][4];
+  block_dots(qi, kj, ti, tj, acc);
+  float* sb = scores + bh * n * n;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int64_t j = j0 + 4 * tj + b;
+    if (j >= n) continue;
+    const float rb = beta * red[bh * n + j];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int64_t i = i0 + 4 * ti + a;
+      if (i >= n) continue;
+      const float gs = (acc[a][b] + 1.0f) * 0.5f;
+      const float la = lambda_ * gs;
+      sb[i * n + j] = la - rb;
+    }
+  }
+}
+
+// Order-preserving map of a float to uint32 (larger float -> larger key);
+// -0 is mapped like +0 so that the two compare equal.  Every finite value
+// maps above 0, which marks "not a candidate".
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (f == 0.0f) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Per-row top-k, one wave per query-block row.  Each lane keeps E keys
+// (columns lane, lane+64, ...).  The k-th largest key T is found bit by bit
+// from the top (32 wave-wide counts), then the row keeps every key above T and
+// the lowest-id columns equal to T until k are kept, writing ids ascending.
+template <int E>
+__global__ __launch_bounds__(256) void k_topk(Geo g, const float* __restrict__ scores,
+                                              int32_t* __restrict__ out, int64_t rows, int k,
+                                              int width, int excl, int wt, int wh, int ww) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t n = g.n_tiles;
+  const int64_t i = row % n;
+  const float* s = scores + row * n;
+  const int ti = (int)(i / ((int64_t)g.ny * g.nx)), yi = (int)((i / g.nx) % g.ny),
+            xi = (int)(i % g.nx);
+  uint32_t key[E];
+  int ncand = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int64_t j = lane + 64 * e;
+    uint32_t kk = 0u;
+    if (j < n) {
+      kk = order_key(s[j]);
+      if (excl) {
+        const int tj = (int)(j / ((int64_t)g.ny * g.nx)), yj = (int)((j / g.nx) % g.ny),
+                  xj = (int)(j % g.nx);
+        if (abs(tj - ti) <= wt && abs(yj - yi) <= wh && abs(xj - xi) <= ww) kk = 0u;
+      }
+    }
+    key[e] = kk;
+    ncand += __popcll(__ballot(kk != 0u));
+  }
+  const int want = min(min(k, width), ncand);
+  int32_t* o = out + row * width;
+  int pos = 0;
+  if (want > 0) {
+    uint32_t thr = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) cnt += __popcll(__ballot(key[e] >= cand));
+      if (cnt >= want) thr = cand;
+    }
+    int above = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) above += __popcll(__ballot(key[e] > thr));
+    const int need = want - above;   // >= 1
+    int ties = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool eq = key[e] == thr;
+      const uint64_t eqm = __ballot(eq);
+      const bool sel = key[e] > thr || (eq && ties + lanes_below(eqm) < need);
+      ties += __popcll(eqm);
+      const uint64_t selm = __ballot(sel);
+      if (sel) o[pos + lanes_below(selm)] = (int32_t)(lane + 64 * e);
+      pos += __popcll(selm);
+    }
+  }
+  for (int p = pos + lane; p < width; p += 64) o[p] = -1;
+}
+
+template <int E>
+hipError_t launch_topk_e(const Geo& g, const TopkArgs& a, hipStream_t s) {
+  const int64_t rows = g.bh * g.n_tiles;
+  hipLaunchKernelGGL(k_topk<E>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, g, a.scores,
+                     a.topk_idx, rows, a.k, a.width, a.exclude_window, a.wt, a.wh, a.ww);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_scores(const Geo& g, const ScoreArgs& a, hipStream_t s) {
+  const int64_t n = g.n_tiles;
+  const int64_t vecs = g.bh * n;
+  const unsigned nb = (unsigned)((vecs + 255) / 256);
+  hipLaunchKernelGGL(k_normalize, dim3(nb), dim3(256), 0, s, a.q_pooled, a.qhat, vecs);
+  hipLaunchKernelGGL(k_normalize, dim3(nb), dim3(256), 0, s, a.k_pooled, a.khat, vecs);
+  const unsigned tiles = (unsigned)((n + kBlk - 1) / kBlk);
+  hipLaunchKernelGGL(k_redundancy, dim3(tiles, (unsigned)g.bh), dim3(256), 0, s, a.khat, a.red,
+                     n);
+  hipLaunchKernelGGL(k_score_matrix, dim3(tiles, tiles, (unsigned)g.bh), dim3(256), 0, s, a.qhat,
+                     a.khat, a.red, a.scores, n, a.lambda_, a.beta);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const Geo& g, const TopkArgs& a, hipStream_t s) {
+  const int64_t slots = (g.n_tiles + 63) / 64;
+  if (slots <= 1) return launch_topk_e<1>(g, a, s);
+  if (slots <= 2) return launch_topk_e<2>(g, a, s);
+  if (slots <= 4) return launch_topk_e<4>(g, a, s);
+  if (slots <= 8) return launch_topk_e<8>(g, a, s);
+  if (slots <= 16) return launch_topk_e<16>(g, a, s);
+  if (slots <= 32) return launch_topk_e<32>(g, a, s);
+  return launch_topk_e<64>(g, a, s);
+}
+
+}  // namespace ssta

@@ -1,0 +1,95 @@
+// Internal declarations shared by the host dispatcher (ssta_api.cpp) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssta {
+
+constexpr int kHeadDim = 128;     // channels per head
+constexpr int kTileTokens = 128;  // tokens per 3D block
+constexpr int kMaxTopkTiles = 4096;
+
+// Geometry with every derived quantity precomputed on the host.
+struct Geo {
+  int32_t batch, heads, D;
+  int32_t T, H, W;
+  int32_t tt, th, tw;       // block size
+  int32_t nt, ny, nx;       // block grid
+  int64_t N;                // tokens per (batch, head)
+  int64_t n_tiles;          // blocks per (batch, head)
+  int64_t bh;               // batch * heads
+};
+
+// Maps a linear workgroup id so that the ids one XCD receives (the hardware
+// deals ids round-robin over the 8 XCDs) form one contiguous range.  A
+// bijection on [0, nblocks) for any nblocks.
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblocks) {
+  const int64_t q = nblocks / 8, r = nblocks % 8;
+  const int64_t xcd = bid % 8, k = bid / 8;
+  return xcd < r ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
+}
+
+// Token index (within one batch/head) of in-block position r of block `tile`.
+__device__ __forceinline__ int64_t tile_token(const Geo& g, int64_t tile, int r) {
+  const int64_t bt = tile / ((int64_t)g.ny * g.nx);
+  const int64_t by = (tile / g.nx) % g.ny;
+  const int64_t bx = tile % g.nx;
+  const int it = r / (g.th * g.tw);
+  const int iy = (r / g.tw) % g.th;
+  const int ix = r % g.tw;
+  return ((bt * g.tt + it) * g.H + (by * g.th + iy)) * (int64_t)g.W + (bx * g.tw + ix);
+}
+
+hipError_t launch_tile_pool(const Geo& g, const void* x, void* x_tiled, int layout,
+                            float* pooled, hipStream_t s);
+hipError_t launch_tile_unpermute(const Geo& g, const void* x_tiled, void* x, hipStream_t s);
+
+struct ScoreArgs {
+  const float* q_pooled;
+  const float* k_pooled;
+  float* qhat;
+  float* khat;
+  float* red;
+  float* scores;
+  float lambda_, beta;
+};
+hipError_t launch_scores(const Geo& g, const ScoreArgs& a, hipStream_t s);
+
+struct TopkArgs {
+  const float* scores;
+  int32_t* topk_idx;
+  int32_t k;            // requested top-k
+  int32_t width;        // row width of topk_idx
+  int32_t exclude_window;
+  int32_t wt, wh, ww;
+};
+hipError_t launch_topk(const Geo& g, const TopkArgs& a, hipStream_t s);
+
+struct MaskArgs {
+  const int32_t* topk_idx;
+  int32_t k_width;
+  int32_t* kv_idx;
+  int32_t* kv_cnt;
+  uint32_t* bitmask;
+  int32_t max_kept;
+  int32_t wt, wh, ww;
+  int32_t combine_and;
+};
+hipError_t launch_build_mask(const Geo& g, const MaskArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  const void* q_t;
+  const void* k_t;
+  const void* v_t;
+  const int32_t* kv_idx;   // nullptr: dense
+  const int32_t* kv_cnt;
+  int32_t max_kept;
+  void* o_t;
+  float* lse;
+  float scale_log2;        // softmax scale * log2(e)
+};
+hipError_t launch_attention(const Geo& g, const AttnArgs& a, hipStream_t s);
+
+}  // namespace ssta

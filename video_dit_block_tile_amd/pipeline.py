@@ -1,0 +1,92 @@
+"""The whole SSTA forward as one sequence of C-ABI calls on one stream.
+
+``SstaPlan`` allocates every buffer once for a geometry (PyTorch is only the
+allocator here) and ``run`` enqueues the five steps:
+
+  1. ssta_tile_pool      Q -> tile-major Q_t + block means  (Step 1 + Step 2 pooling)
+                         K -> tile-major K_t + block means
+                         V -> dim-major tiles V_t
+  2. ssta_score_select   block means -> top-k key blocks per query block  (Step 2)
+  3. ssta_build_mask     top-k + sliding-tile window -> kept lists  (Steps 3-4)
+  4. ssta_attention_fwd  block-sparse attention -> O_t, LSE  (Step 4)
+  5. ssta_tile_unpermute O_t -> token-major O
+
+(Steps as numbered in the "HunyuanVideo 1.5 Technical Report" summary page,
+section "SSTA: Selective and Sliding Tile Attention".)
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+
+class SstaPlan:
+    def __init__(self, geom: L.SstaGeom, params: L.SstaParams, device="cuda",
+                 bitmask: bool = False, dense: bool = False):
+        self.geom, self.params, self.dense = geom, params, dense
+        g = geom
+        dev = torch.device(device)
+        n, R, D = g.n_tiles, g.tile_tokens, g.head_dim
+        bh = (g.batch, g.heads)
+        self.q_t = torch.empty(bh + (n, R, D), dtype=torch.bfloat16, device=dev)
+        self.k_t = torch.empty_like(self.q_t)
+        self.v_t = torch.empty(bh + (n, D, R), dtype=torch.bfloat16, device=dev)
+        self.o_t = torch.empty_like(self.q_t)
+        self.o = torch.empty(bh + (g.n_tokens, D), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(bh + (n, R), dtype=torch.float32, device=dev)
+        self.q_pooled = torch.empty(bh + (n, D), dtype=torch.float32, device=dev)
+        self.k_pooled = torch.empty_like(self.q_pooled)
+        self.width = L.ssta_topk_width(g, params)
+        self.max_kept = L.ssta_max_kept(g, params)
+        self.topk_idx = torch.empty(bh + (n, self.width), dtype=torch.int32, device=dev)
+        self.kv_idx = torch.empty(bh + (n, self.max_kept), dtype=torch.int32, device=dev)
+        self.kv_cnt = torch.empty(bh + (n,), dtype=torch.int32, device=dev)
+        self.bitmask = (torch.empty(bh + (n, (n + 31) // 32), dtype=torch.int32, device=dev)
+                        if bitmask else None)
+        self.workspace = torch.empty(L.ssta_workspace_bytes(g, params), dtype=torch.uint8,
+                                     device=dev)
+
+    # individual steps -----------------------------------------------------
+    def tile_pool(self, q, k, v, stream=None):
+        g = self.geom
+        L.ssta_tile_pool(g, q, self.q_t, L.LAYOUT_TOKEN_MAJOR, self.q_pooled, stream)
+        L.ssta_tile_pool(g, k, self.k_t, L.LAYOUT_TOKEN_MAJOR, self.k_pooled, stream)
+        L.ssta_tile_pool(g, v, self.v_t, L.LAYOUT_DIM_MAJOR, None, stream)
+
+    def select(self, stream=None):
+        g, p = self.geom, self.params
+        if self.width > 0:
+            L.ssta_score_select(g, p, self.q_pooled, self.k_pooled, self.topk_idx,
+                                self.workspace, stream)
+        L.ssta_build_mask(g, p, self.topk_idx, self.kv_idx, self.kv_cnt, self.bitmask, stream)
+
+    def attend(self, stream=None, dense=None):
+        dense = self.dense if dense is None else dense
+        g, p = self.geom, self.params
+        if dense:
+            L.ssta_attention_fwd(g, p, self.q_t, self.k_t, self.v_t, None, None, self.o_t,
+                                 self.lse, stream)
+        else:
+            L.ssta_attention_fwd(g, p, self.q_t, self.k_t, self.v_t, self.kv_idx, self.kv_cnt,
+                                 self.o_t, self.lse, stream)
+
+    def unpermute(self, stream=None):
+        L.ssta_tile_unpermute(self.geom, self.o_t, self.o, stream)
+
+    # whole forward --------------------------------------------------------
+    def run(self, q, k, v, stream=None):
+        """Enqueue the whole forward; returns (o [B,h,N,D] bf16, lse [B,h,n,R] fp32)."""
+        self.tile_pool(q, k, v, stream)
+        if not self.dense:
+            self.select(stream)
+        self.attend(stream)
+        self.unpermute(stream)
+        return self.o, self.lse
+
+
+def ssta_forward(q, k, v, geom: L.SstaGeom, params: L.SstaParams, dense: bool = False):
+    """One-shot SSTA forward on bf16 [B, h, T*H*W, 128] device tensors."""
+    plan = SstaPlan(geom, params, device=q.device, dense=dense)
+    o, lse = plan.run(q, k, v)
+    return o, lse, plan
