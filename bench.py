@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1800,
                     help="query-block rows of head 0 in the CPU oracle sample")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB 5 times (calibrates "
+                         "the HBM byte counters) and exit")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per attention launch measured with rocprofv3 counters")
     return ap.parse_args()
@@ -108,6 +111,15 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib << 19, dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 2, "launches": 5}))
+        return
 
     import synthetic_inputs as si
     import video_dit_block_tile_amd as m

@@ -4,7 +4,9 @@ Each translation unit is compiled to an object under ``_build/`` and the
 objects are linked into ``video_dit_block_tile_amd/libssta.so``.  Packed fp32
 VALU instructions are disabled for all device code.  The scoring and tiling
 units are compiled without floating-point contraction (their results must not
-depend on the compiler's choice to fuse).
+depend on the compiler's choice to fuse).  The attention unit is compiled with
+-fno-honor-nans: its inputs are finite, and IEEE NaN semantics would make
+every fmaxf of a matrix-core result pay an extra canonicalising instruction.
 """
 from __future__ import annotations
 
@@ -29,7 +31,7 @@ SOURCES = {
     "k_tile.hip": ["-ffp-contract=off"],
     "k_score.hip": ["-ffp-contract=off"],
     "k_mask.hip": [],
-    "k_attn.hip": [],
+    "k_attn.hip": ["-fno-honor-nans"],
 }
 
 

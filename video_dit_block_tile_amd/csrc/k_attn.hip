@@ -12,13 +12,26 @@
 // needs a single cross-lane exchange (lane ^ 32).  The softmax runs online in
 // fp32 in the log2 domain.  The probabilities never leave registers: the
 // MFMA output layout of S^T is reused directly as the B operand of
-// O^T += V^T P^T, with the contraction's key order permuted to match, and V
-// arrives dim-major so the A operand (V^T rows) is two 8-byte LDS reads.
+// O^T += V^T P^T.  Each lane feeds key row kperm(lane) (bits 2 and 3 of the
+// lane index swapped) into the S^T product, which makes every 8 output
+// registers of a lane 8 consecutive keys; V arrives dim-major, so the matching
+// A operand of the P.V product is one 16-byte LDS read of a V^T row.
 // K and V^T tiles (32 KB each) are staged in LDS with a 16-byte-chunk XOR
 // swizzle (chunk ^ row%16) so the MFMA operand reads are conflict-free.
-// Workgroup ids are remapped so each XCD walks a contiguous range of query
-// blocks of one head: neighbouring query blocks share most window blocks,
-// which then hit in that XCD's L2.
+// Schedule: the hardware deals workgroup ids round-robin over the 8 XCDs.
+// The grid is laid out so that XCD x receives, head after head, the
+// contiguous slice [x*c, (x+1)*c) of that head's query blocks (c = ceil(n/8)).
+// All XCDs therefore work on the same one or two heads at any time, whose K
+// and V (118 MB per head at the 720p 10 s shape) stay resident in the 256 MB
+// MALL, while within an XCD neighbouring query blocks share most of their
+// window blocks in that XCD's L2.
+// Memory: the next kept block's K and V^T are fetched into registers while
+// the current block is computed, so one global-memory round trip overlaps each
+// block.  Each block is processed as two halves of 64 keys, which halves the
+// live score registers and keeps two waves per SIMD without spills.
+// Softmax: the running max is only raised when some query's max grows by more
+// than 8 in the log2 domain (probabilities stay below 2^8), so the O rescale
+// is skipped on most blocks.
 //
 // Work per kept pair: 4*128^3 = 8.39 MFLOP on the matrix cores, 64 KB of
 // K/V^T reads.  Bound: bf16 MFMA throughput (and the fp32 softmax that must
@@ -39,17 +52,45 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 256 + ((chunk ^ (row & 15)) << 4);
 }
 
+// Loads one 32 KB tile (K or V^T) of block j into registers: 8 x 16 B per thread.
+__device__ __forceinline__ void fetch_tile(u32x4 (&r)[8], const uint8_t* base, int64_t j,
+                                           int tid) {
+  const uint8_t* tile = base + j * kTileBytes;     // uniform across the workgroup
+  const uint32_t off = (uint32_t)tid * 16u;
+#pragma unroll
+  for (int mm = 0; mm < 8; ++mm)
+    r[mm] = *reinterpret_cast<const u32x4*>(tile + off + 4096u * mm);
+}
+
+__device__ __forceinline__ void stage_tile(uint8_t* lds, const u32x4 (&r)[8], int tid) {
+#pragma unroll
+  for (int mm = 0; mm < 8; ++mm) {
+    const int L = tid + 256 * mm;
+    *reinterpret_cast<u32x4*>(lds + swz(L >> 4, L & 15)) = r[mm];
+  }
+}
+
+__device__ __forceinline__ float max4(float a, float b, float c, float d) {
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
-void k_attn_fwd(Geo g, AttnArgs a) {
+void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kTileBytes];
   uint8_t* sK = smem;                 // [key][256 B]
   uint8_t* sV = smem + kTileBytes;    // [d][256 B]
 
-  const int64_t nrows = g.bh * g.n_tiles;
-  const int64_t row = xcd_remap(blockIdx.x, nrows);
-  const int64_t bh = row / g.n_tiles;
+  // Head-synchronous XCD slices (see the file comment).
+  const int64_t bid = blockIdx.x;
+  const int64_t xcd = bid & 7, k8 = bid >> 3;
+  const int64_t bh = k8 / slice;
+  const int64_t qi = xcd * slice + (k8 - bh * slice);
+  if (qi >= g.n_tiles) return;
+  const int64_t row = bh * g.n_tiles + qi;
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hl = lane >> 5;
+  const int kperm = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
   constexpr int64_t kTileElems = kTileTokens * kHeadDim;
 
   const uint16_t* qb = static_cast<const uint16_t*>(a.q_t) + row * kTileElems;
@@ -73,92 +114,105 @@ void k_attn_fwd(Geo g, AttnArgs a) {
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-  float m = -INFINITY;   // running max of the log2-scaled scores
+  float m = -INFINITY;   // running (possibly stale) max of the log2-scaled scores
   float l = 0.0f;        // this lane's part of the running denominator
   const float c = a.scale_log2;
 
+  u32x4 kr[8], vr[8];
+  if (cnt > 0) {
+    const int64_t j0 = dense ? 0 : idx[0];
+    fetch_tile(kr, kb, j0, tid);
+    fetch_tile(vr, vb, j0, tid);
+  }
+
   for (int it = 0; it < cnt; ++it) {
-    const int64_t j = dense ? it : idx[it];
-    const u32x4* kg = reinterpret_cast<const u32x4*>(kb + j * kTileBytes);
-    const u32x4* vg = reinterpret_cast<const u32x4*>(vb + j * kTileBytes);
-    u32x4 kr[8], vr[8];
-#pragma unroll
-    for (int mm = 0; mm < 8; ++mm) {
-      kr[mm] = kg[tid + 256 * mm];
-      vr[mm] = vg[tid + 256 * mm];
-    }
-    __syncthreads();   // the previous block's K/V are no longer read
-#pragma unroll
-    for (int mm = 0; mm < 8; ++mm) {
-      const int L = tid + 256 * mm;
-      *reinterpret_cast<u32x4*>(sK + swz(L >> 4, L & 15)) = kr[mm];
-      *reinterpret_cast<u32x4*>(sV + swz(L >> 4, L & 15)) = vr[mm];
-    }
+    __syncthreads();   // every wave is done reading the previous block's K and V^T
+    stage_tile(sK, kr, tid);
+    stage_tile(sV, vr, tid);
     __syncthreads();
-
-    // S^T: lane holds query l32, keys 32*kt + 8*(r/4) + 4*hl + r%4.
-    f32x16 s[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kt][r] = 0.0f;
-      const int key = 32 * kt + l32;
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(sK + swz(key, 2 * st + hl));
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s[kt], 0, 0, 0);
-      }
+    if (it + 1 < cnt) {   // next block's K and V^T travel while this one is computed
+      const int64_t jn = dense ? it + 1 : idx[it + 1];
+      fetch_tile(kr, kb, jn, tid);
+      fetch_tile(vr, vb, jn, tid);
     }
 
-    // Online softmax (log2 domain).
-    float mx = s[0][0];
+    // Two halves of 64 keys each; the lazily raised max makes them independent.
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int hb = 0; hb < 2; ++hb) {
+      // S^T: the A operand row of lane l32 is key kperm(l32) (bits 2 and 3 of l32
+      // swapped), so output register r of lane (l32, hl) holds query l32 and key
+      // 32*kt + 16*(r/8) + 8*hl + r%8, kt = 2*hb + t: each group of 8 registers is
+      // 8 consecutive keys.
+      f32x16 s[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx * c);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    float rs = 0.0f;
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+        for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], c, -m_new));
-        s[kt][r] = p;
-        rs += p;
-      }
-    l = l * alpha + rs;
-    m = m_new;
+      for (int st = 0; st < 8; ++st)
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-
-    // P^T as B operand: slot (hl, e) of k-step (kt, ks) is key
-    // 32*kt + 16*ks + 8*(e/4) + 4*hl + e%4, i.e. registers 8*ks .. 8*ks+7.
-    bf16x8 pf[4][2];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[kt][ks][e] = (__bf16)s[kt][8 * ks + e];
-
-    // O^T += V^T P^T; A operand: row d, the same permuted keys.
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int d = 32 * db + l32;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int c0 = 4 * kt + 2 * ks;
-          const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(sV + swz(d, c0) + 8 * hl);
-          const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(sV + swz(d, c0 + 1) + 8 * hl);
-          const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kt][ks], o[db], 0, 0, 0);
+        for (int t = 0; t < 2; ++t) {
+          const int key = 32 * (2 * hb + t) + kperm;
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(sK + swz(key, 2 * st + hl));
+          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s[t], 0, 0, 0);
         }
+
+      // Online softmax in the log2 domain: the max is raised only when it grows by > 8.
+      float mq[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float a0 = max4(s[t][0], s[t][1], s[t][2], s[t][3]);
+        const float a1 = max4(s[t][4], s[t][5], s[t][6], s[t][7]);
+        const float a2 = max4(s[t][8], s[t][9], s[t][10], s[t][11]);
+        const float a3 = max4(s[t][12], s[t][13], s[t][14], s[t][15]);
+        mq[t] = max4(a0, a1, a2, a3);
+      }
+      float mx = fmaxf(mq[0], mq[1]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+      if (__any(mx > m + 8.0f)) {
+        const float m_new = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        m = m_new;
+      }
+      float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -m));
+          s[t][r] = p;
+          rs[r & 3] += p;
+        }
+      l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+
+      // P^T as B operand of k-step (kt, ks): registers 8*ks .. 8*ks+7, which are
+      // keys 32*kt + 16*ks + 8*hl + (0..7).
+      bf16x8 pf[2][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pf[t][ks][e] = (__bf16)s[t][8 * ks + e];
+
+      // O^T += V^T P^T; A operand: row d, the same permuted keys.
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            // A operand: row d of V^T, the same 8 consecutive keys (one 16-byte chunk).
+            const int d = 32 * db + l32;
+            const bf16x8 va = *reinterpret_cast<const bf16x8*>(
+                sV + swz(d, 4 * (2 * hb + t) + 2 * ks + hl));
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[t][ks], o[db], 0, 0, 0);
+          }
     }
   }
 
@@ -184,8 +238,9 @@ void k_attn_fwd(Geo g, AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attention(const Geo& g, const AttnArgs& a, hipStream_t s) {
-  const int64_t rows = g.bh * g.n_tiles;
-  hipLaunchKernelGGL(k_attn_fwd, dim3((unsigned)rows), dim3(256), 0, s, g, a);
+  const int64_t slice = (g.n_tiles + 7) / 8;
+  const int64_t blocks = g.bh * slice * 8;
+  hipLaunchKernelGGL(k_attn_fwd, dim3((unsigned)blocks), dim3(256), 0, s, g, a, slice);
   return hipGetLastError();
 }
 
