@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--workload", default="720p-10s")
     ap.add_argument("--dense-steps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--materialised", action="store_true",
+                    help="permute Q/K to tile-major and unpermute O in separate kernels "
+                         "instead of gathering blocks inside the attention kernel")
     ap.add_argument("--cpu-rows", type=int, default=1800,
                     help="query-block rows of head 0 in the CPU oracle sample")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -137,7 +140,8 @@ def main():
     qd, kd, vd = dev(q), dev(k), dev(v)
     g = m.make_geom(wl.batch, wl.heads, wl.T, wl.H, wl.W, tile=wl.tile)
     p = m.make_params(win=wl.win, topk=wl.topk)
-    plan = m.SstaPlan(g, p)
+    fused = not args.materialised
+    plan = m.SstaPlan(g, p, fused_io=fused)
     stream = torch.cuda.current_stream()
 
     phases = ("tile_pool", "select", "attention", "unpermute")
@@ -184,7 +188,7 @@ def main():
     # Dense reference: the same pipeline with every block kept.
     dense_ms = dense_attn_ms = None
     if args.dense_steps > 0:
-        dplan = m.SstaPlan(g, p, dense=True)
+        dplan = m.SstaPlan(g, p, dense=True, fused_io=fused)
         dplan.run(qd, kd, vd)
         torch.cuda.synchronize()
         de = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -218,8 +222,9 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, q, k, v, args.cpu_rows)
 
-    pool_bytes = 6 * wl.batch * wl.heads * wl.n_tokens * 128 * 2 + \
-        2 * wl.batch * wl.heads * n * 128 * 4
+    # tile_pool traffic: Q read (+ written tile-major when materialised), K and V read + written
+    tensor = wl.batch * wl.heads * wl.n_tokens * 128 * 2
+    pool_bytes = (5 if fused else 6) * tensor + 2 * wl.batch * wl.heads * n * 128 * 4
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -238,6 +243,8 @@ def main():
             "batch": wl.batch, "heads": wl.heads, "head_dim": wl.head_dim,
             "grid": [wl.T, wl.H, wl.W], "tile": list(wl.tile), "window_half": list(wl.win),
             "topk": wl.topk, "n_tiles": n, "seq_len": wl.n_tokens,
+            "block_io": ("query blocks gathered / output scattered in the attention kernel"
+                         if fused else "query blocks and output materialised tile-major"),
             "input": "smooth 3D sinusoid field + N(0, 0.5^2) noise, bf16, seed %d" % wl.seed,
         },
         "pct_bf16_peak_step": round(100 * value / PEAK_BF16_TFLOPS, 2),

@@ -65,3 +65,17 @@ def sample_rows(wl, count: int, seed: int = 0) -> np.ndarray:
 def compare_o(o_gpu_rows: np.ndarray, o_ref: np.ndarray):
     err = np.abs(o_gpu_rows.astype(np.float64) - o_ref)
     return float(err.max()), float(err.mean())
+
+
+def token_rows(wl, rows):
+    """[len(rows), 128] token indices of the query rows (b*heads+h)*n_tiles + i, in in-block order."""
+    n = wl.n_tiles
+    return np.array([[oracle.tile_to_token(wl, int(r) % n, t) for t in range(128)] for r in rows])
+
+
+def o_rows(wl, o_tok: torch.Tensor, rows) -> np.ndarray:
+    """fp32 O rows [len(rows), 128, 128] gathered from a token-major output."""
+    o = o_tok.float().cpu().numpy().reshape(wl.batch * wl.heads, wl.n_tokens, 128)
+    tok = token_rows(wl, rows)
+    bh = np.asarray(rows) // wl.n_tiles
+    return o[bh[:, None], tok]

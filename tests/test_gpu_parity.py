@@ -12,8 +12,8 @@ import torch
 
 import oracle
 import synthetic_inputs as si
-from _helpers import (LSE_ABS, O_MAX_ABS, O_MEAN_ABS, bits, compare_o, geom_of, params_of,
-                      sample_rows, to_dev)
+from _helpers import (LSE_ABS, O_MAX_ABS, O_MEAN_ABS, bits, compare_o, geom_of, o_rows,
+                      params_of, sample_rows, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,9 +31,10 @@ def _case(name, flags=0):
     return _cache[key]
 
 
-def _plan(wl, flags=0, bitmask=True, dense=False):
+def _plan(wl, flags=0, bitmask=True, dense=False, fused_io=True):
     import video_dit_block_tile_amd as m
-    return m.SstaPlan(geom_of(wl), params_of(wl, flags), bitmask=bitmask, dense=dense)
+    return m.SstaPlan(geom_of(wl), params_of(wl, flags), bitmask=bitmask, dense=dense,
+                      fused_io=fused_io)
 
 
 @pytest.mark.parametrize("name", SMALL)
@@ -105,30 +106,44 @@ def test_selection_and_lists_bit_exact(name):
 
 def _check_attention(wl, q, k, v, sel, plan, rows):
     o_ref, lse_ref = oracle.attention(wl, q, k, v, sel["kv_idx"], sel["kv_cnt"], rows)
-    o_t = plan.o_t.float().cpu().numpy().reshape(-1, 128, 128)[rows]
-    mx, mean = compare_o(o_t, o_ref)
+    mx, mean = compare_o(o_rows(wl, plan.o, rows), o_ref)
     assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS, (mx, mean)
     lse = plan.lse.cpu().numpy().reshape(-1, 128)[rows]
     assert np.max(np.abs(lse - lse_ref)) <= LSE_ABS
-    # the token-major output holds the same values at the tokens' positions
-    o_tok = bits(plan.o).reshape(wl.batch * wl.heads, wl.n_tokens, 128)
-    o_til = bits(plan.o_t).reshape(-1, 128, 128)
-    n = wl.n_tiles
-    for row in rows[:8]:
-        bh, i = divmod(int(row), n)
-        toks = [oracle.tile_to_token(wl, i, r) for r in range(128)]
-        assert np.array_equal(o_tok[bh][toks], o_til[row])
     return mx, mean
 
 
 @pytest.mark.parametrize("name", SMALL)
-def test_attention_vs_oracle(name):
+@pytest.mark.parametrize("fused", [True, False])
+def test_attention_vs_oracle(name, fused):
     wl, q, k, v, sel = _case(name)
-    plan = _plan(wl)
+    plan = _plan(wl, fused_io=fused)
     plan.run(to_dev(q), to_dev(k), to_dev(v))
     torch.cuda.synchronize()
     rows = sample_rows(wl, 48)
     _check_attention(wl, q, k, v, sel, plan, rows)
+    if not fused:
+        # the tile-major output holds the same bits as the token-major one
+        o_tok = bits(plan.o).reshape(wl.batch * wl.heads, wl.n_tokens, 128)
+        o_til = bits(plan.o_t).reshape(-1, 128, 128)
+        for row in rows[:8]:
+            bh, i = divmod(int(row), wl.n_tiles)
+            toks = [oracle.tile_to_token(wl, i, r) for r in range(128)]
+            assert np.array_equal(o_tok[bh][toks], o_til[row])
+
+
+@pytest.mark.parametrize("name", ["grid32-w1-k2", "ragged", "dup-ties", "wide-k"])
+def test_fused_io_matches_materialised(name):
+    """Gathering blocks inside the kernel gives the same bits as permuting first."""
+    wl, q, k, v, sel = _case(name)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    a = _plan(wl, fused_io=True)
+    b = _plan(wl, fused_io=False)
+    a.run(qd, kd, vd)
+    b.run(qd, kd, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(a.o, b.o)
+    assert torch.equal(a.lse, b.lse)
 
 
 def test_attention_unit_values():
@@ -150,7 +165,7 @@ def test_dense_equals_all_kept():
     sparse.run(qd, kd, vd)
     dense.run(qd, kd, vd)
     torch.cuda.synchronize()
-    assert torch.equal(sparse.o_t, dense.o_t)
+    assert torch.equal(sparse.o, dense.o)
     assert torch.equal(sparse.lse, dense.lse)
 
 
@@ -179,7 +194,7 @@ def test_flag_variants(flags):
     assert np.array_equal(plan.kv_idx.cpu().numpy(), sel["kv_idx"])
     rows = np.arange(wl.batch * wl.heads * wl.n_tiles)
     o_ref, lse_ref = oracle.attention(wl, q, k, v, sel["kv_idx"], sel["kv_cnt"], rows)
-    o_t = plan.o_t.float().cpu().numpy().reshape(-1, 128, 128)
+    o_t = o_rows(wl, plan.o, rows)
     mx, mean = compare_o(o_t, o_ref)
     assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS
     lse = plan.lse.cpu().numpy().reshape(-1, 128)

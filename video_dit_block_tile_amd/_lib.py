@@ -67,6 +67,8 @@ SIGNATURES = {
     "ssta_scores": (ctypes.c_int, [_G, _P, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "ssta_build_mask": (ctypes.c_int, [_G, _P, _vp, _vp, _vp, _vp, _vp]),
     "ssta_attention_fwd": (ctypes.c_int, [_G, _P, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
+    "ssta_attention_fwd_tokens": (ctypes.c_int,
+                                  [_G, _P, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "ssta_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ssta_last_hip_error": (ctypes.c_int, []),
 }
@@ -259,3 +261,26 @@ def ssta_attention_fwd(g: SstaGeom, p: SstaParams, q_t, k_t, v_t, kv_idx, kv_cnt
         _expect("kv_idx", kv_idx, (g.batch, g.heads, g.n_tiles, mk), torch.int32)
     _call("ssta_attention_fwd", ctypes.byref(g), ctypes.byref(p), _ptr(q_t), _ptr(k_t), _ptr(v_t),
           _ptr(kv_idx), _ptr(kv_cnt), mk, _ptr(o_t), _ptr(lse), _stream(stream))
+
+
+def ssta_attention_fwd_tokens(g: SstaGeom, p: SstaParams, q, k_t, v_t, kv_idx, kv_cnt, o,
+                              lse=None, stream=None):
+    """Attention with token-major q and o (query gather / output scatter inside the kernel)."""
+    tok = (g.batch, g.heads, g.n_tokens, g.head_dim)
+    _expect("q", q, tok, torch.bfloat16)
+    _expect("k_t", k_t, _tiled_shape(g), torch.bfloat16)
+    _expect("v_t", v_t, (g.batch, g.heads, g.n_tiles, g.head_dim, g.tile_tokens),
+            torch.bfloat16)
+    _expect("o", o, tok, torch.bfloat16)
+    _expect("lse", lse, (g.batch, g.heads, g.n_tiles, g.tile_tokens), torch.float32,
+            allow_none=True)
+    if kv_cnt is None:
+        if kv_idx is not None:
+            raise ValueError("dense attention takes neither kv_idx nor kv_cnt")
+        mk = 0
+    else:
+        _expect("kv_cnt", kv_cnt, (g.batch, g.heads, g.n_tiles), torch.int32)
+        mk = kv_idx.shape[-1]
+        _expect("kv_idx", kv_idx, (g.batch, g.heads, g.n_tiles, mk), torch.int32)
+    _call("ssta_attention_fwd_tokens", ctypes.byref(g), ctypes.byref(p), _ptr(q), _ptr(k_t),
+          _ptr(v_t), _ptr(kv_idx), _ptr(kv_cnt), mk, _ptr(o), _ptr(lse), _stream(stream))

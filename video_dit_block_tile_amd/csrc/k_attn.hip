@@ -31,7 +31,8 @@
 // live score registers and keeps two waves per SIMD without spills.
 // Softmax: the running max is only raised when some query's max grows by more
 // than 8 in the log2 domain (probabilities stay below 2^8), so the O rescale
-// is skipped on most blocks.
+// is skipped on most blocks; the denominator is summed from the bf16-rounded
+// probabilities with v_dot2 (the same weights the P.V product uses).
 //
 // Work per kept pair: 4*128^3 = 8.39 MFLOP on the matrix cores, 64 KB of
 // K/V^T reads.  Bound: bf16 MFMA throughput (and the fp32 softmax that must
@@ -45,6 +46,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTileBytes = kTileTokens * kHeadDim * 2;   // 32 KB
 
@@ -62,6 +64,20 @@ __device__ __forceinline__ void fetch_tile(u32x4 (&r)[8], const uint8_t* base, i
     r[mm] = *reinterpret_cast<const u32x4*>(tile + off + 4096u * mm);
 }
 
+// Token index of the first token of block j within one (batch, head).
+__device__ __forceinline__ int64_t block_origin(const Geo& g, int64_t j) {
+  const int64_t bt = j / ((int64_t)g.ny * g.nx), by = (j / g.nx) % g.ny, bx = j % g.nx;
+  return ((bt * g.tt) * g.H + by * g.th) * (int64_t)g.W + bx * g.tw;
+}
+
+// Token offset (from the block's first token) of in-block position r; block
+// sizes are powers of two because their product is 128.
+__device__ __forceinline__ uint32_t in_block_offset(const Geo& g, int r) {
+  const int ltw = __builtin_ctz(g.tw), lth = __builtin_ctz(g.th);
+  const int it = r >> (ltw + lth), iy = (r >> ltw) & (g.th - 1), ix = r & (g.tw - 1);
+  return (uint32_t)((it * g.H + iy) * g.W + ix);
+}
+
 __device__ __forceinline__ void stage_tile(uint8_t* lds, const u32x4 (&r)[8], int tid) {
 #pragma unroll
   for (int mm = 0; mm < 8; ++mm) {
@@ -70,10 +86,15 @@ __device__ __forceinline__ void stage_tile(uint8_t* lds, const u32x4 (&r)[8], in
   }
 }
 
-__device__ __forceinline__ float max4(float a, float b, float c, float d) {
-  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return fmaxf(a, fmaxf(b, c));
 }
 
+// kTok: Q and O are token-major [B, h, T*H*W, 128] (the query block is
+// gathered and the output scattered directly); otherwise they are tile-major
+// [B, h, n_tiles, 128, 128].  K is always tile-major: each K block is re-read
+// by every query block that keeps it, so it pays to store it contiguously.
+template <bool kTok>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kTileBytes];
@@ -93,9 +114,15 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   const int kperm = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
   constexpr int64_t kTileElems = kTileTokens * kHeadDim;
 
+  // qb: this lane's query row is qb + (kTok ? 0 : qrow * 128).
   const uint16_t* qb = static_cast<const uint16_t*>(a.q_t) + row * kTileElems;
   const uint8_t* kb = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(a.k_t) +
                                                        bh * g.n_tiles * kTileElems);
+  if (kTok) {
+    // bh * N tokens precede this head; each lane reads its own query row.
+    const uint16_t* qhead = static_cast<const uint16_t*>(a.q_t) + bh * g.N * kHeadDim;
+    qb = qhead + (block_origin(g, qi) + in_block_offset(g, wave * 32 + (lane & 31))) * kHeadDim;
+  }
   const uint8_t* vb = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(a.v_t) +
                                                        bh * g.n_tiles * kTileElems);
   const bool dense = a.kv_cnt == nullptr;
@@ -107,7 +134,7 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   bf16x8 qf[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s)
-    qf[s] = *reinterpret_cast<const bf16x8*>(qb + qrow * kHeadDim + 16 * s + 8 * hl);
+    qf[s] = *reinterpret_cast<const bf16x8*>(qb + (kTok ? 0 : qrow * kHeadDim) + 16 * s + 8 * hl);
 
   f32x16 o[4];
 #pragma unroll
@@ -117,6 +144,7 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   float m = -INFINITY;   // running (possibly stale) max of the log2-scaled scores
   float l = 0.0f;        // this lane's part of the running denominator
   const float c = a.scale_log2;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   u32x4 kr[8], vr[8];
   if (cnt > 0) {
@@ -161,11 +189,14 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
       float mq[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const float a0 = max4(s[t][0], s[t][1], s[t][2], s[t][3]);
-        const float a1 = max4(s[t][4], s[t][5], s[t][6], s[t][7]);
-        const float a2 = max4(s[t][8], s[t][9], s[t][10], s[t][11]);
-        const float a3 = max4(s[t][12], s[t][13], s[t][14], s[t][15]);
-        mq[t] = max4(a0, a1, a2, a3);
+        float x = max3f(s[t][0], s[t][1], s[t][2]);
+        x = max3f(x, s[t][3], s[t][4]);
+        x = max3f(x, s[t][5], s[t][6]);
+        x = max3f(x, s[t][7], s[t][8]);
+        x = max3f(x, s[t][9], s[t][10]);
+        x = max3f(x, s[t][11], s[t][12]);
+        x = max3f(x, s[t][13], s[t][14]);
+        mq[t] = fmaxf(x, s[t][15]);
       }
       float mx = fmaxf(mq[0], mq[1]);
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
@@ -179,26 +210,27 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
           for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
         m = m_new;
       }
-      float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -m));
-          s[t][r] = p;
-          rs[r & 3] += p;
-        }
-      l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 
       // P^T as B operand of k-step (kt, ks): registers 8*ks .. 8*ks+7, which are
-      // keys 32*kt + 16*ks + 8*hl + (0..7).
+      // keys 32*kt + 16*ks + 8*hl + (0..7).  The denominator sums the
+      // bf16-rounded probabilities (the weights the P.V product uses) with v_dot2.
       bf16x8 pf[2][2];
+      float l0 = 0.0f, l1 = 0.0f;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pf[t][ks][e] = (__bf16)s[t][8 * ks + e];
+          for (int e = 0; e < 8; ++e)
+            pf[t][ks][e] =
+                (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * ks + e], c, -m));
+          const bf16x8 v = pf[t][ks];
+          l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), ones, l0, false);
+          l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), ones, l1, false);
+          l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), ones, l0, false);
+          l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), ones, l1, false);
+        }
+      l += l0 + l1;
 
       // O^T += V^T P^T; A operand: row d, the same permuted keys.
 #pragma unroll
@@ -220,6 +252,9 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   const float lt = l + __shfl_xor(l, 32);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   uint16_t* ob = static_cast<uint16_t*>(a.o_t) + row * kTileElems + qrow * kHeadDim;
+  if (kTok)
+    ob = static_cast<uint16_t*>(a.o_t) +
+         (bh * g.N + block_origin(g, qi) + in_block_offset(g, qrow)) * kHeadDim;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -240,7 +275,10 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
 hipError_t launch_attention(const Geo& g, const AttnArgs& a, hipStream_t s) {
   const int64_t slice = (g.n_tiles + 7) / 8;
   const int64_t blocks = g.bh * slice * 8;
-  hipLaunchKernelGGL(k_attn_fwd, dim3((unsigned)blocks), dim3(256), 0, s, g, a, slice);
+  if (a.token_io)
+    hipLaunchKernelGGL(k_attn_fwd<true>, dim3((unsigned)blocks), dim3(256), 0, s, g, a, slice);
+  else
+    hipLaunchKernelGGL(k_attn_fwd<false>, dim3((unsigned)blocks), dim3(256), 0, s, g, a, slice);
   return hipGetLastError();
 }
 

@@ -295,17 +295,17 @@ int ssta_build_mask(const ssta_geom_t* g, const ssta_params_t* p, const int32_t*
   return hip_status(ssta::launch_build_mask(geo, ma, as_stream(stream)));
 }
 
-int ssta_attention_fwd(const ssta_geom_t* g, const ssta_params_t* p, const void* q_t,
-                       const void* k_t, const void* v_t, const int32_t* kv_idx,
-                       const int32_t* kv_cnt, int32_t max_kept_, void* o_t, float* lse,
-                       void* stream) {
+namespace {
+int attention_common(const ssta_geom_t* g, const ssta_params_t* p, const void* q, const void* k,
+                     const void* v_t, const int32_t* kv_idx, const int32_t* kv_cnt,
+                     int32_t max_kept_, void* o, float* lse, void* stream, int token_io) {
   Geo geo;
   SSTA_TRY(check_geom(g, &geo));
   SSTA_TRY(check_params(p));
-  SSTA_TRY(check_ptr(q_t, false));
-  SSTA_TRY(check_ptr(k_t, false));
+  SSTA_TRY(check_ptr(q, false));
+  SSTA_TRY(check_ptr(k, false));
   SSTA_TRY(check_ptr(v_t, false));
-  SSTA_TRY(check_ptr(o_t, false));
+  SSTA_TRY(check_ptr(o, false));
   SSTA_TRY(check_ptr(lse, true));
   const bool dense = kv_cnt == nullptr;
   if (dense) {
@@ -317,16 +317,32 @@ int ssta_attention_fwd(const ssta_geom_t* g, const ssta_params_t* p, const void*
   }
   SSTA_TRY(check_device());
   ssta::AttnArgs aa;
-  aa.q_t = q_t;
-  aa.k_t = k_t;
+  aa.q_t = q;
+  aa.k_t = k;
   aa.v_t = v_t;
   aa.kv_idx = kv_idx;
   aa.kv_cnt = kv_cnt;
   aa.max_kept = max_kept_;
-  aa.o_t = o_t;
+  aa.o_t = o;
   aa.lse = lse;
   aa.scale_log2 = p->scale * 1.44269504088896340736f;
+  aa.token_io = token_io;
   return hip_status(ssta::launch_attention(geo, aa, as_stream(stream)));
+}
+}  // namespace
+
+int ssta_attention_fwd(const ssta_geom_t* g, const ssta_params_t* p, const void* q_t,
+                       const void* k_t, const void* v_t, const int32_t* kv_idx,
+                       const int32_t* kv_cnt, int32_t max_kept_, void* o_t, float* lse,
+                       void* stream) {
+  return attention_common(g, p, q_t, k_t, v_t, kv_idx, kv_cnt, max_kept_, o_t, lse, stream, 0);
+}
+
+int ssta_attention_fwd_tokens(const ssta_geom_t* g, const ssta_params_t* p, const void* q,
+                              const void* k_t, const void* v_t, const int32_t* kv_idx,
+                              const int32_t* kv_cnt, int32_t max_kept_, void* o, float* lse,
+                              void* stream) {
+  return attention_common(g, p, q, k_t, v_t, kv_idx, kv_cnt, max_kept_, o, lse, stream, 1);
 }
 
 const char* ssta_status_string(int status) {

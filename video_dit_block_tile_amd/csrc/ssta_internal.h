@@ -89,6 +89,7 @@ struct AttnArgs {
   void* o_t;
   float* lse;
   float scale_log2;        // softmax scale * log2(e)
+  int32_t token_io;        // 1: q_t, k_t, o_t are token-major [B, h, N, 128]
 };
 hipError_t launch_attention(const Geo& g, const AttnArgs& a, hipStream_t s);
 

@@ -1,15 +1,18 @@
 """The whole SSTA forward as one sequence of C-ABI calls on one stream.
 
 ``SstaPlan`` allocates every buffer once for a geometry (PyTorch is only the
-allocator here) and ``run`` enqueues the five steps:
+allocator here) and ``run`` enqueues the steps.  Default (``fused_io=True``):
 
-  1. ssta_tile_pool      Q -> tile-major Q_t + block means  (Step 1 + Step 2 pooling)
-                         K -> tile-major K_t + block means
-                         V -> dim-major tiles V_t
-  2. ssta_score_select   block means -> top-k key blocks per query block  (Step 2)
-  3. ssta_build_mask     top-k + sliding-tile window -> kept lists  (Steps 3-4)
-  4. ssta_attention_fwd  block-sparse attention -> O_t, LSE  (Step 4)
-  5. ssta_tile_unpermute O_t -> token-major O
+  1. ssta_tile_pool            Q -> block means; K -> tile-major K_t + block
+                               means; V -> dim-major tiles V_t  (Step 1 + Step 2 pooling)
+  2. ssta_score_select         block means -> top-k key blocks per query block  (Step 2)
+  3. ssta_build_mask           top-k + sliding-tile window -> kept lists  (Steps 3-4)
+  4. ssta_attention_fwd_tokens block-sparse attention, reading each query block
+                               from token order and writing O in token order  (Step 4)
+
+With ``fused_io=False`` the query gather is materialised instead: step 1 also
+writes tile-major Q_t, step 4 is ssta_attention_fwd, and ssta_tile_unpermute
+brings O_t back to token order.  Both give bit-identical O.
 
 (Steps as numbered in the "HunyuanVideo 1.5 Technical Report" summary page,
 section "SSTA: Selective and Sliding Tile Attention".)
@@ -23,16 +26,19 @@ from . import _lib as L
 
 class SstaPlan:
     def __init__(self, geom: L.SstaGeom, params: L.SstaParams, device="cuda",
-                 bitmask: bool = False, dense: bool = False):
-        self.geom, self.params, self.dense = geom, params, dense
+                 bitmask: bool = False, dense: bool = False, fused_io: bool = True):
+        self.geom, self.params, self.dense, self.fused_io = geom, params, dense, fused_io
         g = geom
         dev = torch.device(device)
         n, R, D = g.n_tiles, g.tile_tokens, g.head_dim
         bh = (g.batch, g.heads)
-        self.q_t = torch.empty(bh + (n, R, D), dtype=torch.bfloat16, device=dev)
-        self.k_t = torch.empty_like(self.q_t)
+        self.k_t = torch.empty(bh + (n, R, D), dtype=torch.bfloat16, device=dev)
+        if fused_io:
+            self.q_t = self.o_t = None
+        else:
+            self.q_t = torch.empty_like(self.k_t)
+            self.o_t = torch.empty_like(self.k_t)
         self.v_t = torch.empty(bh + (n, D, R), dtype=torch.bfloat16, device=dev)
-        self.o_t = torch.empty_like(self.q_t)
         self.o = torch.empty(bh + (g.n_tokens, D), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty(bh + (n, R), dtype=torch.float32, device=dev)
         self.q_pooled = torch.empty(bh + (n, D), dtype=torch.float32, device=dev)
@@ -50,6 +56,7 @@ class SstaPlan:
     # individual steps -----------------------------------------------------
     def tile_pool(self, q, k, v, stream=None):
         g = self.geom
+        self._q = q
         L.ssta_tile_pool(g, q, self.q_t, L.LAYOUT_TOKEN_MAJOR, self.q_pooled, stream)
         L.ssta_tile_pool(g, k, self.k_t, L.LAYOUT_TOKEN_MAJOR, self.k_pooled, stream)
         L.ssta_tile_pool(g, v, self.v_t, L.LAYOUT_DIM_MAJOR, None, stream)
@@ -62,17 +69,21 @@ class SstaPlan:
         L.ssta_build_mask(g, p, self.topk_idx, self.kv_idx, self.kv_cnt, self.bitmask, stream)
 
     def attend(self, stream=None, dense=None):
+        """Attention for the inputs of the last tile_pool call."""
         dense = self.dense if dense is None else dense
         g, p = self.geom, self.params
-        if dense:
-            L.ssta_attention_fwd(g, p, self.q_t, self.k_t, self.v_t, None, None, self.o_t,
-                                 self.lse, stream)
+        idx, cnt = (None, None) if dense else (self.kv_idx, self.kv_cnt)
+        if self.fused_io:
+            L.ssta_attention_fwd_tokens(g, p, self._q, self.k_t, self.v_t, idx, cnt, self.o,
+                                        self.lse, stream)
         else:
-            L.ssta_attention_fwd(g, p, self.q_t, self.k_t, self.v_t, self.kv_idx, self.kv_cnt,
-                                 self.o_t, self.lse, stream)
+            L.ssta_attention_fwd(g, p, self.q_t, self.k_t, self.v_t, idx, cnt, self.o_t,
+                                 self.lse, stream)
 
     def unpermute(self, stream=None):
-        L.ssta_tile_unpermute(self.geom, self.o_t, self.o, stream)
+        """Token-order O (a no-op for the fused path, which writes it directly)."""
+        if not self.fused_io:
+            L.ssta_tile_unpermute(self.geom, self.o_t, self.o, stream)
 
     # whole forward --------------------------------------------------------
     def run(self, q, k, v, stream=None):
@@ -85,8 +96,9 @@ class SstaPlan:
         return self.o, self.lse
 
 
-def ssta_forward(q, k, v, geom: L.SstaGeom, params: L.SstaParams, dense: bool = False):
+def ssta_forward(q, k, v, geom: L.SstaGeom, params: L.SstaParams, dense: bool = False,
+                 fused_io: bool = True):
     """One-shot SSTA forward on bf16 [B, h, T*H*W, 128] device tensors."""
-    plan = SstaPlan(geom, params, device=q.device, dense=dense)
+    plan = SstaPlan(geom, params, device=q.device, dense=dense, fused_io=fused_io)
     o, lse = plan.run(q, k, v)
     return o, lse, plan
