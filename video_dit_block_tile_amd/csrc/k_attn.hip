@@ -45,23 +45,53 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTileBytes = kTileTokens * kHeadDim * 2;   // 32 KB
+constexpr int kHalfBytes = kTileBytes / 2;               // 16 KB: 64 keys of K or V^T
+constexpr unsigned kWaitVm0 = 0x0F70;                    // s_waitcnt vmcnt(0)
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-__device__ __forceinline__ int swz(int row, int chunk) {
+// K half slot: 64 key rows of 256 B; 16-byte chunk c of row r sits at chunk c ^ (r % 16).
+__device__ __forceinline__ int swz_k(int row, int chunk) {
   return row * 256 + ((chunk ^ (row & 15)) << 4);
 }
+// V^T half slot: 128 channel rows of 128 B (64 keys); chunk c of row d sits at
+// chunk c ^ ((d / 2) % 8), so 16 consecutive rows read the same chunk from 16
+// distinct bank groups.
+__device__ __forceinline__ int swz_v(int d, int chunk) {
+  return d * 128 + ((chunk ^ ((d >> 1) & 7)) << 4);
+}
 
-// Loads one 32 KB tile (K or V^T) of block j into registers: 8 x 16 B per thread.
-__device__ __forceinline__ void fetch_tile(u32x4 (&r)[8], const uint8_t* base, int64_t j,
-                                           int tid) {
-  const uint8_t* tile = base + j * kTileBytes;     // uniform across the workgroup
-  const uint32_t off = (uint32_t)tid * 16u;
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return fmaxf(a, fmaxf(b, c));
+}
+
+// Direct global->LDS loads (global_load_lds_dwordx4) of half h of one block.
+// Each of the 4 waves issues 4 instructions of 1 KB; lane i of an instruction
+// lands at byte 16*i of its 1 KB destination block, so the source address of
+// each lane is chosen to put the right chunk there.
+__device__ __forceinline__ void dma_k_half(lds_u8* dst, const uint8_t* tile, int h, int wave,
+                                           int lane) {
 #pragma unroll
-  for (int mm = 0; mm < 8; ++mm)
-    r[mm] = *reinterpret_cast<const u32x4*>(tile + off + 4096u * mm);
+  for (int mm = 0; mm < 4; ++mm) {
+    const int b = 4 * wave + mm;            // rows 4b .. 4b+3 of the half
+    const int row = 4 * b + (lane >> 4);
+    const int lc = (lane & 15) ^ (row & 15);
+    __builtin_amdgcn_global_load_lds(tile + (64 * h + row) * 256 + lc * 16, dst + b * 1024, 16,
+                                     0, 0);
+  }
+}
+__device__ __forceinline__ void dma_v_half(lds_u8* dst, const uint8_t* tile, int h, int wave,
+                                           int lane) {
+#pragma unroll
+  for (int mm = 0; mm < 4; ++mm) {
+    const int b = 4 * wave + mm;            // channel rows 8b .. 8b+7
+    const int d = 8 * b + (lane >> 3);
+    const int lc = (lane & 7) ^ ((d >> 1) & 7);
+    __builtin_amdgcn_global_load_lds(tile + d * 256 + 128 * h + lc * 16, dst + b * 1024, 16, 0,
+                                     0);
+  }
 }
 
 // Token index of the first token of block j within one (batch, head).
@@ -78,17 +108,7 @@ __device__ __forceinline__ uint32_t in_block_offset(const Geo& g, int r) {
   return (uint32_t)((it * g.H + iy) * g.W + ix);
 }
 
-__device__ __forceinline__ void stage_tile(uint8_t* lds, const u32x4 (&r)[8], int tid) {
-#pragma unroll
-  for (int mm = 0; mm < 8; ++mm) {
-    const int L = tid + 256 * mm;
-    *reinterpret_cast<u32x4*>(lds + swz(L >> 4, L & 15)) = r[mm];
-  }
-}
 
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  return fmaxf(a, fmaxf(b, c));
-}
 
 // kTok: Q and O are token-major [B, h, T*H*W, 128] (the query block is
 // gathered and the output scattered directly); otherwise they are tile-major
@@ -97,9 +117,8 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 template <bool kTok>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kTileBytes];
-  uint8_t* sK = smem;                 // [key][256 B]
-  uint8_t* sV = smem + kTileBytes;    // [d][256 B]
+  // Two-slot rings of half blocks: K slots at 0 and 16 KB, V^T slots at 32 and 48 KB.
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kHalfBytes];
 
   // Head-synchronous XCD slices (see the file comment).
   const int64_t bid = blockIdx.x;
@@ -112,17 +131,18 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hl = lane >> 5;
   const int kperm = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   constexpr int64_t kTileElems = kTileTokens * kHeadDim;
 
   // qb: this lane's query row is qb + (kTok ? 0 : qrow * 128).
   const uint16_t* qb = static_cast<const uint16_t*>(a.q_t) + row * kTileElems;
-  const uint8_t* kb = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(a.k_t) +
-                                                       bh * g.n_tiles * kTileElems);
   if (kTok) {
     // bh * N tokens precede this head; each lane reads its own query row.
     const uint16_t* qhead = static_cast<const uint16_t*>(a.q_t) + bh * g.N * kHeadDim;
     qb = qhead + (block_origin(g, qi) + in_block_offset(g, wave * 32 + (lane & 31))) * kHeadDim;
   }
+  const uint8_t* kb = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(a.k_t) +
+                                                       bh * g.n_tiles * kTileElems);
   const uint8_t* vb = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(a.v_t) +
                                                        bh * g.n_tiles * kTileElems);
   const bool dense = a.kv_cnt == nullptr;
@@ -146,106 +166,104 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   const float c = a.scale_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  u32x4 kr[8], vr[8];
-  if (cnt > 0) {
+  // Units u = 2*(list position) + half; unit u uses slot u % 2.
+  const int units = 2 * cnt;
+  if (units > 0) {
     const int64_t j0 = dense ? 0 : idx[0];
-    fetch_tile(kr, kb, j0, tid);
-    fetch_tile(vr, vb, j0, tid);
+    dma_k_half((lds_u8*)smem, kb + j0 * kTileBytes, 0, wv, lane);
+    dma_v_half((lds_u8*)(smem + 2 * kHalfBytes), vb + j0 * kTileBytes, 0, wv, lane);
   }
 
-  for (int it = 0; it < cnt; ++it) {
-    __syncthreads();   // every wave is done reading the previous block's K and V^T
-    stage_tile(sK, kr, tid);
-    stage_tile(sV, vr, tid);
-    __syncthreads();
-    if (it + 1 < cnt) {   // next block's K and V^T travel while this one is computed
-      const int64_t jn = dense ? it + 1 : idx[it + 1];
-      fetch_tile(kr, kb, jn, tid);
-      fetch_tile(vr, vb, jn, tid);
+  for (int u = 0; u < units; ++u) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's loads of unit u have landed
+    __syncthreads();                        // ... every wave's; and unit u-1 is done
+    const int slot = u & 1;
+    if (u + 1 < units) {                    // unit u+1 travels while unit u is computed
+      const int un = u + 1;
+      const int64_t jn = dense ? (un >> 1) : idx[un >> 1];
+      dma_k_half((lds_u8*)(smem + (1 - slot) * kHalfBytes), kb + jn * kTileBytes, un & 1, wv,
+                 lane);
+      dma_v_half((lds_u8*)(smem + (3 - slot) * kHalfBytes), vb + jn * kTileBytes, un & 1, wv,
+                 lane);
     }
+    const uint8_t* sK = smem + slot * kHalfBytes;
+    const uint8_t* sV = smem + (2 + slot) * kHalfBytes;
 
-    // Two halves of 64 keys each; the lazily raised max makes them independent.
+    // S^T for the unit's 64 keys: the A operand row of lane l32 is key kperm(l32)
+    // (bits 2 and 3 of l32 swapped), so output register r of lane (l32, hl) holds
+    // query l32 and key 32*t + 16*(r/8) + 8*hl + r%8 of the unit: each group of 8
+    // registers is 8 consecutive keys.
+    f32x16 s[2];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      // S^T: the A operand row of lane l32 is key kperm(l32) (bits 2 and 3 of l32
-      // swapped), so output register r of lane (l32, hl) holds query l32 and key
-      // 32*kt + 16*(r/8) + 8*hl + r%8, kt = 2*hb + t: each group of 8 registers is
-      // 8 consecutive keys.
-      f32x16 s[2];
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
-#pragma unroll
-      for (int st = 0; st < 8; ++st)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int key = 32 * (2 * hb + t) + kperm;
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(sK + swz(key, 2 * st + hl));
-          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s[t], 0, 0, 0);
-        }
-
-      // Online softmax in the log2 domain: the max is raised only when it grows by > 8.
-      float mq[2];
+    for (int st = 0; st < 8; ++st)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        float x = max3f(s[t][0], s[t][1], s[t][2]);
-        x = max3f(x, s[t][3], s[t][4]);
-        x = max3f(x, s[t][5], s[t][6]);
-        x = max3f(x, s[t][7], s[t][8]);
-        x = max3f(x, s[t][9], s[t][10]);
-        x = max3f(x, s[t][11], s[t][12]);
-        x = max3f(x, s[t][13], s[t][14]);
-        mq[t] = fmaxf(x, s[t][15]);
-      }
-      float mx = fmaxf(mq[0], mq[1]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
-      if (__any(mx > m + 8.0f)) {
-        const float m_new = fmaxf(m, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-        m = m_new;
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(sK + swz_k(32 * t + kperm, 2 * st + hl));
+        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s[t], 0, 0, 0);
       }
 
-      // P^T as B operand of k-step (kt, ks): registers 8*ks .. 8*ks+7, which are
-      // keys 32*kt + 16*ks + 8*hl + (0..7).  The denominator sums the
-      // bf16-rounded probabilities (the weights the P.V product uses) with v_dot2.
-      bf16x8 pf[2][2];
-      float l0 = 0.0f, l1 = 0.0f;
+    // Online softmax in the log2 domain: the max is raised only when it grows by > 8.
+    float mq[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            pf[t][ks][e] =
-                (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * ks + e], c, -m));
-          const bf16x8 v = pf[t][ks];
-          l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), ones, l0, false);
-          l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), ones, l1, false);
-          l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), ones, l0, false);
-          l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), ones, l1, false);
-        }
-      l += l0 + l1;
-
-      // O^T += V^T P^T; A operand: row d, the same permuted keys.
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            // A operand: row d of V^T, the same 8 consecutive keys (one 16-byte chunk).
-            const int d = 32 * db + l32;
-            const bf16x8 va = *reinterpret_cast<const bf16x8*>(
-                sV + swz(d, 4 * (2 * hb + t) + 2 * ks + hl));
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[t][ks], o[db], 0, 0, 0);
-          }
+    for (int t = 0; t < 2; ++t) {
+      float x = max3f(s[t][0], s[t][1], s[t][2]);
+      x = max3f(x, s[t][3], s[t][4]);
+      x = max3f(x, s[t][5], s[t][6]);
+      x = max3f(x, s[t][7], s[t][8]);
+      x = max3f(x, s[t][9], s[t][10]);
+      x = max3f(x, s[t][11], s[t][12]);
+      x = max3f(x, s[t][13], s[t][14]);
+      mq[t] = fmaxf(x, s[t][15]);
     }
+    float mx = fmaxf(mq[0], mq[1]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+    if (__any(mx > m + 8.0f)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      m = m_new;
+    }
+
+    // P^T as B operand of k-step (t, ks): registers 8*ks .. 8*ks+7, which are
+    // keys 32*t + 16*ks + 8*hl + (0..7) of the unit.  The denominator sums the
+    // bf16-rounded probabilities (the weights the P.V product uses) with v_dot2.
+    bf16x8 pf[2][2];
+    float l0 = 0.0f, l1 = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pf[t][ks][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * ks + e], c, -m));
+        const bf16x8 v = pf[t][ks];
+        l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), ones, l0, false);
+        l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), ones, l1, false);
+        l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), ones, l0, false);
+        l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), ones, l1, false);
+      }
+    l += l0 + l1;
+
+    // O^T += V^T P^T; A operand: row d of V^T, the same 8 consecutive keys
+    // (chunk 4*t + 2*ks + hl of the unit's 64 keys).
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(
+              sV + swz_v(32 * db + l32, 4 * t + 2 * ks + hl));
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[t][ks], o[db], 0, 0, 0);
+        }
   }
 
   // Epilogue: lane holds query qrow, channels 32*db + 8*g4 + 4*hl + (0..3).
