@@ -67,31 +67,58 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return fmaxf(a, fmaxf(b, c));
 }
 
+// Lanes l and l^32 hold the two halves of one query's keys.  v_permlane32_swap
+// with the value as both operands leaves {own, partner} in the two results (in
+// an order that depends on the half), so their max and sum are the pair's.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Direct global->LDS loads (global_load_lds_dwordx4) of half h of one block.
 // Each of the 4 waves issues 4 instructions of 1 KB; lane i of an instruction
 // lands at byte 16*i of its 1 KB destination block, so the source address of
-// each lane is chosen to put the right chunk there.
-__device__ __forceinline__ void dma_k_half(lds_u8* dst, const uint8_t* tile, int h, int wave,
-                                           int lane) {
+// each lane is chosen to put the right chunk there.  The per-lane byte offsets
+// depend only on the lane and wave (computed once); the block base is uniform,
+// so the loads use a scalar base plus a 32-bit lane offset.
+struct DmaOffsets {
+  uint32_t k[4], v[4];
+};
+
+__device__ __forceinline__ DmaOffsets dma_offsets(int wave, int lane) {
+  DmaOffsets o;
 #pragma unroll
   for (int mm = 0; mm < 4; ++mm) {
-    const int b = 4 * wave + mm;            // rows 4b .. 4b+3 of the half
-    const int row = 4 * b + (lane >> 4);
-    const int lc = (lane & 15) ^ (row & 15);
-    __builtin_amdgcn_global_load_lds(tile + (64 * h + row) * 256 + lc * 16, dst + b * 1024, 16,
-                                     0, 0);
+    const int b = 4 * wave + mm;
+    const int row = 4 * b + (lane >> 4);            // K: rows 4b .. 4b+3 of the half
+    o.k[mm] = row * 256 + (((lane & 15) ^ (row & 15)) << 4);
+    const int d = 8 * b + (lane >> 3);              // V^T: channel rows 8b .. 8b+7
+    o.v[mm] = d * 256 + (((lane & 7) ^ ((d >> 1) & 7)) << 4);
   }
+  return o;
 }
-__device__ __forceinline__ void dma_v_half(lds_u8* dst, const uint8_t* tile, int h, int wave,
-                                           int lane) {
+
+// K half h of the block at `tile`: rows 64h .. 64h+63 (16 KB contiguous).
+__device__ __forceinline__ void dma_k_half(lds_u8* dst, const uint8_t* tile, int h, int wave,
+                                           const DmaOffsets& off) {
+  const uint8_t* base = tile + h * kHalfBytes;
 #pragma unroll
-  for (int mm = 0; mm < 4; ++mm) {
-    const int b = 4 * wave + mm;            // channel rows 8b .. 8b+7
-    const int d = 8 * b + (lane >> 3);
-    const int lc = (lane & 7) ^ ((d >> 1) & 7);
-    __builtin_amdgcn_global_load_lds(tile + d * 256 + 128 * h + lc * 16, dst + b * 1024, 16, 0,
-                                     0);
-  }
+  for (int mm = 0; mm < 4; ++mm)
+    __builtin_amdgcn_global_load_lds(base + off.k[mm], dst + (4 * wave + mm) * 1024, 16, 0, 0);
+}
+// V^T half h of the block at `tile`: bytes 128h .. 128h+127 of each of the 128 rows.
+__device__ __forceinline__ void dma_v_half(lds_u8* dst, const uint8_t* tile, int h, int wave,
+                                           const DmaOffsets& off) {
+  const uint8_t* base = tile + h * 128;
+#pragma unroll
+  for (int mm = 0; mm < 4; ++mm)
+    __builtin_amdgcn_global_load_lds(base + off.v[mm], dst + (4 * wave + mm) * 1024, 16, 0, 0);
 }
 
 // Token index of the first token of block j within one (batch, head).
@@ -168,10 +195,11 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
 
   // Units u = 2*(list position) + half; unit u uses slot u % 2.
   const int units = 2 * cnt;
+  const DmaOffsets doff = dma_offsets(wv, lane);
   if (units > 0) {
     const int64_t j0 = dense ? 0 : idx[0];
-    dma_k_half((lds_u8*)smem, kb + j0 * kTileBytes, 0, wv, lane);
-    dma_v_half((lds_u8*)(smem + 2 * kHalfBytes), vb + j0 * kTileBytes, 0, wv, lane);
+    dma_k_half((lds_u8*)smem, kb + j0 * kTileBytes, 0, wv, doff);
+    dma_v_half((lds_u8*)(smem + 2 * kHalfBytes), vb + j0 * kTileBytes, 0, wv, doff);
   }
 
   for (int u = 0; u < units; ++u) {
@@ -182,9 +210,9 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
       const int un = u + 1;
       const int64_t jn = dense ? (un >> 1) : idx[un >> 1];
       dma_k_half((lds_u8*)(smem + (1 - slot) * kHalfBytes), kb + jn * kTileBytes, un & 1, wv,
-                 lane);
+                 doff);
       dma_v_half((lds_u8*)(smem + (3 - slot) * kHalfBytes), vb + jn * kTileBytes, un & 1, wv,
-                 lane);
+                 doff);
     }
     const uint8_t* sK = smem + slot * kHalfBytes;
     const uint8_t* sV = smem + (2 + slot) * kHalfBytes;
@@ -220,7 +248,7 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
       mq[t] = fmaxf(x, s[t][15]);
     }
     float mx = fmaxf(mq[0], mq[1]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+    mx = pair_max(mx) * c;
     if (__any(mx > m + 8.0f)) {
       const float m_new = fmaxf(m, mx);
       const float alpha = __builtin_amdgcn_exp2f(m - m_new);
@@ -267,7 +295,7 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   }
 
   // Epilogue: lane holds query qrow, channels 32*db + 8*g4 + 4*hl + (0..3).
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = pair_sum(l);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   uint16_t* ob = static_cast<uint16_t*>(a.o_t) + row * kTileElems + qrow * kHeadDim;
   if (kTok)
