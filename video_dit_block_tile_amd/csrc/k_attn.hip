@@ -16,8 +16,9 @@
 // lane index swapped) into the S^T product, which makes every 8 output
 // registers of a lane 8 consecutive keys; V arrives dim-major, so the matching
 // A operand of the P.V product is one 16-byte LDS read of a V^T row.
-// K and V^T tiles (32 KB each) are staged in LDS with a 16-byte-chunk XOR
-// swizzle (chunk ^ row%16) so the MFMA operand reads are conflict-free.
+// K rows and V^T rows are staged in LDS with a 16-byte-chunk XOR swizzle
+// (K: chunk ^ row%16; V^T: chunk ^ (row/2)%8) so the MFMA operand reads are
+// conflict-free.
 // Schedule: the hardware deals workgroup ids round-robin over the 8 XCDs.
 // The grid is laid out so that XCD x receives, head after head, the
 // contiguous slice [x*c, (x+1)*c) of that head's query blocks (c = ceil(n/8)).
@@ -25,14 +26,21 @@
 // and V (118 MB per head at the 720p 10 s shape) stay resident in the 256 MB
 // MALL, while within an XCD neighbouring query blocks share most of their
 // window blocks in that XCD's L2.
-// Memory: the next kept block's K and V^T are fetched into registers while
-// the current block is computed, so one global-memory round trip overlaps each
-// block.  Each block is processed as two halves of 64 keys, which halves the
-// live score registers and keeps two waves per SIMD without spills.
-// Softmax: the running max is only raised when some query's max grows by more
-// than 8 in the log2 domain (probabilities stay below 2^8), so the O rescale
-// is skipped on most blocks; the denominator is summed from the bf16-rounded
-// probabilities with v_dot2 (the same weights the P.V product uses).
+// Memory: each kept block is processed as two units of 64 keys.  A unit's K
+// rows and V^T columns (16 KB each) go straight from global memory into LDS
+// with global_load_lds_dwordx4 (no register staging) into a two-slot ring;
+// the next unit's loads are issued once the current unit's scores are on the
+// matrix cores and overlap the rest of the unit.  Kept-block ids are read 64
+// at a time into one register per lane and taken out with v_readlane, so no
+// per-unit global load sits on the critical path.
+// LDS operand reads are issued ahead of their products (up to 8 for K, the
+// first 8 V^T operands before the softmax), held in place by scheduling
+// fences; waves raise their issue priority around the matrix-core sections.
+// Softmax: the running max m is raised only when the probabilities formed
+// with the current m would exceed 2^32 on some lane (always on a row's first
+// unit), so most units need neither a max reduction nor an O rescale; the
+// denominator is summed from the bf16-rounded probabilities with v_dot2 (the
+// same weights the P.V product uses).
 //
 // Work per kept pair: 4*128^3 = 8.39 MFLOP on the matrix cores, 64 KB of
 // K/V^T reads.  Bound: bf16 MFMA throughput (and the fp32 softmax that must
@@ -48,17 +56,25 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTileBytes = kTileTokens * kHeadDim * 2;   // 32 KB
-constexpr int kHalfBytes = kTileBytes / 2;               // 16 KB: 64 keys of K or V^T
+constexpr int kSlotBytes = kTileBytes / 2;               // one unit of 64 keys: 16 KB of K or V^T
 constexpr unsigned kWaitVm0 = 0x0F70;                    // s_waitcnt vmcnt(0)
+// Scheduling fence that lets vector, scalar and transcendental ALU
+// instructions move across it but keeps matrix, LDS and global memory
+// instructions on their side, so LDS operand reads stay issued a fixed number
+// of products ahead of their use.
+// Largest per-lane probability sum of one unit accepted without raising the
+// running max (see the softmax in the kernel).
+constexpr float kMaxUnitSum = 4294967296.0f;   // 2^32
+constexpr int kFenceKeepDs = 0x0002 | 0x0004 | 0x0400;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-// K half slot: 64 key rows of 256 B; 16-byte chunk c of row r sits at chunk c ^ (r % 16).
+// K slot (64 rows of 256 B): chunk c of row r sits at chunk c ^ (r % 16).
 __device__ __forceinline__ int swz_k(int row, int chunk) {
   return row * 256 + ((chunk ^ (row & 15)) << 4);
 }
-// V^T half slot: 128 channel rows of 128 B (64 keys); chunk c of row d sits at
-// chunk c ^ ((d / 2) % 8), so 16 consecutive rows read the same chunk from 16
-// distinct bank groups.
+// V^T slot (128 channel rows of 128 B): chunk c of row d sits at chunk
+// c ^ ((d / 2) % 8), so 16 consecutive rows read one chunk from 16 distinct
+// bank groups.
 __device__ __forceinline__ int swz_v(int d, int chunk) {
   return d * 128 + ((chunk ^ ((d >> 1) & 7)) << 4);
 }
@@ -81,12 +97,12 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Direct global->LDS loads (global_load_lds_dwordx4) of half h of one block.
-// Each of the 4 waves issues 4 instructions of 1 KB; lane i of an instruction
-// lands at byte 16*i of its 1 KB destination block, so the source address of
-// each lane is chosen to put the right chunk there.  The per-lane byte offsets
-// depend only on the lane and wave (computed once); the block base is uniform,
-// so the loads use a scalar base plus a 32-bit lane offset.
+// Direct global->LDS loads (global_load_lds_dwordx4).  A slot is 16 KB: each
+// of the 4 waves issues 4 instructions of 1 KB; lane i of an instruction lands
+// at byte 16*i of its 1 KB destination block, so the source address of each
+// lane is chosen to put the right (swizzled) chunk there.  The per-lane byte
+// offsets depend only on the lane and wave (computed once); the unit base is
+// uniform, so the loads use a scalar base plus a 32-bit lane offset.
 struct DmaOffsets {
   uint32_t k[4], v[4];
 };
@@ -95,30 +111,51 @@ __device__ __forceinline__ DmaOffsets dma_offsets(int wave, int lane) {
   DmaOffsets o;
 #pragma unroll
   for (int mm = 0; mm < 4; ++mm) {
-    const int b = 4 * wave + mm;
-    const int row = 4 * b + (lane >> 4);            // K: rows 4b .. 4b+3 of the half
+    const int b = 4 * wave + mm;                 // 1 KB destination block
+    const int row = 4 * b + (lane >> 4);         // K: rows 4b .. 4b+3
     o.k[mm] = row * 256 + (((lane & 15) ^ (row & 15)) << 4);
-    const int d = 8 * b + (lane >> 3);              // V^T: channel rows 8b .. 8b+7
+    const int d = 8 * b + (lane >> 3);           // V^T: channel rows 8b .. 8b+7
     o.v[mm] = d * 256 + (((lane & 7) ^ ((d >> 1) & 7)) << 4);
   }
   return o;
 }
 
-// K half h of the block at `tile`: rows 64h .. 64h+63 (16 KB contiguous).
-__device__ __forceinline__ void dma_k_half(lds_u8* dst, const uint8_t* tile, int h, int wave,
-                                           const DmaOffsets& off) {
-  const uint8_t* base = tile + h * kHalfBytes;
+// Half p (keys 64p .. 64p+63) of a K block: 64 contiguous rows.
+__device__ __forceinline__ void dma_k(uint8_t* dst, const uint8_t* ktile, int p, int wave,
+                                      const DmaOffsets& off) {
+  const uint8_t* base = ktile + p * kSlotBytes;
 #pragma unroll
   for (int mm = 0; mm < 4; ++mm)
-    __builtin_amdgcn_global_load_lds(base + off.k[mm], dst + (4 * wave + mm) * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(base + off.k[mm], (lds_u8*)(dst + (4 * wave + mm) * 1024),
+                                     16, 0, 0);
 }
-// V^T half h of the block at `tile`: bytes 128h .. 128h+127 of each of the 128 rows.
-__device__ __forceinline__ void dma_v_half(lds_u8* dst, const uint8_t* tile, int h, int wave,
-                                           const DmaOffsets& off) {
-  const uint8_t* base = tile + h * 128;
+// Half p of a V^T block: bytes 128p .. 128p+127 of each 256-byte channel row.
+__device__ __forceinline__ void dma_v(uint8_t* dst, const uint8_t* vtile, int p, int wave,
+                                      const DmaOffsets& off) {
+  const uint8_t* base = vtile + p * 128;
 #pragma unroll
   for (int mm = 0; mm < 4; ++mm)
-    __builtin_amdgcn_global_load_lds(base + off.v[mm], dst + (4 * wave + mm) * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(base + off.v[mm], (lds_u8*)(dst + (4 * wave + mm) * 1024),
+                                     16, 0, 0);
+}
+
+// S^T for the 64 keys of a K slot: the A operand row of lane l32 is key
+// kperm(l32) (bits 2 and 3 of l32 swapped), so output register r of lane
+// (l32, hl) of s[t] holds query l32 and key 32*t + 16*(r/8) + 8*hl + r%8: each
+// group of 8 registers is 8 consecutive keys.
+__device__ __forceinline__ void scores(f32x16 (&s)[2], const uint8_t* sK, const bf16x8 (&qf)[8],
+                                       int kperm, int hl) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
+#pragma unroll
+  for (int st = 0; st < 8; ++st)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(sK + swz_k(32 * t + kperm, 2 * st + hl));
+      s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s[t], 0, 0, 0);
+    }
 }
 
 // Token index of the first token of block j within one (batch, head).
@@ -135,8 +172,6 @@ __device__ __forceinline__ uint32_t in_block_offset(const Geo& g, int r) {
   return (uint32_t)((it * g.H + iy) * g.W + ix);
 }
 
-
-
 // kTok: Q and O are token-major [B, h, T*H*W, 128] (the query block is
 // gathered and the output scattered directly); otherwise they are tile-major
 // [B, h, n_tiles, 128, 128].  K is always tile-major: each K block is re-read
@@ -144,8 +179,8 @@ __device__ __forceinline__ uint32_t in_block_offset(const Geo& g, int r) {
 template <bool kTok>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
-  // Two-slot rings of half blocks: K slots at 0 and 16 KB, V^T slots at 32 and 48 KB.
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kHalfBytes];
+  // K slots at 0 and 16 KB, V^T slots at 32 and 48 KB.
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kSlotBytes];
 
   // Head-synchronous XCD slices (see the file comment).
   const int64_t bid = blockIdx.x;
@@ -193,63 +228,113 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   const float c = a.scale_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // Units u = 2*(list position) + half; unit u uses slot u % 2.
+  // Unit u = keys 64*(u%2) .. of the (u/2)-th kept block, in slot u%2 of the
+  // K and V^T rings; unit u+1 is loaded while unit u is computed.
   const int units = 2 * cnt;
   const DmaOffsets doff = dma_offsets(wv, lane);
+  // Kept-block ids, 64 at a time: lane i holds entry ibase + i.
+  int ibase = 0;
+  int ids = (!dense && lane < cnt) ? idx[lane] : 0;
+  auto block_at = [&](int pos) -> int64_t {
+    if (dense) return pos;
+    if (pos >= ibase + 64) {   // uniform: next 64 entries
+      ibase += 64;
+      ids = (ibase + lane < cnt) ? idx[ibase + lane] : 0;
+    }
+    return __builtin_amdgcn_readlane(ids, pos - ibase);
+  };
   if (units > 0) {
-    const int64_t j0 = dense ? 0 : idx[0];
-    dma_k_half((lds_u8*)smem, kb + j0 * kTileBytes, 0, wv, doff);
-    dma_v_half((lds_u8*)(smem + 2 * kHalfBytes), vb + j0 * kTileBytes, 0, wv, doff);
+    const int64_t j0 = block_at(0);
+    dma_k(smem, kb + j0 * kTileBytes, 0, wv, doff);
+    dma_v(smem + 2 * kSlotBytes, vb + j0 * kTileBytes, 0, wv, doff);
   }
 
   for (int u = 0; u < units; ++u) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's loads of unit u have landed
     __syncthreads();                        // ... every wave's; and unit u-1 is done
     const int slot = u & 1;
-    if (u + 1 < units) {                    // unit u+1 travels while unit u is computed
-      const int un = u + 1;
-      const int64_t jn = dense ? (un >> 1) : idx[un >> 1];
-      dma_k_half((lds_u8*)(smem + (1 - slot) * kHalfBytes), kb + jn * kTileBytes, un & 1, wv,
-                 doff);
-      dma_v_half((lds_u8*)(smem + (3 - slot) * kHalfBytes), vb + jn * kTileBytes, un & 1, wv,
-                 doff);
-    }
-    const uint8_t* sK = smem + slot * kHalfBytes;
-    const uint8_t* sV = smem + (2 + slot) * kHalfBytes;
+    const uint8_t* sK = smem + slot * kSlotBytes;
+    const uint8_t* sV = smem + (2 + slot) * kSlotBytes;
 
-    // S^T for the unit's 64 keys: the A operand row of lane l32 is key kperm(l32)
-    // (bits 2 and 3 of l32 swapped), so output register r of lane (l32, hl) holds
-    // query l32 and key 32*t + 16*(r/8) + 8*hl + r%8 of the unit: each group of 8
-    // registers is 8 consecutive keys.
+    // S^T: 16 products in the order (st, t); their K operands are read
+    // kKAhead products ahead so the LDS latency overlaps the matrix cores.
+    constexpr int kKAhead = 8;
+    __builtin_amdgcn_s_setprio(1);
     f32x16 s[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
+    bf16x8 kr[kKAhead];
 #pragma unroll
-    for (int st = 0; st < 8; ++st)
+    for (int i = 0; i < kKAhead; ++i)
+      kr[i] = *reinterpret_cast<const bf16x8*>(sK + swz_k(32 * (i & 1) + kperm, 2 * (i >> 1) + hl));
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(sK + swz_k(32 * t + kperm, 2 * st + hl));
-        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s[t], 0, 0, 0);
-      }
-
-    // Online softmax in the log2 domain: the max is raised only when it grows by > 8.
-    float mq[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      float x = max3f(s[t][0], s[t][1], s[t][2]);
-      x = max3f(x, s[t][3], s[t][4]);
-      x = max3f(x, s[t][5], s[t][6]);
-      x = max3f(x, s[t][7], s[t][8]);
-      x = max3f(x, s[t][9], s[t][10]);
-      x = max3f(x, s[t][11], s[t][12]);
-      x = max3f(x, s[t][13], s[t][14]);
-      mq[t] = fmaxf(x, s[t][15]);
+    for (int i = 0; i < 16; ++i) {
+      const int st = i >> 1, t = i & 1;
+      s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i % kKAhead], qf[st], s[t], 0, 0, 0);
+      const int n = i + kKAhead;
+      if (n < 16)
+        kr[i % kKAhead] =
+            *reinterpret_cast<const bf16x8*>(sK + swz_k(32 * (n & 1) + kperm, 2 * (n >> 1) + hl));
+      __builtin_amdgcn_sched_barrier(0);
     }
-    float mx = fmaxf(mq[0], mq[1]);
-    mx = pair_max(mx) * c;
-    if (__any(mx > m + 8.0f)) {
+
+    // V^T operands of the first kVAhead P.V products (order (t, ks, db)),
+    // requested before the softmax so they arrive while it runs.
+    constexpr int kVAhead = 8;
+    bf16x8 vr[kVAhead];
+#pragma unroll
+    for (int i = 0; i < kVAhead; ++i)
+      vr[i] = *reinterpret_cast<const bf16x8*>(
+          sV + swz_v(32 * (i & 3) + l32, 4 * (i >> 3) + 2 * ((i >> 2) & 1) + hl));
+
+    __builtin_amdgcn_s_setprio(0);
+    if (u + 1 < units) {
+      const int64_t j = block_at((u + 1) >> 1);
+      dma_k(smem + (1 - slot) * kSlotBytes, kb + j * kTileBytes, (u + 1) & 1, wv, doff);
+      dma_v(smem + (3 - slot) * kSlotBytes, vb + j * kTileBytes, (u + 1) & 1, wv, doff);
+    }
+    __builtin_amdgcn_sched_barrier(kFenceKeepDs);
+
+    // Online softmax in the log2 domain against the running max m, which is
+    // only raised when needed: the probabilities are first formed with the
+    // current m; if some lane's sum over its 32 keys leaves [0, 2^32] (always
+    // on a row's first unit, where m = -inf), the unit's max is taken, O and l
+    // are rescaled and the probabilities are formed again.  Every probability
+    // that enters O is therefore at most 2^32.
+    // P^T as B operand of k-step (t, ks): registers 8*ks .. 8*ks+7, which are
+    // keys 32*t + 16*ks + 8*hl + (0..7) of the unit.  The denominator sums the
+    // bf16-rounded probabilities (the weights the P.V product uses) with v_dot2.
+    bf16x8 pf[2][2];
+    float lu;
+    auto probabilities = [&]() {
+      float l0 = 0.0f, l1 = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            pf[t][ks][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * ks + e], c, -m));
+          const bf16x8 v = pf[t][ks];
+          l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), ones, l0, false);
+          l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), ones, l1, false);
+          l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), ones, l0, false);
+          l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), ones, l1, false);
+        }
+      lu = l0 + l1;
+    };
+    probabilities();
+    if (__any(!(lu <= kMaxUnitSum))) {
+      float x0 = max3f(s[0][0], s[0][1], s[0][2]);
+      float x1 = max3f(s[1][0], s[1][1], s[1][2]);
+#pragma unroll
+      for (int r = 3; r < 15; r += 2) {
+        x0 = max3f(x0, s[0][r], s[0][r + 1]);
+        x1 = max3f(x1, s[1][r], s[1][r + 1]);
+      }
+      const float mx = pair_max(max3f(max3f(x0, x1, s[0][15]), s[1][15], -INFINITY)) * c;
       const float m_new = fmaxf(m, mx);
       const float alpha = __builtin_amdgcn_exp2f(m - m_new);
       l *= alpha;
@@ -258,40 +343,24 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       m = m_new;
+      probabilities();
     }
+    l += lu;
 
-    // P^T as B operand of k-step (t, ks): registers 8*ks .. 8*ks+7, which are
-    // keys 32*t + 16*ks + 8*hl + (0..7) of the unit.  The denominator sums the
-    // bf16-rounded probabilities (the weights the P.V product uses) with v_dot2.
-    bf16x8 pf[2][2];
-    float l0 = 0.0f, l1 = 0.0f;
+    __builtin_amdgcn_s_setprio(1);
+    // O^T += V^T P^T in the order (t, ks, db); A operand: row d of V^T, the
+    // same 8 consecutive keys (chunk 4*t + 2*ks + hl of the unit's keys).
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pf[t][ks][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * ks + e], c, -m));
-        const bf16x8 v = pf[t][ks];
-        l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), ones, l0, false);
-        l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), ones, l1, false);
-        l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), ones, l0, false);
-        l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), ones, l1, false);
-      }
-    l += l0 + l1;
-
-    // O^T += V^T P^T; A operand: row d of V^T, the same 8 consecutive keys
-    // (chunk 4*t + 2*ks + hl of the unit's 64 keys).
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(
-              sV + swz_v(32 * db + l32, 4 * t + 2 * ks + hl));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[t][ks], o[db], 0, 0, 0);
-        }
+    for (int i = 0; i < 16; ++i) {
+      const int t = i >> 3, ks = (i >> 2) & 1, db = i & 3;
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[i % kVAhead], pf[t][ks], o[db], 0, 0, 0);
+      const int n = i + kVAhead;
+      if (n < 16)
+        vr[i % kVAhead] = *reinterpret_cast<const bf16x8*>(
+            sV + swz_v(32 * (n & 3) + l32, 4 * (n >> 3) + 2 * ((n >> 2) & 1) + hl));
+      __builtin_amdgcn_sched_barrier(kFenceKeepDs);
+    }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // Epilogue: lane holds query qrow, channels 32*db + 8*g4 + 4*hl + (0..3).
