@@ -2,9 +2,11 @@
 arrays and the comparison bars.
 
 Tolerances for the bf16 attention output against the fp64 oracle: max-abs
-2e-2 and mean-abs 2e-3 (bf16 inputs and output, fp32 accumulation); LSE
-1e-3 absolute.  Everything integer (tile copies, top-k ids, kept lists,
-bitmasks) and the fp32 block means and scores must match bit for bit.
+2e-2 and mean-abs 2e-3 (bf16 inputs and output, fp32 accumulation).  The LSE
+is held to a per-query bound derived from the kernel's arithmetic (see
+lse_bound; rows with nothing kept must be exactly -inf).  Everything integer (tile copies, top-k
+ids, kept lists, bitmasks) and the fp32 block means and scores must match bit
+for bit.
 """
 from __future__ import annotations
 
@@ -16,7 +18,6 @@ import synthetic_inputs as si
 
 O_MAX_ABS = 2e-2
 O_MEAN_ABS = 2e-3
-LSE_ABS = 1e-3
 
 
 def to_dev(x: np.ndarray) -> torch.Tensor:
@@ -79,3 +80,41 @@ def o_rows(wl, o_tok: torch.Tensor, rows) -> np.ndarray:
     tok = token_rows(wl, rows)
     bh = np.asarray(rows) // wl.n_tiles
     return o[bh[:, None], tok]
+
+
+def lse_bound(wl, q, k, rows) -> np.ndarray:
+    """[len(rows), 128] bound on |LSE - LSE_oracle| (natural log) per query.
+
+    Three error sources, each bounded generously:
+    - the denominator sums the probabilities after rounding them to bf16 (the
+      same weights the P.V product uses): relative error at most 2^-9, so
+      the LSE moves by at most log(1 + 2^-9);
+    - each score is a 128-term fp32 accumulation on the matrix cores: error at
+      most 128 * 2^-23 * sum_d |q_d k_d| <= 2^-16 * |q| * |k| (Cauchy-Schwarz),
+      times the softmax scale; the LSE, a smooth maximum of the scores, moves
+      by at most the largest score error, so |k| is the head's largest key norm;
+    - fp32 exp2/log2, the scaling fma and the fp32 running sum: at most 2^-12.
+    """
+    bh_all = wl.batch * wl.heads
+    qn = np.linalg.norm(si.bf16_bits_to_f32(q).reshape(bh_all, wl.n_tokens, 128)
+                        .astype(np.float64), axis=-1)
+    kmax = np.linalg.norm(si.bf16_bits_to_f32(k).reshape(bh_all, wl.n_tokens, 128)
+                          .astype(np.float64), axis=-1).max(axis=-1)
+    rows = np.asarray(rows)
+    bh = rows // wl.n_tiles
+    tok = token_rows(wl, rows)
+    scale = oracle.default_scale(wl)
+    return (np.log1p(2.0 ** -9) + 2.0 ** -16 * scale * qn[bh[:, None], tok] * kmax[bh][:, None]
+            + 2.0 ** -12)
+
+
+def check_lse(wl, q, k, rows, lse: np.ndarray, lse_ref: np.ndarray):
+    """Empty rows (-inf) must match exactly; the rest must lie within lse_bound.
+    Returns the largest error as a fraction of its bound."""
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse), empty)
+    if empty.all():
+        return 0.0
+    ratio = float((np.abs(lse - lse_ref)[~empty] / lse_bound(wl, q, k, rows)[~empty]).max())
+    assert ratio <= 1.0, ratio
+    return ratio
