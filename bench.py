@@ -2,17 +2,25 @@
 """SSTA forward benchmark on one MI355X.
 
 One step = the whole SSTA forward on one batch of synthetic inputs already
-resident in HBM: tile/pool Q, K, V -> scores + top-k -> window/union lists ->
-block-sparse attention -> unpermute O.  W untimed warm-up steps, then K timed
-steps between device synchronisations.  Prints one JSON line.
+resident in HBM: tile/pool Q, K, V -> block scores + top-k -> window/union
+lists -> block-sparse attention (-> unpermute O when the block I/O is
+materialised).  W untimed warm-up steps, then K timed steps between device
+synchronisations.  Prints one JSON line.
 
-  value  = effective TFLOP/s on kept blocks over the whole step
-           (kept (query block, key block) pairs x 4*128^3 FLOP / step time)
-  roofline: the attention kernel (the dominant kernel), achieved TFLOP/s from
-           HIP events recorded around its launches on the launch stream, vs the
-           dense bf16 MFMA peak of 2.5 PFLOP/s
+  value        effective TFLOP/s on kept blocks over the whole step
+               (kept (query block, key block) pairs x 4*128^3 FLOP / step time)
+  phase_ms     per phase (tile_pool, score_select, build_mask, attention,
+               unpermute): mean, median, p10, p90 over the K steps, from HIP
+               events recorded on the launch stream
+  phase_rates  algorithmic bytes, GB/s and % of HBM peak per phase; VALU FLOP
+               and % of the fp32 vector peak for the block scoring
+  cold_cache   steps timed right after overwriting a 512 MB buffer
+  roofline     the attention kernel (the dominant kernel): kept FLOP / its
+               mean launch time vs the dense bf16 MFMA peak of 2.5 PFLOP/s;
+               traffic = HBM bytes per launch from rocprofv3 counters, if they
+               were taken on this version of the kernel
   speedup vs dense: the same pipeline with every block kept (dense attention)
-  cpu_baseline: the CPU oracle on a bounded sample of the same workload
+  cpu_baseline the CPU oracle on a bounded sample of the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -31,6 +39,7 @@ if ROOT not in sys.path:
 METRIC = "SSTA fwd effective TFLOP/s on kept blocks (% bf16 MFMA peak) + speedup vs dense"
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_VECTOR_TFLOPS = 157.3    # MI355X published fp32 vector peak (packed FMA)
 FLOP_PER_PAIR = 4 * 128 ** 3       # Q.K^T and P.V for one 128x128 block pair
 
 
@@ -41,6 +50,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="720p-10s")
     ap.add_argument("--dense-steps", type=int, default=2)
+    ap.add_argument("--cold-steps", type=int, default=3,
+                    help="extra steps, each after overwriting a 512 MB buffer (cold caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--materialised", action="store_true",
                     help="permute Q/K to tile-major and unpermute O in separate kernels "
@@ -144,28 +155,26 @@ def main():
     plan = m.SstaPlan(g, p, fused_io=fused)
     stream = torch.cuda.current_stream()
 
-    phases = ("tile_pool", "select", "attention", "unpermute")
+    phases = ("tile_pool", "score_select", "build_mask", "attention", "unpermute")
+    calls = (lambda: plan.tile_pool(qd, kd, vd), plan.score_select, plan.build_mask,
+             plan.attend, plan.unpermute)
 
     def step(ev=None):
+        for j, call in enumerate(calls):
+            if ev is not None:
+                ev[j].record(stream)
+            call()
         if ev is not None:
-            ev[0].record(stream)
-        plan.tile_pool(qd, kd, vd)
-        if ev is not None:
-            ev[1].record(stream)
-        plan.select()
-        if ev is not None:
-            ev[2].record(stream)
-        plan.attend()
-        if ev is not None:
-            ev[3].record(stream)
-        plan.unpermute()
-        if ev is not None:
-            ev[4].record(stream)
+            ev[len(calls)].record(stream)
+
+    def new_events(count):
+        return [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+                for _ in range(count)]
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = new_events(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -173,9 +182,31 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    phase_ms = {ph: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1])
-                                   for i in range(args.steps)]))
-                for j, ph in enumerate(phases)}
+
+    def stats(xs):
+        xs = np.asarray(xs, dtype=np.float64)
+        return {"mean": round(float(xs.mean()), 4), "median": round(float(np.median(xs)), 4),
+                "p10": round(float(np.percentile(xs, 10)), 4),
+                "p90": round(float(np.percentile(xs, 90)), 4)}
+
+    phase_stats = {ph: stats([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)])
+                   for j, ph in enumerate(phases)}
+    phase_ms = {ph: st["mean"] for ph, st in phase_stats.items()}
+    step_event_stats = stats([evs[i][0].elapsed_time(evs[i][-1]) for i in range(args.steps)])
+
+    # Cold L2/MALL: a 512 MB buffer is overwritten before each of these steps.
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        ce = new_events(args.cold_steps)
+        for i in range(args.cold_steps):
+            flush.fill_(i & 0xFF)
+            step(ce[i])
+        torch.cuda.synchronize()
+        cold = {"step_ms": stats([e[0].elapsed_time(e[-1]) for e in ce]),
+                "attention_ms": stats([e[3].elapsed_time(e[4]) for e in ce])}
+        del flush
+
     pairs = int(plan.kv_cnt.sum().item())
     n = wl.n_tiles
     total_pairs = wl.batch * wl.heads * n * n
@@ -222,9 +253,37 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, q, k, v, args.cpu_rows)
 
-    # tile_pool traffic: Q read (+ written tile-major when materialised), K and V read + written
-    tensor = wl.batch * wl.heads * wl.n_tokens * 128 * 2
-    pool_bytes = (5 if fused else 6) * tensor + 2 * wl.batch * wl.heads * n * 128 * 4
+    # Algorithmic bytes and VALU work of each phase (what the step must move or
+    # compute at minimum; the design doc lists the per-unit figures).
+    bh = wl.batch * wl.heads
+    tensor = bh * wl.n_tokens * 128 * 2                 # one of Q, K, V, O in bf16
+    pooled = bh * n * 128 * 4
+    phase_bytes = {
+        # read Q, K, V; write K_t, V_t (and Q_t when materialised); write both pooled arrays
+        "tile_pool": (5 if fused else 6) * tensor + 2 * pooled,
+        # read both pooled arrays, write the top-k ids
+        "score_select": 2 * pooled + bh * n * plan.width * 4,
+        # read the top-k ids, write the kept lists and counts
+        "build_mask": bh * n * (plan.width + plan.max_kept + 1) * 4,
+        # each kept pair reads one 32 KB K block and one 32 KB V block; Q read, O written once
+        "attention": pairs * 2 * 128 * 128 * 2 + 2 * tensor,
+        "unpermute": 0 if fused else 2 * tensor,
+    }
+    phase_rates = {}
+    for ph in phases:
+        ms = phase_stats[ph]["median"]
+        gbs = phase_bytes[ph] / (ms * 1e-3) / 1e9 if ms > 0 and phase_bytes[ph] else None
+        phase_rates[ph] = {"bytes": phase_bytes[ph],
+                           "gbs": None if gbs is None else round(gbs, 1),
+                           "pct_hbm": None if gbs is None else round(100 * gbs / PEAK_HBM_GBS, 1)}
+    # tile-score GEMV (q.k for every block pair) and key redundancy (k.k for every
+    # pair): one fp32 FMA (2 FLOP) per channel each
+    score_flop = 2 * bh * n * n * 128 * 2 if plan.width > 0 else 0
+    ss_ms = phase_stats["score_select"]["median"]
+    score_tflops = score_flop / (ss_ms * 1e-3) / 1e12 if ss_ms > 0 else 0.0
+    phase_rates["score_select"].update({
+        "valu_flop": score_flop, "valu_tflops": round(score_tflops, 2),
+        "pct_fp32_vector_peak": round(100 * score_tflops / PEAK_FP32_VECTOR_TFLOPS, 1)})
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -252,8 +311,10 @@ def main():
         "pct_bf16_peak_attention": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
         "kept_pairs": pairs,
         "kept_fraction": round(pairs / total_pairs, 5),
-        "phase_ms": {kk: round(vv, 4) for kk, vv in phase_ms.items()},
-        "tile_pool_gbs": round(pool_bytes / (phase_ms["tile_pool"] * 1e-3) / 1e9, 1),
+        "phase_ms": phase_stats,
+        "step_ms_events": step_event_stats,
+        "phase_rates": phase_rates,
+        "cold_cache": cold,
         "dense_ms_per_step": None if dense_ms is None else round(dense_ms, 3),
         "dense_attention_ms": None if dense_attn_ms is None else round(dense_attn_ms, 3),
         "speedup_vs_dense_step": None if dense_ms is None else round(dense_ms / ms_step, 3),

@@ -28,11 +28,15 @@
 // window blocks in that XCD's L2.
 // Memory: each kept block is processed as two units of 64 keys.  A unit's K
 // rows and V^T columns (16 KB each) go straight from global memory into LDS
-// with global_load_lds_dwordx4 (no register staging) into a two-slot ring;
-// the next unit's loads are issued once the current unit's scores are on the
-// matrix cores and overlap the rest of the unit.  Kept-block ids are read 64
-// at a time into one register per lane and taken out with v_readlane, so no
-// per-unit global load sits on the critical path.
+// with buffer_load_dwordx4 ... lds (no register staging) into a two-slot
+// ring; the next unit's loads are issued right after the barrier that frees
+// its slot and overlap the whole current unit.  The buffer form (a per-head
+// resource with a 32-bit offset, range-checked by the hardware) is used
+// rather than global_load_lds because the compiler then tracks the LDS
+// operand reads that follow with exact lgkmcnt waits instead of draining
+// them all.  Kept-block ids are read 64 at a time into one register per lane
+// and taken out with v_readlane, so no per-unit global load sits on the
+// critical path.
 // LDS operand reads are issued ahead of their products (up to 8 for K, the
 // first 8 V^T operands before the softmax), held in place by scheduling
 // fences; waves raise their issue priority around the matrix-core sections.
@@ -120,23 +124,30 @@ __device__ __forceinline__ DmaOffsets dma_offsets(int wave, int lane) {
   return o;
 }
 
-// Half p (keys 64p .. 64p+63) of a K block: 64 contiguous rows.
-__device__ __forceinline__ void dma_k(uint8_t* dst, const uint8_t* ktile, int p, int wave,
-                                      const DmaOffsets& off) {
-  const uint8_t* base = ktile + p * kSlotBytes;
-#pragma unroll
-  for (int mm = 0; mm < 4; ++mm)
-    __builtin_amdgcn_global_load_lds(base + off.k[mm], (lds_u8*)(dst + (4 * wave + mm) * 1024),
-                                     16, 0, 0);
+// Buffer resource over one head's K_t or V_t blocks (n_tiles x 32 KB); loads
+// beyond num_records return zero instead of touching other memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t* base, int64_t n_tiles) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0,
+                                           (int)(n_tiles * kTileBytes), 0x00020000);
 }
-// Half p of a V^T block: bytes 128p .. 128p+127 of each 256-byte channel row.
-__device__ __forceinline__ void dma_v(uint8_t* dst, const uint8_t* vtile, int p, int wave,
-                                      const DmaOffsets& off) {
-  const uint8_t* base = vtile + p * 128;
+
+// Half p (keys 64p .. 64p+63) of K block j: 64 contiguous rows.
+__device__ __forceinline__ void dma_k(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, int64_t j, int p,
+                                      int wave, const DmaOffsets& off) {
+  const uint32_t so = (uint32_t)(j * kTileBytes + p * kSlotBytes);
 #pragma unroll
   for (int mm = 0; mm < 4; ++mm)
-    __builtin_amdgcn_global_load_lds(base + off.v[mm], (lds_u8*)(dst + (4 * wave + mm) * 1024),
-                                     16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (4 * wave + mm) * 1024), 16,
+                                             off.k[mm], so, 0, 0);
+}
+// Half p of V^T block j: bytes 128p .. 128p+127 of each 256-byte channel row.
+__device__ __forceinline__ void dma_v(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, int64_t j, int p,
+                                      int wave, const DmaOffsets& off) {
+  const uint32_t so = (uint32_t)(j * kTileBytes + p * 128);
+#pragma unroll
+  for (int mm = 0; mm < 4; ++mm)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (4 * wave + mm) * 1024), 16,
+                                             off.v[mm], so, 0, 0);
 }
 
 // S^T for the 64 keys of a K slot: the A operand row of lane l32 is key
@@ -232,6 +243,7 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   // K and V^T rings; unit u+1 is loaded while unit u is computed.
   const int units = 2 * cnt;
   const DmaOffsets doff = dma_offsets(wv, lane);
+  const __amdgpu_buffer_rsrc_t krs = block_rsrc(kb, g.n_tiles), vrs = block_rsrc(vb, g.n_tiles);
   // Kept-block ids, 64 at a time: lane i holds entry ibase + i.
   int ibase = 0;
   int ids = (!dense && lane < cnt) ? idx[lane] : 0;
@@ -245,14 +257,19 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   };
   if (units > 0) {
     const int64_t j0 = block_at(0);
-    dma_k(smem, kb + j0 * kTileBytes, 0, wv, doff);
-    dma_v(smem + 2 * kSlotBytes, vb + j0 * kTileBytes, 0, wv, doff);
+    dma_k(smem, krs, j0, 0, wv, doff);
+    dma_v(smem + 2 * kSlotBytes, vrs, j0, 0, wv, doff);
   }
 
   for (int u = 0; u < units; ++u) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's loads of unit u have landed
     __syncthreads();                        // ... every wave's; and unit u-1 is done
     const int slot = u & 1;
+    if (u + 1 < units) {
+      const int64_t j = block_at((u + 1) >> 1);
+      dma_k(smem + (1 - slot) * kSlotBytes, krs, j, (u + 1) & 1, wv, doff);
+      dma_v(smem + (3 - slot) * kSlotBytes, vrs, j, (u + 1) & 1, wv, doff);
+    }
     const uint8_t* sK = smem + slot * kSlotBytes;
     const uint8_t* sV = smem + (2 + slot) * kSlotBytes;
 
@@ -290,11 +307,6 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
           sV + swz_v(32 * (i & 3) + l32, 4 * (i >> 3) + 2 * ((i >> 2) & 1) + hl));
 
     __builtin_amdgcn_s_setprio(0);
-    if (u + 1 < units) {
-      const int64_t j = block_at((u + 1) >> 1);
-      dma_k(smem + (1 - slot) * kSlotBytes, kb + j * kTileBytes, (u + 1) & 1, wv, doff);
-      dma_v(smem + (3 - slot) * kSlotBytes, vb + j * kTileBytes, (u + 1) & 1, wv, doff);
-    }
     __builtin_amdgcn_sched_barrier(kFenceKeepDs);
 
     // Online softmax in the log2 domain against the running max m, which is

@@ -61,12 +61,20 @@ class SstaPlan:
         L.ssta_tile_pool(g, k, self.k_t, L.LAYOUT_TOKEN_MAJOR, self.k_pooled, stream)
         L.ssta_tile_pool(g, v, self.v_t, L.LAYOUT_DIM_MAJOR, None, stream)
 
-    def select(self, stream=None):
-        g, p = self.geom, self.params
+    def score_select(self, stream=None):
+        """Block scores and per-query-block top-k (Step 2)."""
         if self.width > 0:
-            L.ssta_score_select(g, p, self.q_pooled, self.k_pooled, self.topk_idx,
-                                self.workspace, stream)
-        L.ssta_build_mask(g, p, self.topk_idx, self.kv_idx, self.kv_cnt, self.bitmask, stream)
+            L.ssta_score_select(self.geom, self.params, self.q_pooled, self.k_pooled,
+                                self.topk_idx, self.workspace, stream)
+
+    def build_mask(self, stream=None):
+        """Window union top-k -> ascending kept lists (Steps 3-4)."""
+        L.ssta_build_mask(self.geom, self.params, self.topk_idx, self.kv_idx, self.kv_cnt,
+                          self.bitmask, stream)
+
+    def select(self, stream=None):
+        self.score_select(stream)
+        self.build_mask(stream)
 
     def attend(self, stream=None, dense=None):
         """Attention for the inputs of the last tile_pool call."""
