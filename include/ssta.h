@@ -26,7 +26,9 @@
  *     grid, and the tokens of one block row-major over (tile_t, tile_h,
  *     tile_w).  n_tiles = (T/tile_t)(H/tile_h)(W/tile_w)  (Step 1).
  *   - Current limits: head_dim == 128, tile_t*tile_h*tile_w == 128 tokens,
- *     tile sizes divide T, H, W; ssta_score_select needs n_tiles <= 4096.
+ *     tile sizes divide T, H, W; ssta_score_select needs n_tiles <= 4096;
+ *     the attention entry points need n_tiles < 65536 (one head's blocks are
+ *     addressed with 32-bit offsets).
  */
 #ifndef SSTA_H
 #define SSTA_H

@@ -307,6 +307,9 @@ int attention_common(const ssta_geom_t* g, const ssta_params_t* p, const void* q
   SSTA_TRY(check_ptr(v_t, false));
   SSTA_TRY(check_ptr(o, false));
   SSTA_TRY(check_ptr(lse, true));
+  // One head's K_t / V_t blocks are addressed with 32-bit buffer offsets.
+  if (geo.n_tiles * int64_t(ssta::kTileTokens) * ssta::kHeadDim * 2 > 0x7FFFFFFF)
+    return SSTA_ERR_SHAPE;
   const bool dense = kv_cnt == nullptr;
   if (dense) {
     if (kv_idx != nullptr || max_kept_ != 0) return SSTA_ERR_ARG;
