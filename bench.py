@@ -19,6 +19,9 @@ synchronisations.  Prints one JSON line.
                mean launch time vs the dense bf16 MFMA peak of 2.5 PFLOP/s;
                traffic = HBM bytes per launch from rocprofv3 counters, if they
                were taken on this version of the kernel
+  mfma_sustained  the chip's sustained bf16 matrix-core rate on random and on
+               constant operands (ssta_calibrate_mfma): under random data the
+               power limit holds the clock well below its peak
   speedup vs dense: the same pipeline with every block kept (dense attention)
   cpu_baseline the CPU oracle on a bounded sample of the same workload
 
@@ -53,6 +56,8 @@ def parse():
     ap.add_argument("--cold-steps", type=int, default=3,
                     help="extra steps, each after overwriting a 512 MB buffer (cold caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mfma-ceiling", action="store_true",
+                    help="skip the sustained bf16 matrix-core rate measurement")
     ap.add_argument("--materialised", action="store_true",
                     help="permute Q/K to tile-major and unpermute O in separate kernels "
                          "instead of gathering blocks inside the attention kernel")
@@ -113,6 +118,31 @@ def cpu_baseline(wl, q, k, v, rows_wanted):
                    "attention of %d of %d query blocks (%d kept pairs, %.1f s)"
                    % (wl.name, t_sel, len(rows), n, pairs, t_att)),
     }
+
+
+def mfma_ceiling(torch, m, iters=160000, reps=3):
+    """Sustained bf16 matrix-core rate with the chip fully loaded (2 workgroups
+    of 4 waves per CU, as the attention kernel runs), for random and for
+    constant operands; about 20 ms per launch so the clock settles."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid = 2 * cus
+    gen = torch.Generator().manual_seed(7)
+    tables = {"random_operands_tflops": torch.randn(256, 8, generator=gen).to(torch.bfloat16),
+              "constant_operands_tflops": torch.full((256, 8), 0.5, dtype=torch.bfloat16)}
+    sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    flop = grid * 4 * iters * 4 * 32768.0
+    out = {"grid": grid, "iters": iters, "flop_per_launch": flop}
+    for name, tab in tables.items():
+        tab = tab.cuda()
+        m.ssta_calibrate_mfma(tab, sink, grid, iters)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            m.ssta_calibrate_mfma(tab, sink, grid, iters)
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(flop * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    return out
 
 
 def main():
@@ -237,6 +267,12 @@ def main():
         print("[bench] dense step %.1f ms, attention %.1f ms" % (dense_ms, dense_attn_ms),
               file=sys.stderr, flush=True)
 
+    ceiling = None if args.no_mfma_ceiling else mfma_ceiling(torch, m)
+    if ceiling is not None:
+        print("[bench] sustained bf16 MFMA: %.0f TFLOP/s random operands, %.0f constant"
+              % (ceiling["random_operands_tflops"], ceiling["constant_operands_tflops"]),
+              file=sys.stderr, flush=True)
+
     traffic = load_traffic(args.traffic_json, wl.name, kernel_hash())
     roof = {
         "kernel": "k_attn_fwd",
@@ -248,6 +284,8 @@ def main():
         "traffic": traffic,
         "algorithmic_flop_per_launch": flop,
         "avg_launch_ms": round(phase_ms["attention"], 4),
+        "frac_of_sustained_random": (None if ceiling is None else
+                                     round(attn_tflops / ceiling["random_operands_tflops"], 4)),
     }
     cpu = None
     if not args.no_cpu_baseline:
@@ -321,6 +359,7 @@ def main():
         "speedup_vs_dense_attention": (None if dense_attn_ms is None
                                        else round(dense_attn_ms / phase_ms["attention"], 3)),
         "roofline": roof,
+        "mfma_sustained": ceiling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

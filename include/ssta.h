@@ -193,6 +193,20 @@ int ssta_attention_fwd_tokens(const ssta_geom_t* g, const ssta_params_t* p, cons
                               const int32_t* kv_cnt, int32_t max_kept, void* o, float* lse,
                               void* stream);
 
+/* Measurement aid, not a step of the method.  For callers that want the
+ * sustained bf16 matrix-core rate of the chip next to the attention kernel:
+ * `grid` workgroups of 4 waves each run `iters` rounds of 4 independent
+ * v_mfma_f32_32x32x16_bf16 products on register-resident operands read once
+ * from `operands`.  The rate under random operands is what the power limit
+ * allows for real data; constant operands draw less power.
+ *   operands in : device, 256 x 8 bf16 (4 KB, 16-byte aligned).
+ *   sink    out : device, grid*256 floats (keeps the work from being dropped).
+ *   Work: grid * 4 * iters * 4 * 32768 FLOP.
+ * Errors: SSTA_ERR_ARG for grid or iters <= 0 or null pointers, SSTA_ERR_ALIGN,
+ * SSTA_ERR_NO_DEVICE / _ARCH, SSTA_ERR_HIP. */
+int ssta_calibrate_mfma(const void* operands, float* sink, int32_t grid, int32_t iters,
+                        void* stream);
+
 /* Static text for a status code. */
 const char* ssta_status_string(int status);
 

@@ -127,6 +127,14 @@ def test_attention_argument_rules():
                                   16, None, None) == ARG          # max_kept > n_tiles
 
 
+def test_calibration_argument_rules():
+    lib = m.load()
+    assert lib.ssta_calibrate_mfma(16, 16, 0, 10, None) == ARG       # empty grid
+    assert lib.ssta_calibrate_mfma(16, 16, 4, 0, None) == ARG        # no iterations
+    assert lib.ssta_calibrate_mfma(None, 16, 4, 10, None) == ARG
+    assert lib.ssta_calibrate_mfma(8, 16, 4, 10, None) == ALIGN
+
+
 def test_no_device_is_an_error_not_a_fallback():
     import torch
     if torch.cuda.is_available():
@@ -134,5 +142,6 @@ def test_no_device_is_an_error_not_a_fallback():
     lib = m.load()
     g = _g()
     assert lib.ssta_tile_pool(ctypes.byref(g), 16, 32, 0, None, None) == NO_DEV
+    assert lib.ssta_calibrate_mfma(16, 16, 4, 10, None) == NO_DEV
     with pytest.raises(m.SstaError):
         L._call("ssta_tile_pool", ctypes.byref(g), 16, 32, 0, None, None)

@@ -239,3 +239,16 @@ def test_device_argument_errors():
     rc = lib.ssta_tile_pool(ctypes.byref(g), x.data_ptr(), None, 0, None, None)
     assert rc == -1                                   # no output requested
     torch.cuda.synchronize()
+
+
+def test_calibrate_mfma_runs():
+    """The matrix-core calibration loop computes what it claims: with all
+    operands 1.0 every product adds 16 to each accumulator element, so each
+    thread's sink value is 4 chains x 16 elements x 16 x iters."""
+    import video_dit_block_tile_amd as m
+    grid, iters = 8, 100
+    ops = torch.ones(256, 8, dtype=torch.bfloat16, device="cuda")
+    sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    m.ssta_calibrate_mfma(ops, sink, grid, iters)
+    torch.cuda.synchronize()
+    assert torch.all(sink == 4 * 16 * 16 * iters)

@@ -69,6 +69,7 @@ SIGNATURES = {
     "ssta_attention_fwd": (ctypes.c_int, [_G, _P, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "ssta_attention_fwd_tokens": (ctypes.c_int,
                                   [_G, _P, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
+    "ssta_calibrate_mfma": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp]),
     "ssta_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ssta_last_hip_error": (ctypes.c_int, []),
 }
@@ -284,3 +285,11 @@ def ssta_attention_fwd_tokens(g: SstaGeom, p: SstaParams, q, k_t, v_t, kv_idx, k
         _expect("kv_idx", kv_idx, (g.batch, g.heads, g.n_tiles, mk), torch.int32)
     _call("ssta_attention_fwd_tokens", ctypes.byref(g), ctypes.byref(p), _ptr(q), _ptr(k_t),
           _ptr(v_t), _ptr(kv_idx), _ptr(kv_cnt), mk, _ptr(o), _ptr(lse), _stream(stream))
+
+
+def ssta_calibrate_mfma(operands, sink, grid: int, iters: int, stream=None):
+    """Measurement aid: grid x 4 waves x iters x 4 bf16 32x32x16 products on
+    register-resident operands (operands: 256x8 bf16, sink: grid*256 fp32)."""
+    _expect("operands", operands, (256, 8), torch.bfloat16)
+    _expect("sink", sink, (grid * 256,), torch.float32)
+    _call("ssta_calibrate_mfma", _ptr(operands), _ptr(sink), grid, iters, _stream(stream))

@@ -32,6 +32,7 @@ SOURCES = {
     "k_score.hip": ["-ffp-contract=off"],
     "k_mask.hip": [],
     "k_attn.hip": ["-fno-honor-nans"],
+    "k_calib.hip": [],
 }
 
 

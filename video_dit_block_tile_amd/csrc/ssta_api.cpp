@@ -348,6 +348,15 @@ int ssta_attention_fwd_tokens(const ssta_geom_t* g, const ssta_params_t* p, cons
   return attention_common(g, p, q, k_t, v_t, kv_idx, kv_cnt, max_kept_, o, lse, stream, 1);
 }
 
+int ssta_calibrate_mfma(const void* operands, float* sink, int32_t grid, int32_t iters,
+                        void* stream) {
+  if (grid <= 0 || iters <= 0 || operands == nullptr || sink == nullptr) return SSTA_ERR_ARG;
+  SSTA_TRY(check_ptr(operands, false));
+  SSTA_TRY(check_ptr(sink, false));
+  SSTA_TRY(check_device());
+  return hip_status(ssta::launch_calibrate_mfma(operands, sink, grid, iters, as_stream(stream)));
+}
+
 const char* ssta_status_string(int status) {
   switch (status) {
     case SSTA_OK: return "ok";

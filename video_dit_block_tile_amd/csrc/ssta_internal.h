@@ -93,4 +93,8 @@ struct AttnArgs {
 };
 hipError_t launch_attention(const Geo& g, const AttnArgs& a, hipStream_t s);
 
+// Sustained matrix-core rate (measurement aid; see k_calib.hip).
+hipError_t launch_calibrate_mfma(const void* operands, float* sink, int grid, int iters,
+                                 hipStream_t s);
+
 }  // namespace ssta
