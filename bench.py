@@ -297,13 +297,13 @@ def main():
     tensor = bh * wl.n_tokens * 128 * 2                 # one of Q, K, V, O in bf16
     pooled = bh * n * 128 * 4
     phase_bytes = {
-        # read Q, K, V; write K_t, V_t (and Q_t when materialised); write both pooled arrays
-        "tile_pool": (5 if fused else 6) * tensor + 2 * pooled,
+        # read Q, K, V; write V_t (and Q_t, K_t when materialised); write both pooled arrays
+        "tile_pool": (4 if fused else 6) * tensor + 2 * pooled,
         # read both pooled arrays, write the top-k ids
         "score_select": 2 * pooled + bh * n * plan.width * 4,
         # read the top-k ids, write the kept lists and counts
         "build_mask": bh * n * (plan.width + plan.max_kept + 1) * 4,
-        # each kept pair reads one 32 KB K block and one 32 KB V block; Q read, O written once
+        # each kept pair reads one 32 KB K block and one 32 KB V^T block; Q read, O written once
         "attention": pairs * 2 * 128 * 128 * 2 + 2 * tensor,
         "unpermute": 0 if fused else 2 * tensor,
     }

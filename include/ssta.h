@@ -176,20 +176,22 @@ int ssta_attention_fwd(const ssta_geom_t* g, const ssta_params_t* p, const void*
                        void* stream);
 
 /*
- * Step 4 with the query gather and the output scatter folded into the
- * attention kernel: the same computation as ssta_attention_fwd, but Q and the
- * output O stay in the caller's token order, so Q needs no tile-major copy
- * and O no unpermute.  K and V keep their block layouts (every query block
- * that keeps a key block re-reads it, so those are stored contiguously).
+ * Step 4 with the block gathers and the output scatter folded into the
+ * attention kernel: the same computation as ssta_attention_fwd, but Q, K and
+ * the output O stay in the caller's token order, so neither Q nor K needs a
+ * tile-major copy and O no unpermute (each kept key block is gathered token
+ * row by token row straight into LDS).  V keeps its dim-major block layout:
+ * the P.V product needs 8 consecutive keys of one channel per lane.
  *   q        in : bf16 [batch, heads, T*H*W, head_dim] (token-major).
- *   k_t      in : bf16 [batch, heads, n_tiles, tile_tokens, head_dim] (token-major tiles).
+ *   k        in : bf16 [batch, heads, T*H*W, head_dim] (token-major).
  *   v_t      in : bf16 [batch, heads, n_tiles, head_dim, tile_tokens] (dim-major tiles).
  *   kv_idx, kv_cnt, max_kept, lse: as for ssta_attention_fwd (LSE stays tile-major).
  *   o       out : bf16 [batch, heads, T*H*W, head_dim] (token-major).
- * Results are bit-identical to ssta_attention_fwd followed by ssta_tile_unpermute.
+ * Results are bit-identical to permuting Q and K with ssta_tile_pool,
+ * ssta_attention_fwd and ssta_tile_unpermute.
  */
 int ssta_attention_fwd_tokens(const ssta_geom_t* g, const ssta_params_t* p, const void* q,
-                              const void* k_t, const void* v_t, const int32_t* kv_idx,
+                              const void* k, const void* v_t, const int32_t* kv_idx,
                               const int32_t* kv_cnt, int32_t max_kept, void* o, float* lse,
                               void* stream);
 

@@ -264,12 +264,13 @@ def ssta_attention_fwd(g: SstaGeom, p: SstaParams, q_t, k_t, v_t, kv_idx, kv_cnt
           _ptr(kv_idx), _ptr(kv_cnt), mk, _ptr(o_t), _ptr(lse), _stream(stream))
 
 
-def ssta_attention_fwd_tokens(g: SstaGeom, p: SstaParams, q, k_t, v_t, kv_idx, kv_cnt, o,
+def ssta_attention_fwd_tokens(g: SstaGeom, p: SstaParams, q, k, v_t, kv_idx, kv_cnt, o,
                               lse=None, stream=None):
-    """Attention with token-major q and o (query gather / output scatter inside the kernel)."""
+    """Attention with token-major q, k and o (block gathers and output scatter
+    inside the kernel); v_t dim-major tiles."""
     tok = (g.batch, g.heads, g.n_tokens, g.head_dim)
     _expect("q", q, tok, torch.bfloat16)
-    _expect("k_t", k_t, _tiled_shape(g), torch.bfloat16)
+    _expect("k", k, tok, torch.bfloat16)
     _expect("v_t", v_t, (g.batch, g.heads, g.n_tiles, g.head_dim, g.tile_tokens),
             torch.bfloat16)
     _expect("o", o, tok, torch.bfloat16)
@@ -283,7 +284,7 @@ def ssta_attention_fwd_tokens(g: SstaGeom, p: SstaParams, q, k_t, v_t, kv_idx, k
         _expect("kv_cnt", kv_cnt, (g.batch, g.heads, g.n_tiles), torch.int32)
         mk = kv_idx.shape[-1]
         _expect("kv_idx", kv_idx, (g.batch, g.heads, g.n_tiles, mk), torch.int32)
-    _call("ssta_attention_fwd_tokens", ctypes.byref(g), ctypes.byref(p), _ptr(q), _ptr(k_t),
+    _call("ssta_attention_fwd_tokens", ctypes.byref(g), ctypes.byref(p), _ptr(q), _ptr(k),
           _ptr(v_t), _ptr(kv_idx), _ptr(kv_cnt), mk, _ptr(o), _ptr(lse), _stream(stream))
 
 

@@ -101,6 +101,29 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Token index of the first token of block j within one (batch, head).
+__device__ __forceinline__ int64_t block_origin(const Geo& g, int64_t j) {
+  const int64_t bt = j / ((int64_t)g.ny * g.nx), by = (j / g.nx) % g.ny, bx = j % g.nx;
+  return ((bt * g.tt) * g.H + by * g.th) * (int64_t)g.W + bx * g.tw;
+}
+
+// The same in 32-bit arithmetic (block ids and a head's token count fit).
+__device__ __forceinline__ uint32_t block_origin32(const Geo& g, uint32_t j) {
+  const uint32_t nyx = (uint32_t)g.ny * (uint32_t)g.nx;
+  const uint32_t bt = j / nyx, rem = j - bt * nyx;
+  const uint32_t by = rem / (uint32_t)g.nx, bx = rem - by * (uint32_t)g.nx;
+  return ((bt * (uint32_t)g.tt) * (uint32_t)g.H + by * (uint32_t)g.th) * (uint32_t)g.W +
+         bx * (uint32_t)g.tw;
+}
+
+// Token offset (from the block's first token) of in-block position r; block
+// sizes are powers of two because their product is 128.
+__device__ __forceinline__ uint32_t in_block_offset(const Geo& g, int r) {
+  const int ltw = __builtin_ctz(g.tw), lth = __builtin_ctz(g.th);
+  const int it = r >> (ltw + lth), iy = (r >> ltw) & (g.th - 1), ix = r & (g.tw - 1);
+  return (uint32_t)((it * g.H + iy) * g.W + ix);
+}
+
 // Direct global->LDS loads (global_load_lds_dwordx4).  A slot is 16 KB: each
 // of the 4 waves issues 4 instructions of 1 KB; lane i of an instruction lands
 // at byte 16*i of its 1 KB destination block, so the source address of each
@@ -111,30 +134,40 @@ struct DmaOffsets {
   uint32_t k[4], v[4];
 };
 
-__device__ __forceinline__ DmaOffsets dma_offsets(int wave, int lane) {
+// kTokK: K is read from token-major [.., T*H*W, 128] memory, so key row r of
+// a unit comes from token in_block_offset(r) of its block (a 256-byte row).
+template <bool kTokK>
+__device__ __forceinline__ DmaOffsets dma_offsets(const Geo& g, int wave, int lane) {
   DmaOffsets o;
 #pragma unroll
   for (int mm = 0; mm < 4; ++mm) {
     const int b = 4 * wave + mm;                 // 1 KB destination block
     const int row = 4 * b + (lane >> 4);         // K: rows 4b .. 4b+3
-    o.k[mm] = row * 256 + (((lane & 15) ^ (row & 15)) << 4);
+    const uint32_t src_row = kTokK ? in_block_offset(g, row) : (uint32_t)row;
+    o.k[mm] = src_row * 256 + (((lane & 15) ^ (row & 15)) << 4);
     const int d = 8 * b + (lane >> 3);           // V^T: channel rows 8b .. 8b+7
     o.v[mm] = d * 256 + (((lane & 7) ^ ((d >> 1) & 7)) << 4);
   }
   return o;
 }
 
-// Buffer resource over one head's K_t or V_t blocks (n_tiles x 32 KB); loads
-// beyond num_records return zero instead of touching other memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t* base, int64_t n_tiles) {
+// Buffer resource over one head's K, K_t or V_t (bytes; n_tiles x 32 KB);
+// loads beyond num_records return zero instead of touching other memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint8_t* base, int64_t n_tiles) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0,
                                            (int)(n_tiles * kTileBytes), 0x00020000);
 }
 
-// Half p (keys 64p .. 64p+63) of K block j: 64 contiguous rows.
-__device__ __forceinline__ void dma_k(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, int64_t j, int p,
-                                      int wave, const DmaOffsets& off) {
-  const uint32_t so = (uint32_t)(j * kTileBytes + p * kSlotBytes);
+// Half p (keys 64p .. 64p+63) of K block j.  Tile-major: 64 contiguous rows.
+// Token-major: the rows of the block's tokens; in-block positions are a
+// bit-field code of (t, y, x) offsets, so position 64p + r lies at token
+// offset in_block_offset(64p) + in_block_offset(r) from the block's origin.
+template <bool kTokK>
+__device__ __forceinline__ void dma_k(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, const Geo& g,
+                                      int64_t j, int p, int wave, const DmaOffsets& off) {
+  const uint32_t so =
+      kTokK ? (block_origin32(g, (uint32_t)j) + (p ? in_block_offset(g, 64) : 0u)) * 256u
+            : (uint32_t)(j * kTileBytes + p * kSlotBytes);
 #pragma unroll
   for (int mm = 0; mm < 4; ++mm)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (4 * wave + mm) * 1024), 16,
@@ -169,24 +202,11 @@ __device__ __forceinline__ void scores(f32x16 (&s)[2], const uint8_t* sK, const 
     }
 }
 
-// Token index of the first token of block j within one (batch, head).
-__device__ __forceinline__ int64_t block_origin(const Geo& g, int64_t j) {
-  const int64_t bt = j / ((int64_t)g.ny * g.nx), by = (j / g.nx) % g.ny, bx = j % g.nx;
-  return ((bt * g.tt) * g.H + by * g.th) * (int64_t)g.W + bx * g.tw;
-}
-
-// Token offset (from the block's first token) of in-block position r; block
-// sizes are powers of two because their product is 128.
-__device__ __forceinline__ uint32_t in_block_offset(const Geo& g, int r) {
-  const int ltw = __builtin_ctz(g.tw), lth = __builtin_ctz(g.th);
-  const int it = r >> (ltw + lth), iy = (r >> ltw) & (g.th - 1), ix = r & (g.tw - 1);
-  return (uint32_t)((it * g.H + iy) * g.W + ix);
-}
-
-// kTok: Q and O are token-major [B, h, T*H*W, 128] (the query block is
-// gathered and the output scattered directly); otherwise they are tile-major
-// [B, h, n_tiles, 128, 128].  K is always tile-major: each K block is re-read
-// by every query block that keeps it, so it pays to store it contiguously.
+// kTok: Q, K and O are token-major [B, h, T*H*W, 128] (the query block is
+// gathered, the key blocks are gathered by the LDS loads and the output is
+// scattered directly); otherwise Q, K and O are tile-major
+// [B, h, n_tiles, 128, 128].  V is always dim-major tiles: the P.V product
+// needs 8 consecutive keys of one channel per lane.
 template <bool kTok>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
@@ -215,7 +235,7 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
     qb = qhead + (block_origin(g, qi) + in_block_offset(g, wave * 32 + (lane & 31))) * kHeadDim;
   }
   const uint8_t* kb = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(a.k_t) +
-                                                       bh * g.n_tiles * kTileElems);
+                                                       bh * g.n_tiles * kTileElems);   // = bh * N * 128
   const uint8_t* vb = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(a.v_t) +
                                                        bh * g.n_tiles * kTileElems);
   const bool dense = a.kv_cnt == nullptr;
@@ -242,8 +262,8 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   // Unit u = keys 64*(u%2) .. of the (u/2)-th kept block, in slot u%2 of the
   // K and V^T rings; unit u+1 is loaded while unit u is computed.
   const int units = 2 * cnt;
-  const DmaOffsets doff = dma_offsets(wv, lane);
-  const __amdgpu_buffer_rsrc_t krs = block_rsrc(kb, g.n_tiles), vrs = block_rsrc(vb, g.n_tiles);
+  const DmaOffsets doff = dma_offsets<kTok>(g, wv, lane);
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc(kb, g.n_tiles), vrs = head_rsrc(vb, g.n_tiles);
   // Kept-block ids, 64 at a time: lane i holds entry ibase + i.
   int ibase = 0;
   int ids = (!dense && lane < cnt) ? idx[lane] : 0;
@@ -257,7 +277,7 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   };
   if (units > 0) {
     const int64_t j0 = block_at(0);
-    dma_k(smem, krs, j0, 0, wv, doff);
+    dma_k<kTok>(smem, krs, g, j0, 0, wv, doff);
     dma_v(smem + 2 * kSlotBytes, vrs, j0, 0, wv, doff);
   }
 
@@ -267,7 +287,7 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
     const int slot = u & 1;
     if (u + 1 < units) {
       const int64_t j = block_at((u + 1) >> 1);
-      dma_k(smem + (1 - slot) * kSlotBytes, krs, j, (u + 1) & 1, wv, doff);
+      dma_k<kTok>(smem + (1 - slot) * kSlotBytes, krs, g, j, (u + 1) & 1, wv, doff);
       dma_v(smem + (3 - slot) * kSlotBytes, vrs, j, (u + 1) & 1, wv, doff);
     }
     const uint8_t* sK = smem + slot * kSlotBytes;
