@@ -96,6 +96,8 @@ def _load():
             "orc_topk": (ctypes.c_int, [G, i32, i32, i32, i32, i64, i64, vp, i32, i32, vp]),
             "orc_build_lists": (ctypes.c_int, [G, i32, i32, i32, u32, vp, i32, i32, vp, vp, vp]),
             "orc_attention": (None, [G, f64, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp]),
+            "orc_attention_bwd": (None, [G, f64, vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, i64,
+                                         vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -261,6 +263,37 @@ def attention(wl, q, k, v, kv_idx, kv_cnt, rows=None, scale=None):
     _load().orc_attention(ctypes.byref(_geom(wl)), sc, _p(q), _p(k), _p(v), _p(kv_idx),
                           _p(kv_cnt), mk, rows.size, _p(rows), _p(o), _p(lse))
     return o, lse
+
+
+def attention_bwd(wl, q, k, v, dout, kv_idx, kv_cnt, q_rows=None, k_rows=None, scale=None):
+    """Gradients of Step 4's block-sparse attention with the kept lists held
+    fixed ([TR] section "SSTA: Selective and Sliding Tile Attention": the
+    attention equation, Step 4 and the paragraph on integrating SSTA during
+    distillation training).
+
+    ``q_rows``: flat query-block rows (b*heads + h)*n_tiles + i whose dq is
+    wanted; ``k_rows``: key-block rows whose dk, dv are wanted (defaults: all).
+    Returns (dq [len(q_rows), R, D], dk [len(k_rows), R, D], dv [len(k_rows), R, D])
+    in fp64, rows in in-block token order.
+    """
+    n = n_tiles(wl)
+    R = tile_tokens(wl)
+    allrows = np.arange(wl.batch * wl.heads * n, dtype=np.int64)
+    q_rows = allrows if q_rows is None else np.ascontiguousarray(q_rows, dtype=np.int64)
+    k_rows = allrows if k_rows is None else np.ascontiguousarray(k_rows, dtype=np.int64)
+    q, k, v, dout = (np.ascontiguousarray(a, dtype=np.uint16) for a in (q, k, v, dout))
+    kv_idx = np.ascontiguousarray(kv_idx, dtype=np.int32)
+    kv_cnt = np.ascontiguousarray(kv_cnt, dtype=np.int32)
+    mk = kv_idx.shape[-1]
+    D = wl.head_dim
+    dq = np.empty((q_rows.size, R, D), np.float64)
+    dk = np.empty((k_rows.size, R, D), np.float64)
+    dv = np.empty((k_rows.size, R, D), np.float64)
+    sc = default_scale(wl) if scale is None else float(scale)
+    _load().orc_attention_bwd(ctypes.byref(_geom(wl)), sc, _p(q), _p(k), _p(v), _p(dout),
+                              _p(kv_idx), _p(kv_cnt), mk, q_rows.size, _p(q_rows), _p(dq),
+                              k_rows.size, _p(k_rows), _p(dk), _p(dv))
+    return dq, dk, dv
 
 
 def select(wl, q, k, flags: int = 0, topk=None, lambda_=DEFAULT_LAMBDA, beta=DEFAULT_BETA):

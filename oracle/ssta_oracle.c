@@ -395,3 +395,154 @@ void orc_attention(const orc_geom* g, double scale, const uint16_t* q, const uin
     free(keys);
   }
 }
+
+/*
+ * Gradients of the block-sparse attention of Step 4 ([TR] "SSTA: Selective and
+ * Sliding Tile Attention", the attention equation and Step 4; the same section's
+ * paragraph on parameter-free integration: SSTA is applied while the model is
+ * trained during distillation, so gradients flow through the sparse attention
+ * with the kept lists held fixed -- the selection is an integer and carries none).
+ *
+ * For a query token a of block i with kept key tokens b (the tokens of the
+ * blocks in kv_idx[i]):  s_ab = scale q_a.k_b,  p_ab = softmax_b(s_ab),
+ * o_a = sum_b p_ab v_b.  Given dO:
+ *   D_a   = dO_a . o_a
+ *   dS_ab = p_ab (dO_a . v_b - D_a)
+ *   dq_a  = scale sum_b dS_ab k_b
+ *   dk_b  = scale sum_a dS_ab q_a      (over every query token a that keeps b)
+ *   dv_b  = sum_a p_ab dO_a
+ * Everything in fp64 from the exact widening of the bf16 inputs.
+ * dq is returned for the query-block rows q_rows, dk and dv for the key-block
+ * rows k_rows (flat ids (b*heads + h)*n_tiles + block), in in-block token order.
+ */
+
+/* Softmax row of query token (bh, nq) over the key tokens keys[0..m): p (m), o (D), D_a. */
+static void bwd_row(const orc_geom* g, double scale, int64_t bh, int64_t nq, const uint16_t* q,
+                    const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                    const int64_t* keys, int64_t m, double* qv, double* dov, double* p,
+                    double* o, double* dsum) {
+  const int64_t N = (int64_t)g->T * g->H * g->W, D = g->head_dim;
+  for (int64_t d = 0; d < D; ++d) {
+    qv[d] = (double)bf16_to_f32(q[(bh * N + nq) * D + d]);
+    dov[d] = (double)bf16_to_f32(dout[(bh * N + nq) * D + d]);
+    o[d] = 0.0;
+  }
+  double mx = -INFINITY;
+  for (int64_t t = 0; t < m; ++t) {
+    const uint16_t* kr = k + (bh * N + keys[t]) * D;
+    double acc = 0.0;
+    for (int64_t d = 0; d < D; ++d) acc += qv[d] * (double)bf16_to_f32(kr[d]);
+    p[t] = acc * scale;
+    if (p[t] > mx) mx = p[t];
+  }
+  double l = 0.0;
+  for (int64_t t = 0; t < m; ++t) {
+    p[t] = exp(p[t] - mx);
+    l += p[t];
+  }
+  for (int64_t t = 0; t < m; ++t) {
+    p[t] /= l;
+    const uint16_t* vr = v + (bh * N + keys[t]) * D;
+    for (int64_t d = 0; d < D; ++d) o[d] += p[t] * (double)bf16_to_f32(vr[d]);
+  }
+  double da = 0.0;
+  for (int64_t d = 0; d < D; ++d) da += dov[d] * o[d];
+  *dsum = da;
+}
+
+/* dS_ab for the row (p holds the probabilities, overwritten with dS). */
+static void bwd_ds(const orc_geom* g, int64_t bh, const uint16_t* v, const int64_t* keys,
+                   int64_t m, const double* dov, double da, double* p) {
+  const int64_t N = (int64_t)g->T * g->H * g->W, D = g->head_dim;
+  for (int64_t t = 0; t < m; ++t) {
+    const uint16_t* vr = v + (bh * N + keys[t]) * D;
+    double dp = 0.0;
+    for (int64_t d = 0; d < D; ++d) dp += dov[d] * (double)bf16_to_f32(vr[d]);
+    p[t] = p[t] * (dp - da);
+  }
+}
+
+static int64_t kept_keys(const orc_geom* g, int64_t row, const int32_t* kv_idx,
+                         const int32_t* kv_cnt, int32_t max_kept, int64_t* keys) {
+  const int32_t R = orc_tile_tokens(g);
+  int64_t m = 0;
+  for (int32_t c = 0; c < kv_cnt[row]; ++c) {
+    const int32_t j = kv_idx[row * max_kept + c];
+    for (int32_t rr = 0; rr < R; ++rr) keys[m++] = orc_tile_to_token(g, j, rr);
+  }
+  return m;
+}
+
+void orc_attention_bwd(const orc_geom* g, double scale, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* v, const uint16_t* dout, const int32_t* kv_idx,
+                       const int32_t* kv_cnt, int32_t max_kept, int64_t n_qrows,
+                       const int64_t* q_rows, double* dq_out, int64_t n_krows,
+                       const int64_t* k_rows, double* dk_out, double* dv_out) {
+  const int64_t N = (int64_t)g->T * g->H * g->W, D = g->head_dim, n = orc_n_tiles(g);
+  const int32_t R = orc_tile_tokens(g);
+  const size_t cap = (size_t)max_kept * R + 8;
+#pragma omp parallel
+  {
+    double* p = (double*)malloc(sizeof(double) * cap);
+    int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * cap);
+    double* qv = (double*)malloc(sizeof(double) * (size_t)D);
+    double* dov = (double*)malloc(sizeof(double) * (size_t)D);
+    double* o = (double*)malloc(sizeof(double) * (size_t)D);
+    /* dq: one selected query-block row per iteration */
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t a = 0; a < n_qrows; ++a) {
+      const int64_t row = q_rows[a], bh = row / n, i = row % n;
+      const int64_t m = kept_keys(g, row, kv_idx, kv_cnt, max_kept, keys);
+      for (int32_t r = 0; r < R; ++r) {
+        double* dq = dq_out + (a * R + r) * D;
+        for (int64_t d = 0; d < D; ++d) dq[d] = 0.0;
+        if (m == 0) continue;
+        double da;
+        bwd_row(g, scale, bh, orc_tile_to_token(g, i, r), q, k, v, dout, keys, m, qv, dov, p,
+                o, &da);
+        bwd_ds(g, bh, v, keys, m, dov, da, p);
+        for (int64_t t = 0; t < m; ++t) {
+          const uint16_t* kr = k + (bh * N + keys[t]) * D;
+          for (int64_t d = 0; d < D; ++d) dq[d] += scale * p[t] * (double)bf16_to_f32(kr[d]);
+        }
+      }
+    }
+    /* dk, dv: one selected key-block row per iteration; every query block of
+       the head that keeps it contributes, in ascending block order */
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t a = 0; a < n_krows; ++a) {
+      const int64_t krow = k_rows[a], bh = krow / n, j = krow % n;
+      double* dk = dk_out + a * R * D;
+      double* dv = dv_out + a * R * D;
+      for (int64_t e = 0; e < (int64_t)R * D; ++e) dk[e] = dv[e] = 0.0;
+      for (int64_t i = 0; i < n; ++i) {
+        const int64_t row = bh * n + i;
+        int32_t pos = -1;
+        for (int32_t c = 0; c < kv_cnt[row]; ++c)
+          if (kv_idx[row * max_kept + c] == j) pos = c;
+        if (pos < 0) continue;
+        const int64_t m = kept_keys(g, row, kv_idx, kv_cnt, max_kept, keys);
+        for (int32_t r = 0; r < R; ++r) {
+          double da;
+          bwd_row(g, scale, bh, orc_tile_to_token(g, i, r), q, k, v, dout, keys, m, qv, dov,
+                  p, o, &da);
+          /* keep p for dv before it becomes dS */
+          for (int32_t rr = 0; rr < R; ++rr) {
+            const double pb = p[(int64_t)pos * R + rr];
+            for (int64_t d = 0; d < D; ++d) dv[rr * D + d] += pb * dov[d];
+          }
+          bwd_ds(g, bh, v, keys, m, dov, da, p);
+          for (int32_t rr = 0; rr < R; ++rr) {
+            const double ds = p[(int64_t)pos * R + rr];
+            for (int64_t d = 0; d < D; ++d) dk[rr * D + d] += scale * ds * qv[d];
+          }
+        }
+      }
+    }
+    free(p);
+    free(keys);
+    free(qv);
+    free(dov);
+    free(o);
+  }
+}

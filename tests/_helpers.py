@@ -35,10 +35,11 @@ def geom_of(wl):
     return m.make_geom(wl.batch, wl.heads, wl.T, wl.H, wl.W, tile=wl.tile, head_dim=wl.head_dim)
 
 
-def params_of(wl, flags=0, topk=None):
+def params_of(wl, flags=0, topk=None, lambda_=None, beta=None):
     import video_dit_block_tile_amd as m
     return m.make_params(win=wl.win, topk=wl.topk if topk is None else topk,
-                         lambda_=float(oracle.DEFAULT_LAMBDA), beta=float(oracle.DEFAULT_BETA),
+                         lambda_=float(oracle.DEFAULT_LAMBDA if lambda_ is None else lambda_),
+                         beta=float(oracle.DEFAULT_BETA if beta is None else beta),
                          scale=oracle.default_scale(wl), flags=flags)
 
 

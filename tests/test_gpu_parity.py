@@ -252,3 +252,20 @@ def test_calibrate_mfma_runs():
     m.ssta_calibrate_mfma(ops, sink, grid, iters)
     torch.cuda.synchronize()
     assert torch.all(sink == 4 * 16 * 16 * iters)
+
+
+@pytest.mark.parametrize("name", ["grid32-w1-k2", "ragged"])
+def test_similarity_only_variant(name):
+    """lambda = 1, beta = 0 through every GPU step: scores, ids and lists bit-exact."""
+    import video_dit_block_tile_amd as m
+    wl = si.ALL[name]
+    q, k, v = si.make_qkv(wl)
+    sel = oracle.select(wl, q, k, lambda_=1.0, beta=0.0)
+    plan = m.SstaPlan(geom_of(wl), params_of(wl, lambda_=1.0, beta=0.0), bitmask=True)
+    plan.run(to_dev(q), to_dev(k), to_dev(v))
+    torch.cuda.synchronize()
+    assert np.array_equal(plan.topk_idx.cpu().numpy(), sel["topk"])
+    assert np.array_equal(plan.kv_idx.cpu().numpy(), sel["kv_idx"])
+    assert np.array_equal(plan.kv_cnt.cpu().numpy(), sel["kv_cnt"])
+    rows = sample_rows(wl, 24, seed=4)
+    _check_attention(wl, q, k, v, sel, plan, rows)

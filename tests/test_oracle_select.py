@@ -113,3 +113,30 @@ def test_and_lists():
         want = sorted(set(oracle.window(wl, i).tolist()) & set(tk[0, h, i].tolist()))
         c = out["kv_cnt"][0, h, i]
         assert out["kv_idx"][0, h, i, :c].tolist() == want
+
+
+@pytest.mark.parametrize("name", ["grid32-w1-k2", "ragged"])
+def test_similarity_only_sampling(name):
+    """lambda = 1, beta = 0 (the similarity-only variant): Score_i equals Score_s
+    exactly, and the kept ids are the k most query-similar key blocks, checked
+    against cosines recomputed in fp64 wherever the k-th gap is not a near tie."""
+    wl = si.ALL[name]
+    q, k = si.generate(wl, 0), si.generate(wl, 1)
+    out = oracle.select(wl, q, k, lambda_=1.0, beta=0.0)
+    qh, kh = out["q_hat"], out["k_hat"]
+    gs = oracle.scores(qh, kh, out["red"] * 0.0, 1.0, 0.0)
+    assert np.array_equal(out["scores"].view(np.uint32), gs.view(np.uint32))
+    qp = oracle.pool(wl, q).astype(np.float64)
+    kp = oracle.pool(wl, k).astype(np.float64)
+    cos = np.einsum("bhid,bhjd->bhij", qp / np.linalg.norm(qp, axis=-1, keepdims=True),
+                    kp / np.linalg.norm(kp, axis=-1, keepdims=True))
+    kk = min(wl.topk, wl.n_tiles)
+    checked = 0
+    for b, h, i in itertools.product(range(wl.batch), range(wl.heads), range(wl.n_tiles)):
+        row = cos[b, h, i]
+        order = np.argsort(-row, kind="stable")
+        if kk < wl.n_tiles and row[order[kk - 1]] - row[order[kk]] < 1e-5:
+            continue
+        assert out["topk"][b, h, i].tolist() == sorted(order[:kk].tolist())
+        checked += 1
+    assert checked > 0.9 * wl.batch * wl.heads * wl.n_tiles
