@@ -195,6 +195,38 @@ int ssta_attention_fwd_tokens(const ssta_geom_t* g, const ssta_params_t* p, cons
                               const int32_t* kv_cnt, int32_t max_kept, void* o, float* lse,
                               void* stream);
 
+/* Device workspace bytes that ssta_attention_bwd needs.  < 0 on a bad argument. */
+int64_t ssta_attention_bwd_workspace_bytes(const ssta_geom_t* g);
+
+/*
+ * Gradients of Step 4's block-sparse attention with the kept lists held fixed
+ * ("HunyuanVideo 1.5 Technical Report" summary page, section "SSTA: Selective
+ * and Sliding Tile Attention": the attention equation and Step 4; the same
+ * section applies SSTA while the model is trained during distillation, so
+ * gradients flow through the sparse attention; the block selection is an
+ * integer and carries none).  For a query token a and the tokens b of its
+ * kept blocks: p_ab = exp(scale q_a.k_b - lse_a), D_a = dO_a.O_a,
+ * dS_ab = p_ab (dO_a.v_b - D_a); dq_a = scale sum_b dS_ab k_b,
+ * dk_b = scale sum_a dS_ab q_a, dv_b = sum_a p_ab dO_a.
+ *   q, k, v, o, dout in : bf16 [batch, heads, T*H*W, head_dim] (token-major);
+ *                         o and lse are the forward's outputs for these inputs.
+ *   lse      in : fp32 [batch, heads, n_tiles, tile_tokens] (tile-major, as the
+ *                 forward writes it).  A query block that keeps nothing gets
+ *                 dq = 0 and contributes to no dk, dv.
+ *   kv_idx, kv_cnt, max_kept: the forward's kept lists (NULL, NULL, 0: dense).
+ *   dq, dk, dv out : bf16 [batch, heads, T*H*W, head_dim] (token-major).
+ *   workspace: device scratch of ws_bytes >= ssta_attention_bwd_workspace_bytes()
+ *              (dim-major copies of K, Q, dO; per-query (lse, D); the transposed
+ *              lists).  Caller-owned; contents on return are unspecified.
+ * Probabilities and dS enter the matrix products as bf16, accumulation is fp32.
+ * Errors: as ssta_attention_fwd, plus SSTA_ERR_WORKSPACE.
+ */
+int ssta_attention_bwd(const ssta_geom_t* g, const ssta_params_t* p, const void* q,
+                       const void* k, const void* v, const void* o, const void* dout,
+                       const float* lse, const int32_t* kv_idx, const int32_t* kv_cnt,
+                       int32_t max_kept, void* dq, void* dk, void* dv, void* workspace,
+                       size_t ws_bytes, void* stream);
+
 /* Measurement aid, not a step of the method.  For callers that want the
  * sustained bf16 matrix-core rate of the chip next to the attention kernel:
  * `grid` workgroups of 4 waves each run `iters` rounds of 4 independent

@@ -1,0 +1,102 @@
+"""GPU parity of the attention backward (dq, dk, dv with the kept lists held
+fixed) against the fp64 oracle, through the C ABI.
+
+Bars (bf16 inputs and outputs; probabilities and dS enter the products as
+bf16, accumulation in fp32): per tensor, max-abs error <= 2e-2 * max|ref| and
+mean-abs error <= 5e-3 * mean|ref|.  Empty rows give exactly zero dq.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+from _helpers import geom_of, params_of, sample_rows, to_dev, token_rows
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL = 2e-2
+MEAN_REL = 5e-3
+
+
+def _rows_of(wl, t, rows):
+    """fp32 [len(rows), 128, 128] block rows of a token-major device tensor."""
+    x = t.float().cpu().numpy().reshape(wl.batch * wl.heads, wl.n_tokens, 128)
+    tok = token_rows(wl, rows)
+    bh = np.asarray(rows) // wl.n_tiles
+    return x[bh[:, None], tok].astype(np.float64)
+
+
+def _check(name, got, ref):
+    err = np.abs(got - ref)
+    mx, mean = float(err.max()), float(err.mean())
+    rmx, rmean = float(np.abs(ref).max()), float(np.abs(ref).mean())
+    print("  %s: max-abs %.3e (ref max %.3e), mean-abs %.3e (ref mean %.3e)"
+          % (name, mx, rmx, mean, rmean), flush=True)
+    assert mx <= MAX_REL * rmx and mean <= MEAN_REL * rmean, name
+
+
+def _run(wl, q, k, v, do, flags=0, dense=False):
+    import video_dit_block_tile_amd as m
+    g, p = geom_of(wl), params_of(wl, flags)
+    plan = m.SstaPlan(g, p, dense=dense)
+    qd, kd, vd, dod = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
+    plan.run(qd, kd, vd)
+    dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
+    ws = torch.empty(m.ssta_attention_bwd_workspace_bytes(g), dtype=torch.uint8, device="cuda")
+    idx, cnt = (None, None) if dense else (plan.kv_idx, plan.kv_cnt)
+    m.ssta_attention_bwd(g, p, qd, kd, vd, plan.o, dod, plan.lse, idx, cnt, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    return plan, dq, dk, dv
+
+
+@pytest.mark.parametrize("name", ["tiny", "grid32-w1-k2", "ragged", "dup-ties"])
+def test_backward_vs_oracle(name):
+    wl = si.ALL[name]
+    q, k, v = si.make_qkv(wl)
+    do = si.generate(wl, 3)
+    print("[%s]" % name, flush=True)
+    plan, dq, dk, dv = _run(wl, q, k, v, do)
+    sel = oracle.select(wl, q, k)
+    assert np.array_equal(plan.kv_idx.cpu().numpy(), sel["kv_idx"])
+    rows = np.arange(wl.batch * wl.heads * wl.n_tiles)
+    rq, rk, rv = oracle.attention_bwd(wl, q, k, v, do, sel["kv_idx"], sel["kv_cnt"])
+    _check("dq", _rows_of(wl, dq, rows), rq)
+    _check("dk", _rows_of(wl, dk, rows), rk)
+    _check("dv", _rows_of(wl, dv, rows), rv)
+
+
+def test_backward_dense_equals_all_kept():
+    wl = si.ALL["wide-k"]                          # every block kept
+    q, k, v = si.make_qkv(wl)
+    do = si.generate(wl, 3)
+    _, dq1, dk1, dv1 = _run(wl, q, k, v, do)
+    _, dq2, dk2, dv2 = _run(wl, q, k, v, do, dense=True)
+    assert torch.equal(dq1, dq2) and torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+
+
+def test_backward_empty_rows():
+    wl = si.ALL["grid32-w1-k2"]
+    q, k, v = si.make_qkv(wl)
+    do = si.generate(wl, 3)
+    flags = oracle.COMBINE_AND | oracle.TOPK_EXCLUDE_WINDOW   # nothing kept anywhere
+    plan, dq, dk, dv = _run(wl, q, k, v, do, flags)
+    assert int(plan.kv_cnt.sum()) == 0
+    assert not dq.any() and not dk.any() and not dv.any()
+
+
+def test_backward_full_size_sampled():
+    wl = si.CONFIGS["720p-10s"]
+    q, k, v = si.make_qkv(wl)
+    do = si.generate(wl, 3)
+    print("[720p-10s] inputs ready", flush=True)
+    plan, dq, dk, dv = _run(wl, q, k, v, do)
+    print("[720p-10s] gpu done", flush=True)
+    kv_idx, kv_cnt = plan.kv_idx.cpu().numpy(), plan.kv_cnt.cpu().numpy()
+    rows = sample_rows(wl, 2, seed=5)[:10]
+    krows = rows[:4]
+    rq, rk, rv = oracle.attention_bwd(wl, q, k, v, do, kv_idx, kv_cnt, rows, krows)
+    print("[720p-10s] oracle done", flush=True)
+    _check("dq", _rows_of(wl, dq, rows), rq)
+    _check("dk", _rows_of(wl, dk, krows), rk)
+    _check("dv", _rows_of(wl, dv, krows), rv)

@@ -70,6 +70,9 @@ SIGNATURES = {
     "ssta_attention_fwd_tokens": (ctypes.c_int,
                                   [_G, _P, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "ssta_calibrate_mfma": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp]),
+    "ssta_attention_bwd_workspace_bytes": (_i64, [_G]),
+    "ssta_attention_bwd": (ctypes.c_int, [_G, _P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                          _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "ssta_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ssta_last_hip_error": (ctypes.c_int, []),
 }
@@ -294,3 +297,32 @@ def ssta_calibrate_mfma(operands, sink, grid: int, iters: int, stream=None):
     _expect("operands", operands, (256, 8), torch.bfloat16)
     _expect("sink", sink, (grid * 256,), torch.float32)
     _call("ssta_calibrate_mfma", _ptr(operands), _ptr(sink), grid, iters, _stream(stream))
+
+
+def ssta_attention_bwd_workspace_bytes(g: SstaGeom) -> int:
+    v = load().ssta_attention_bwd_workspace_bytes(ctypes.byref(g))
+    if v < 0:
+        raise SstaError("ssta_attention_bwd_workspace_bytes", v)
+    return v
+
+
+def ssta_attention_bwd(g: SstaGeom, p: SstaParams, q, k, v, o, dout, lse, kv_idx, kv_cnt, dq, dk,
+                       dv, workspace, stream=None):
+    """Gradients of the block-sparse attention with the kept lists fixed; all
+    tensors token-major bf16 [B, h, N, 128] except lse (tile-major fp32)."""
+    tok = (g.batch, g.heads, g.n_tokens, g.head_dim)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
+                    ("dk", dk), ("dv", dv)):
+        _expect(name, t, tok, torch.bfloat16)
+    _expect("lse", lse, (g.batch, g.heads, g.n_tiles, g.tile_tokens), torch.float32)
+    if kv_cnt is None:
+        if kv_idx is not None:
+            raise ValueError("dense attention takes neither kv_idx nor kv_cnt")
+        mk = 0
+    else:
+        _expect("kv_cnt", kv_cnt, (g.batch, g.heads, g.n_tiles), torch.int32)
+        mk = kv_idx.shape[-1]
+        _expect("kv_idx", kv_idx, (g.batch, g.heads, g.n_tiles, mk), torch.int32)
+    _call("ssta_attention_bwd", ctypes.byref(g), ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+          _ptr(o), _ptr(dout), _ptr(lse), _ptr(kv_idx), _ptr(kv_cnt), mk, _ptr(dq), _ptr(dk),
+          _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream))

@@ -33,6 +33,7 @@ SOURCES = {
     "k_mask.hip": [],
     "k_attn.hip": ["-fno-honor-nans"],
     "k_calib.hip": [],
+    "k_attn_bwd.hip": ["-fno-honor-nans"],
 }
 
 

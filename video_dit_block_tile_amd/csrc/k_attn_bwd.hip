@@ -1,0 +1,497 @@
+// Gradients of Step 4's block-sparse attention with the kept lists held fixed
+// ("HunyuanVideo 1.5 Technical Report" summary page, section "SSTA: Selective
+// and Sliding Tile Attention": the attention equation, Step 4, and the
+// paragraph on integrating SSTA while the model is trained during
+// distillation).  For a query token a and a kept key token b,
+//   p_ab = exp(s_ab - lse_a),  D_a = dO_a . O_a,
+//   dS_ab = p_ab (dO_a . v_b - D_a),
+//   dq_a = scale sum_b dS_ab k_b,  dk_b = scale sum_a dS_ab q_a,
+//   dv_b = sum_a p_ab dO_a,
+// with lse_a the forward's log-sum-exp, so the probabilities are recomputed
+// exactly instead of with a running max.
+//
+// gfx950 design.  Three kernels, each one workgroup of 4 waves per block and
+// the matrix-core layouts of the forward kernel (v_mfma_f32_32x32x16_bf16; a
+// lane feeds row kperm(lane) of the A operand, bits 2 and 3 swapped, so every
+// 8 output registers are 8 consecutive rows and feed the next product as its
+// B operand straight from registers):
+//   k_attn_bwd_dq  per query block, over its kept key blocks in units of 32
+//                  keys: S^T = K Q^T and dP^T = V dO^T (Q, dO of the wave's 32
+//                  queries held in registers), dS^T in registers, then
+//                  dQ^T += K^T dS^T with K^T from dim-major tiles;
+//   k_attn_bwd_dv  per key block, over the query blocks that keep it, in
+//                  units of 32 queries: S = Q K^T (the wave's 32 keys held in
+//                  registers), P in registers, dV^T += dO^T P;
+//   k_attn_bwd_dk  per key block likewise: S = Q K^T, dP = dO V^T, dS in
+//                  registers, dK^T += Q^T dS.
+// dV and dK are separate kernels so that each keeps two waves per SIMD (their
+// fused accumulators would not fit 256 VGPRs).  Every streamed unit (token
+// rows gathered from token-major memory, 32-column slices of dim-major tiles,
+// and the per-query (lse*log2 e, D) pairs) goes straight into LDS with
+// buffer_load_dwordx4 ... lds into a two-slot ring, as in the forward kernel.
+//
+// Algorithmic work per kept (query block, key block) pair: five 128^3
+// products (S, dP, dQ, dK, dV) = 21.0 MFLOP; the split recomputes S twice and
+// dP once more, 33.6 MFLOP executed.
+#include "ssta_internal.h"
+
+namespace ssta {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+constexpr int kBlockBytes = kTileTokens * kHeadDim * 2;   // 32 KB: one block of one tensor
+constexpr int kUnitBytes = kBlockBytes / 4;               // 32 rows, or 32 columns of a tile
+constexpr unsigned kWaitVm0 = 0x0F70;                     // s_waitcnt vmcnt(0)
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// Unit of 32 token rows (256 B each): chunk c of row r sits at chunk c ^ (r % 16).
+__device__ __forceinline__ int swz_row(int row, int chunk) {
+  return row * 256 + ((chunk ^ (row & 15)) << 4);
+}
+// Unit of 32 columns of a dim-major tile (128 channel rows of 64 B): chunk c
+// of row d sits at chunk c ^ ((d / 4) % 4), so 16 consecutive rows read one
+// chunk from 16 distinct bank groups.
+__device__ __forceinline__ int swz_col(int d, int chunk) {
+  return d * 64 + ((chunk ^ ((d >> 2) & 3)) << 4);
+}
+
+__device__ __forceinline__ int64_t block_origin(const Geo& g, int64_t j) {
+  const int64_t bt = j / ((int64_t)g.ny * g.nx), by = (j / g.nx) % g.ny, bx = j % g.nx;
+  return ((bt * g.tt) * g.H + by * g.th) * (int64_t)g.W + bx * g.tw;
+}
+__device__ __forceinline__ uint32_t block_origin32(const Geo& g, uint32_t j) {
+  const uint32_t nyx = (uint32_t)g.ny * (uint32_t)g.nx;
+  const uint32_t bt = j / nyx, rem = j - bt * nyx;
+  const uint32_t by = rem / (uint32_t)g.nx, bx = rem - by * (uint32_t)g.nx;
+  return ((bt * (uint32_t)g.tt) * (uint32_t)g.H + by * (uint32_t)g.th) * (uint32_t)g.W +
+         bx * (uint32_t)g.tw;
+}
+// Token offset (from the block's first token) of in-block position r.  The
+// position is a bit-field code of (t, y, x) offsets (block sizes are powers of
+// two), so positions with disjoint bits add: off(32p + r) = off(32p) + off(r).
+__device__ __forceinline__ uint32_t in_block_offset(const Geo& g, int r) {
+  const int ltw = __builtin_ctz(g.tw), lth = __builtin_ctz(g.th);
+  const int it = r >> (ltw + lth), iy = (r >> ltw) & (g.th - 1), ix = r & (g.tw - 1);
+  return (uint32_t)((it * g.H + iy) * g.W + ix);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Per-lane source offsets of this wave's two 1 KB loads of a row unit and of
+// a column unit.
+struct UnitOffsets {
+  uint32_t rows[2], cols[2];
+};
+__device__ __forceinline__ UnitOffsets unit_offsets(const Geo& g, int wave, int lane) {
+  UnitOffsets o;
+#pragma unroll
+  for (int mm = 0; mm < 2; ++mm) {
+    const int b = 2 * wave + mm;                   // 1 KB destination block 0..7
+    const int row = 4 * b + (lane >> 4);           // token rows 4b .. 4b+3
+    o.rows[mm] = in_block_offset(g, row) * 256 + (((lane & 15) ^ (row & 15)) << 4);
+    const int d = 16 * b + (lane >> 2);            // channel rows 16b .. 16b+15
+    o.cols[mm] = d * 256 + (((lane & 3) ^ ((d >> 2) & 3)) << 4);
+  }
+  return o;
+}
+// Rows 32p .. 32p+31 of block j, gathered from token-major memory.
+__device__ __forceinline__ void dma_rows(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, const Geo& g,
+                                         uint32_t j, int p, int wave, const UnitOffsets& off) {
+  const uint32_t so = (block_origin32(g, j) + in_block_offset(g, 32 * p)) * 256u;
+#pragma unroll
+  for (int mm = 0; mm < 2; ++mm)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (2 * wave + mm) * 1024), 16,
+                                             off.rows[mm], so, 0, 0);
+}
+// Columns 32p .. 32p+31 of dim-major block j.
+__device__ __forceinline__ void dma_cols(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, uint32_t j,
+                                         int p, int wave, const UnitOffsets& off) {
+  const uint32_t so = j * (uint32_t)kBlockBytes + 64u * p;
+#pragma unroll
+  for (int mm = 0; mm < 2; ++mm)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (2 * wave + mm) * 1024), 16,
+                                             off.cols[mm], so, 0, 0);
+}
+
+// Kept-block ids of one list, 64 at a time (lane i holds entry base + i);
+// positions are requested in non-decreasing order.
+struct IdStream {
+  const int32_t* idx;
+  int cnt, base, ids;
+  bool dense;
+  __device__ __forceinline__ void init(const int32_t* p, int c, bool d, int lane) {
+    idx = p; cnt = c; dense = d; base = 0;
+    ids = (!d && lane < c) ? p[lane] : 0;
+  }
+  __device__ __forceinline__ uint32_t at(int pos, int lane) {
+    if (dense) return (uint32_t)pos;
+    if (pos >= base + 64) {
+      base += 64;
+      ids = (base + lane < cnt) ? idx[base + lane] : 0;
+    }
+    return (uint32_t)__builtin_amdgcn_readlane(ids, pos - base);
+  }
+};
+
+// Token-major row of token `tok` as 8 B operands of a 32x32x16 product:
+// channels 16*s + 8*hl .. +8.
+__device__ __forceinline__ void load_row_operand(bf16x8 (&f)[8], const uint16_t* row, int hl) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) f[s] = *reinterpret_cast<const bf16x8*>(row + 16 * s + 8 * hl);
+}
+
+// Writes a [128 ch x 32 tok] fp32 accumulator (lane: token l32, channels
+// 32*db + 8*g4 + 4*hl + 0..3) times `mul` as bf16 into the token's row.
+__device__ __forceinline__ void store_row(uint16_t* row, const f32x16 (&acc)[4], float mul,
+                                          int hl) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[db][4 * g4 + e] * mul);
+      *reinterpret_cast<bf16x4*>(row + 32 * db + 8 * g4 + 4 * hl) = w;
+    }
+}
+
+// ------------------------------------------------------------------ dQ
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void k_attn_bwd_dq(Geo g, BwdArgs a, int64_t slice) {
+  // slot s (24 KB): K rows | V rows | K^T columns of one 32-key unit
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 3 * kUnitBytes];
+  const int64_t bid = blockIdx.x;
+  const int64_t xcd = bid & 7, k8 = bid >> 3;
+  const int64_t bh = k8 / slice;
+  const int64_t qi = xcd * slice + (k8 - bh * slice);
+  if (qi >= g.n_tiles) return;
+  const int64_t row = bh * g.n_tiles + qi;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int kperm = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+  const int qrow = 32 * wv + l32;
+  const int64_t head = bh * g.N;
+  const int64_t qtok = head + block_origin(g, qi) + in_block_offset(g, qrow);
+
+  bf16x8 qf[8], df[8];
+  load_row_operand(qf, static_cast<const uint16_t*>(a.q) + qtok * kHeadDim, hl);
+  load_row_operand(df, static_cast<const uint16_t*>(a.dout) + qtok * kHeadDim, hl);
+  const float lse2 = a.ld[(row * kTileTokens + qrow) * 2];
+  const float dq_d = a.ld[(row * kTileTokens + qrow) * 2 + 1];
+  const float c = a.scale_log2;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+
+  const bool dense = a.kv_cnt == nullptr;
+  const int cnt = dense ? (int)g.n_tiles : a.kv_cnt[row];
+  IdStream ids;
+  ids.init(dense ? nullptr : a.kv_idx + row * a.max_kept, cnt, dense, lane);
+  const UnitOffsets off = unit_offsets(g, wv, lane);
+  const int64_t head_bytes = g.n_tiles * (int64_t)kBlockBytes;
+  const __amdgpu_buffer_rsrc_t krs = rsrc(static_cast<const uint16_t*>(a.k) + head * kHeadDim,
+                                          head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = rsrc(static_cast<const uint16_t*>(a.v) + head * kHeadDim,
+                                          head_bytes);
+  const __amdgpu_buffer_rsrc_t ktrs = rsrc(
+      static_cast<const uint16_t*>(a.k_cols) + bh * g.n_tiles * (int64_t)kTileTokens * kHeadDim,
+      head_bytes);
+  auto load_unit = [&](int u, uint8_t* dst) {
+    const uint32_t j = ids.at(u >> 2, lane);
+    const int p = u & 3;
+    dma_rows(dst, krs, g, j, p, wv, off);
+    dma_rows(dst + kUnitBytes, vrs, g, j, p, wv, off);
+    dma_cols(dst + 2 * kUnitBytes, ktrs, j, p, wv, off);
+  };
+
+  const int units = 4 * cnt;
+  if (units > 0) load_unit(0, smem);
+  for (int u = 0; u < units; ++u) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    uint8_t* cur = smem + (u & 1) * 3 * kUnitBytes;
+    if (u + 1 < units) load_unit(u + 1, smem + ((u + 1) & 1) * 3 * kUnitBytes);
+    const uint8_t* sK = cur;
+    const uint8_t* sV = cur + kUnitBytes;
+    const uint8_t* sKT = cur + 2 * kUnitBytes;
+
+    // S^T and dP^T for the unit's 32 keys: register r of lane (l32, hl) is
+    // query l32 and key 16*(r/8) + 8*hl + r%8.
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.0f;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(sK + swz_row(kperm, 2 * st + hl));
+      const bf16x8 va = *reinterpret_cast<const bf16x8*>(sV + swz_row(kperm, 2 * st + hl));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[st], dp, 0, 0, 0);
+    }
+    // dS^T = P^T (dP^T - D), as the B operand of k-step ks (keys 16*ks + 8*hl + e).
+    bf16x8 dsf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * ks + e;
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
+        dsf[ks][e] = (__bf16)(pr * (dp[r] - dq_d));
+      }
+    // dQ^T += K^T dS^T: A operand row d of K^T, the same 8 keys.
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8 kt =
+            *reinterpret_cast<const bf16x8*>(sKT + swz_col(32 * db + l32, 2 * ks + hl));
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsf[ks], acc[db], 0, 0, 0);
+      }
+  }
+  store_row(static_cast<uint16_t*>(a.dq) + qtok * kHeadDim, acc, a.scale, hl);
+}
+
+// ------------------------------------------------------------------ dV, dK
+
+// kDK = false: dV^T += dO^T P.  kDK = true: dK^T += Q^T dS with dS = P (dP - D).
+template <bool kDK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void k_attn_bwd_kv(Geo g, BwdArgs a, int64_t slice) {
+  // slot: Q rows | (dK: dO rows) | columns (dV: dO^T, dK: Q^T) | 32 (lse2, D) pairs
+  constexpr int kParts = kDK ? 3 : 2;
+  constexpr int kSlot = kParts * kUnitBytes + 256;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kSlot];
+  const int64_t bid = blockIdx.x;
+  const int64_t xcd = bid & 7, k8 = bid >> 3;
+  const int64_t bh = k8 / slice;
+  const int64_t kj = xcd * slice + (k8 - bh * slice);
+  if (kj >= g.n_tiles) return;
+  const int64_t krow = bh * g.n_tiles + kj;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int kperm = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+  const int kr = 32 * wv + l32;                  // this lane's key within the block
+  const int64_t head = bh * g.N;
+  const int64_t ktok = head + block_origin(g, kj) + in_block_offset(g, kr);
+
+  // B operands: the wave's 32 keys (and their values for dP).
+  bf16x8 kf[8], vf[8];
+  load_row_operand(kf, static_cast<const uint16_t*>(a.k) + ktok * kHeadDim, hl);
+  if (kDK) load_row_operand(vf, static_cast<const uint16_t*>(a.v) + ktok * kHeadDim, hl);
+  const float c = a.scale_log2;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+
+  const bool dense = a.q_cnt == nullptr;
+  const int cnt = dense ? (int)g.n_tiles : a.q_cnt[krow];
+  IdStream ids;
+  ids.init(dense ? nullptr : a.q_idx + krow * a.q_width, cnt, dense, lane);
+  const UnitOffsets off = unit_offsets(g, wv, lane);
+  const int64_t head_bytes = g.n_tiles * (int64_t)kBlockBytes;
+  const __amdgpu_buffer_rsrc_t qrs = rsrc(static_cast<const uint16_t*>(a.q) + head * kHeadDim,
+                                          head_bytes);
+  const __amdgpu_buffer_rsrc_t drs = rsrc(static_cast<const uint16_t*>(a.dout) + head * kHeadDim,
+                                          head_bytes);
+  const int64_t cols_off = bh * g.n_tiles * (int64_t)kTileTokens * kHeadDim;
+  const __amdgpu_buffer_rsrc_t crs =
+      rsrc(static_cast<const uint16_t*>(kDK ? a.q_cols : a.dout_cols) + cols_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t lrs =
+      rsrc(a.ld + bh * g.n_tiles * kTileTokens * 2, g.n_tiles * kTileTokens * 8);
+  auto load_unit = [&](int u, uint8_t* dst) {
+    const uint32_t i = ids.at(u >> 2, lane);
+    const int p = u & 3;
+    dma_rows(dst, qrs, g, i, p, wv, off);
+    if (kDK) dma_rows(dst + kUnitBytes, drs, g, i, p, wv, off);
+    dma_cols(dst + (kParts - 1) * kUnitBytes, crs, i, p, wv, off);
+    if (wv == 0 && lane < 16)   // 32 (lse2, D) pairs = 256 B
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          lrs, (lds_u8*)(dst + kParts * kUnitBytes), 16, (uint32_t)lane * 16,
+          (i * (uint32_t)kTileTokens + 32u * p) * 8u, 0, 0);
+  };
+
+  const int units = 4 * cnt;
+  if (units > 0) load_unit(0, smem);
+  for (int u = 0; u < units; ++u) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    uint8_t* cur = smem + (u & 1) * kSlot;
+    if (u + 1 < units) load_unit(u + 1, smem + ((u + 1) & 1) * kSlot);
+    const uint8_t* sQ = cur;
+    const uint8_t* sD = cur + kUnitBytes;
+    const uint8_t* sC = cur + (kParts - 1) * kUnitBytes;
+    const float* sL = reinterpret_cast<const float*>(cur + kParts * kUnitBytes);
+
+    // S (queries x keys, lane = key l32): register r is query 16*(r/8) + 8*hl + r%8.
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.0f;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(sQ + swz_row(kperm, 2 * st + hl));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[st], s, 0, 0, 0);
+      if (kDK) {
+        const bf16x8 da = *reinterpret_cast<const bf16x8*>(sD + swz_row(kperm, 2 * st + hl));
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[st], dp, 0, 0, 0);
+      }
+    }
+    // P (dV) or dS (dK) as the B operand of k-step ks (queries 16*ks + 8*hl + e).
+    bf16x8 bf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const f32x4* lp = reinterpret_cast<const f32x4*>(sL + 2 * (16 * ks + 8 * hl));
+      f32x4 lv[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) lv[x] = lp[x];   // (lse2, D) of 8 consecutive queries
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * ks + e;
+        const float lse2 = lv[e >> 1][(e & 1) * 2];
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
+        if (kDK) {
+          const float dd = lv[e >> 1][(e & 1) * 2 + 1];
+          bf[ks][e] = (__bf16)(pr * (dp[r] - dd));
+        } else {
+          bf[ks][e] = (__bf16)pr;
+        }
+      }
+    }
+    // dV^T += dO^T P  or  dK^T += Q^T dS: A operand row d, the same 8 queries.
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8 ca =
+            *reinterpret_cast<const bf16x8*>(sC + swz_col(32 * db + l32, 2 * ks + hl));
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca, bf[ks], acc[db], 0, 0, 0);
+      }
+  }
+  store_row(static_cast<uint16_t*>(kDK ? a.dk : a.dv) + ktok * kHeadDim, acc,
+            kDK ? a.scale : 1.0f, hl);
+}
+
+// ------------------------------------------------------------------ helpers
+
+// (lse * log2 e, D = dO . O) per query, tile-major like the LSE: one
+// workgroup per (batch*head, block), two threads per token (64 channels each).
+__global__ __launch_bounds__(256) void k_attn_bwd_prep(Geo g, const uint16_t* __restrict__ o,
+                                                       const uint16_t* __restrict__ dout,
+                                                       const float* __restrict__ lse,
+                                                       float* __restrict__ ld) {
+  const int64_t blk = blockIdx.x, bh = blk / g.n_tiles, tile = blk % g.n_tiles;
+  const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const int64_t tok = bh * g.N + tile_token(g, tile, r);
+  const uint16_t* orow = o + tok * kHeadDim + 64 * half;
+  const uint16_t* drow = dout + tok * kHeadDim + 64 * half;
+  float acc = 0.0f;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    const bf16x8 ov = *reinterpret_cast<const bf16x8*>(orow + 8 * x);
+    const bf16x8 dv = *reinterpret_cast<const bf16x8*>(drow + 8 * x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)ov[e], (float)dv[e], acc);
+  }
+  acc += __shfl_xor(acc, 1);
+  if (half == 0) {
+    const int64_t qi = blk * kTileTokens + r;
+    ld[qi * 2] = lse[qi] * kLog2e;
+    ld[qi * 2 + 1] = acc;
+  }
+}
+
+// Zero fill of a word array (no memset, so the sequence can be captured).
+__global__ __launch_bounds__(256) void k_fill_zero(uint32_t* __restrict__ p, int64_t words) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < words) p[i] = 0u;
+}
+
+// Transposed membership bits: mask_t[bh][j] has bit i set if query block i
+// keeps key block j.
+__global__ __launch_bounds__(256) void k_set_bits(Geo g, const int32_t* __restrict__ kv_idx,
+                                                  const int32_t* __restrict__ kv_cnt,
+                                                  int32_t max_kept, uint32_t* __restrict__ mask_t,
+                                                  int64_t words) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = t / max_kept, c = t % max_kept;
+  if (row >= g.bh * g.n_tiles || c >= kv_cnt[row]) return;
+  const int64_t bh = row / g.n_tiles, i = row % g.n_tiles;
+  const int64_t j = kv_idx[row * max_kept + c];
+  atomicOr(mask_t + (bh * g.n_tiles + j) * words + (i >> 5), 1u << (i & 31));
+}
+
+// Ascending query-block list of every key block from its bit row.
+__global__ __launch_bounds__(256) void k_gather_lists(Geo g, const uint32_t* __restrict__ mask_t,
+                                                      int64_t words, int32_t* __restrict__ q_idx,
+                                                      int32_t* __restrict__ q_cnt) {
+  const int64_t krow = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (krow >= g.bh * g.n_tiles) return;
+  const uint32_t* bits = mask_t + krow * words;
+  int32_t* out = q_idx + krow * g.n_tiles;
+  int32_t m = 0;
+  for (int64_t w = 0; w < words; ++w) {
+    uint32_t x = bits[w];
+    while (x) {
+      const int b = __builtin_ctz(x);
+      out[m++] = (int32_t)(w * 32 + b);
+      x &= x - 1;
+    }
+  }
+  q_cnt[krow] = m;
+}
+
+}  // namespace
+
+hipError_t launch_attention_bwd_prep(const Geo& g, const void* o, const void* dout,
+                                     const float* lse, float* ld, hipStream_t s) {
+  hipLaunchKernelGGL(k_attn_bwd_prep, dim3((unsigned)(g.bh * g.n_tiles)), dim3(256), 0, s, g,
+                     static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dout), lse,
+                     ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_lists(const Geo& g, const int32_t* kv_idx, const int32_t* kv_cnt,
+                                  int32_t max_kept, uint32_t* mask_t, int32_t* q_idx,
+                                  int32_t* q_cnt, hipStream_t s) {
+  const int64_t rows = g.bh * g.n_tiles;
+  const int64_t words = (g.n_tiles + 31) / 32;
+  const int64_t total = rows * words;
+  hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, mask_t,
+                     total);
+  if (max_kept > 0) {
+    const int64_t pairs = rows * max_kept;
+    hipLaunchKernelGGL(k_set_bits, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s, g,
+                       kv_idx, kv_cnt, max_kept, mask_t, words);
+  }
+  hipLaunchKernelGGL(k_gather_lists, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, g,
+                     mask_t, words, q_idx, q_cnt);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_bwd(const Geo& g, const BwdArgs& a, hipStream_t s) {
+  const int64_t slice = (g.n_tiles + 7) / 8;
+  const int64_t blocks = g.bh * slice * 8;
+  hipLaunchKernelGGL(k_attn_bwd_dq, dim3((unsigned)blocks), dim3(256), 0, s, g, a, slice);
+  hipLaunchKernelGGL(k_attn_bwd_kv<false>, dim3((unsigned)blocks), dim3(256), 0, s, g, a, slice);
+  hipLaunchKernelGGL(k_attn_bwd_kv<true>, dim3((unsigned)blocks), dim3(256), 0, s, g, a, slice);
+  return hipGetLastError();
+}
+
+}  // namespace ssta

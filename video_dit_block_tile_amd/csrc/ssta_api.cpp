@@ -349,6 +349,96 @@ int ssta_attention_fwd_tokens(const ssta_geom_t* g, const ssta_params_t* p, cons
   return attention_common(g, p, q, k, v_t, kv_idx, kv_cnt, max_kept_, o, lse, stream, 1);
 }
 
+namespace {
+struct BwdLayout {
+  int64_t k_cols, q_cols, d_cols, ld, mask, q_idx, q_cnt, total;
+};
+BwdLayout bwd_layout(const Geo& g) {
+  BwdLayout w;
+  const int64_t tensor = g.bh * g.n_tiles * int64_t(ssta::kTileTokens) * ssta::kHeadDim * 2;
+  const int64_t rows = g.bh * g.n_tiles;
+  w.k_cols = 0;
+  w.q_cols = w.k_cols + align256(tensor);
+  w.d_cols = w.q_cols + align256(tensor);
+  w.ld = w.d_cols + align256(tensor);
+  w.mask = w.ld + align256(rows * ssta::kTileTokens * 8);
+  w.q_idx = w.mask + align256(rows * ((g.n_tiles + 31) / 32) * 4);
+  w.q_cnt = w.q_idx + align256(rows * g.n_tiles * 4);
+  w.total = w.q_cnt + align256(rows * 4);
+  return w;
+}
+}  // namespace
+
+int64_t ssta_attention_bwd_workspace_bytes(const ssta_geom_t* g) {
+  Geo geo;
+  SSTA_TRY(check_geom(g, &geo));
+  return bwd_layout(geo).total;
+}
+
+int ssta_attention_bwd(const ssta_geom_t* g, const ssta_params_t* p, const void* q,
+                       const void* k, const void* v, const void* o, const void* dout,
+                       const float* lse, const int32_t* kv_idx, const int32_t* kv_cnt,
+                       int32_t max_kept_, void* dq, void* dk, void* dv, void* workspace,
+                       size_t ws_bytes, void* stream) {
+  Geo geo;
+  SSTA_TRY(check_geom(g, &geo));
+  SSTA_TRY(check_params(p));
+  for (const void* ptr : {q, k, v, o, dout, static_cast<const void*>(lse)})
+    SSTA_TRY(check_ptr(ptr, false));
+  for (void* ptr : {dq, dk, dv}) SSTA_TRY(check_ptr(ptr, false));
+  if (geo.n_tiles * int64_t(ssta::kTileTokens) * ssta::kHeadDim * 2 > 0x7FFFFFFF)
+    return SSTA_ERR_SHAPE;
+  const bool dense = kv_cnt == nullptr;
+  if (dense) {
+    if (kv_idx != nullptr || max_kept_ != 0) return SSTA_ERR_ARG;
+  } else {
+    if (max_kept_ < 0 || max_kept_ > geo.n_tiles) return SSTA_ERR_ARG;
+    SSTA_TRY(check_ptr(kv_cnt, false));
+    SSTA_TRY(check_ptr(kv_idx, max_kept_ == 0));
+  }
+  const BwdLayout lay = bwd_layout(geo);
+  if (workspace == nullptr || (int64_t)ws_bytes < lay.total) return SSTA_ERR_WORKSPACE;
+  SSTA_TRY(check_ptr(workspace, false));
+  SSTA_TRY(check_device());
+  hipStream_t st = as_stream(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  SSTA_TRY(hip_status(ssta::launch_tile_pool(geo, k, ws + lay.k_cols, SSTA_LAYOUT_DIM_MAJOR,
+                                             nullptr, st)));
+  SSTA_TRY(hip_status(ssta::launch_tile_pool(geo, q, ws + lay.q_cols, SSTA_LAYOUT_DIM_MAJOR,
+                                             nullptr, st)));
+  SSTA_TRY(hip_status(ssta::launch_tile_pool(geo, dout, ws + lay.d_cols, SSTA_LAYOUT_DIM_MAJOR,
+                                             nullptr, st)));
+  float* ld = reinterpret_cast<float*>(ws + lay.ld);
+  SSTA_TRY(hip_status(ssta::launch_attention_bwd_prep(geo, o, dout, lse, ld, st)));
+  int32_t* q_idx = reinterpret_cast<int32_t*>(ws + lay.q_idx);
+  int32_t* q_cnt = reinterpret_cast<int32_t*>(ws + lay.q_cnt);
+  if (!dense)
+    SSTA_TRY(hip_status(ssta::launch_transpose_lists(
+        geo, kv_idx, kv_cnt, max_kept_, reinterpret_cast<uint32_t*>(ws + lay.mask), q_idx,
+        q_cnt, st)));
+  ssta::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.k_cols = ws + lay.k_cols;
+  a.q_cols = ws + lay.q_cols;
+  a.dout_cols = ws + lay.d_cols;
+  a.ld = ld;
+  a.kv_idx = kv_idx;
+  a.kv_cnt = kv_cnt;
+  a.max_kept = max_kept_;
+  a.q_idx = dense ? nullptr : q_idx;
+  a.q_cnt = dense ? nullptr : q_cnt;
+  a.q_width = (int32_t)geo.n_tiles;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.scale = p->scale;
+  a.scale_log2 = p->scale * 1.44269504088896340736f;
+  return hip_status(ssta::launch_attention_bwd(geo, a, st));
+}
+
 int ssta_calibrate_mfma(const void* operands, float* sink, int32_t grid, int32_t iters,
                         void* stream) {
   if (grid <= 0 || iters <= 0 || operands == nullptr || sink == nullptr) return SSTA_ERR_ARG;

@@ -93,6 +93,34 @@ struct AttnArgs {
 };
 hipError_t launch_attention(const Geo& g, const AttnArgs& a, hipStream_t s);
 
+// Backward of the block-sparse attention (kept lists held fixed).
+struct BwdArgs {
+  const void* q;          // token-major bf16 [bh][N][128]
+  const void* k;
+  const void* v;
+  const void* dout;
+  const void* k_cols;     // dim-major tiles bf16 [bh][n][128 ch][128 tok]
+  const void* q_cols;
+  const void* dout_cols;
+  const float* ld;        // [bh][n][128][2]: (lse * log2(e), D = dO . O) per query
+  const int32_t* kv_idx;  // query block -> kept key blocks (NULL: dense)
+  const int32_t* kv_cnt;
+  int32_t max_kept;
+  const int32_t* q_idx;   // key block -> query blocks that keep it, ascending (NULL: dense)
+  const int32_t* q_cnt;
+  int32_t q_width;
+  void* dq;               // token-major bf16 outputs
+  void* dk;
+  void* dv;
+  float scale, scale_log2;
+};
+hipError_t launch_attention_bwd_prep(const Geo& g, const void* o, const void* dout,
+                                     const float* lse, float* ld, hipStream_t s);
+hipError_t launch_transpose_lists(const Geo& g, const int32_t* kv_idx, const int32_t* kv_cnt,
+                                  int32_t max_kept, uint32_t* mask_t, int32_t* q_idx,
+                                  int32_t* q_cnt, hipStream_t s);
+hipError_t launch_attention_bwd(const Geo& g, const BwdArgs& a, hipStream_t s);
+
 // Sustained matrix-core rate (measurement aid; see k_calib.hip).
 hipError_t launch_calibrate_mfma(const void* operands, float* sink, int grid, int iters,
                                  hipStream_t s);
