@@ -19,6 +19,9 @@ synchronisations.  Prints one JSON line.
                mean launch time vs the dense bf16 MFMA peak of 2.5 PFLOP/s;
                traffic = HBM bytes per launch from rocprofv3 counters, if they
                were taken on this version of the kernel
+  backward     the attention backward (dq, dk, dv) on the same kept lists:
+               time, algorithmic TFLOP/s (5 products per kept pair) and
+               executed TFLOP/s (8: S is recomputed in all three kernels)
   mfma_sustained  the chip's sustained bf16 matrix-core rate on random and on
                constant operands (ssta_calibrate_mfma): under random data the
                power limit holds the clock well below its peak
@@ -56,6 +59,8 @@ def parse():
     ap.add_argument("--cold-steps", type=int, default=3,
                     help="extra steps, each after overwriting a 512 MB buffer (cold caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward-steps", type=int, default=3,
+                    help="timed runs of the attention backward (dq, dk, dv) after the forward")
     ap.add_argument("--no-mfma-ceiling", action="store_true",
                     help="skip the sustained bf16 matrix-core rate measurement")
     ap.add_argument("--materialised", action="store_true",
@@ -118,6 +123,45 @@ def cpu_baseline(wl, q, k, v, rows_wanted):
                    "attention of %d of %d query blocks (%d kept pairs, %.1f s)"
                    % (wl.name, t_sel, len(rows), n, pairs, t_att)),
     }
+
+
+def backward_bench(torch, m, si, wl, plan, g, p, qd, kd, vd, pairs, steps):
+    """The attention backward (dq, dk, dv for a seeded synthetic dO, kept lists
+    of the timed forward) timed with HIP events on the launch stream."""
+    import numpy as np
+    do = si.generate(wl, 3)
+    dod = torch.from_numpy(do.view(np.int16)).view(torch.bfloat16).cuda()
+    plan.run(qd, kd, vd)
+    dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
+    ws = torch.empty(m.ssta_attention_bwd_workspace_bytes(g), dtype=torch.uint8, device="cuda")
+
+    def run():
+        m.ssta_attention_bwd(g, p, qd, kd, vd, plan.o, dod, plan.lse, plan.kv_idx, plan.kv_cnt,
+                             dq, dk, dv, ws)
+
+    run()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    # five 128^3 products per kept pair (S, dP, dQ, dK, dV); the kernels also
+    # recompute S twice and dP once more
+    alg = pairs * 5 * 2 * 128 ** 3
+    exe = pairs * 8 * 2 * 128 ** 3
+    mean = float(ms.mean())
+    return {"ms": {"mean": round(mean, 4), "median": round(float(np.median(ms)), 4),
+                   "min": round(float(ms.min()), 4), "max": round(float(ms.max()), 4)},
+            "steps": steps,
+            "algorithmic_flop": alg, "executed_flop": exe,
+            "algorithmic_tflops": round(alg / (mean * 1e-3) / 1e12, 2),
+            "executed_tflops": round(exe / (mean * 1e-3) / 1e12, 2),
+            "pct_bf16_peak_executed": round(100 * exe / (mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "dout": "seeded synthetic, same field + noise recipe as Q/K/V"}
 
 
 def mfma_ceiling(torch, m, iters=160000, reps=3):
@@ -267,6 +311,14 @@ def main():
         print("[bench] dense step %.1f ms, attention %.1f ms" % (dense_ms, dense_attn_ms),
               file=sys.stderr, flush=True)
 
+    backward = None
+    if args.backward_steps > 0:
+        backward = backward_bench(torch, m, si, wl, plan, g, p, qd, kd, vd, pairs,
+                                  args.backward_steps)
+        print("[bench] backward %.3f ms (%.1f algorithmic TFLOP/s)"
+              % (backward["ms"]["mean"], backward["algorithmic_tflops"]), file=sys.stderr,
+              flush=True)
+
     ceiling = None if args.no_mfma_ceiling else mfma_ceiling(torch, m)
     if ceiling is not None:
         print("[bench] sustained bf16 MFMA: %.0f TFLOP/s random operands, %.0f constant"
@@ -360,6 +412,7 @@ def main():
                                        else round(dense_attn_ms / phase_ms["attention"], 3)),
         "roofline": roof,
         "mfma_sustained": ceiling,
+        "backward": backward,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
