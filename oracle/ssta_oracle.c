@@ -52,11 +52,13 @@ static float bf16_to_f32(uint16_t b) {
   return f;
 }
 
-static int64_t tiles_t(const orc_geom* g) { return g->T / g->tile_t; }
-static int64_t tiles_h(const orc_geom* g) { return g->H / g->tile_h; }
-static int64_t tiles_w(const orc_geom* g) { return g->W / g->tile_w; }
+/* Reading for grids the block size does not divide: the block grid rounds up
+ * and the blocks on the far edges hold only the tokens that exist. */
+static int64_t tiles_t(const orc_geom* g) { return (g->T + g->tile_t - 1) / g->tile_t; }
+static int64_t tiles_h(const orc_geom* g) { return (g->H + g->tile_h - 1) / g->tile_h; }
+static int64_t tiles_w(const orc_geom* g) { return (g->W + g->tile_w - 1) / g->tile_w; }
 
-/* [TR] Step 1: block count = (F/tile_t)(H/tile_h)(W/tile_w). */
+/* [TR] Step 1: block count = (F/tile_t)(H/tile_h)(W/tile_w), rounded up per axis. */
 int64_t orc_n_tiles(const orc_geom* g) { return tiles_t(g) * tiles_h(g) * tiles_w(g); }
 
 int32_t orc_tile_tokens(const orc_geom* g) { return g->tile_t * g->tile_h * g->tile_w; }
@@ -74,7 +76,8 @@ void orc_token_to_tile(const orc_geom* g, int64_t n, int64_t* tile, int32_t* r) 
   *r = (int32_t)(((t % g->tile_t) * g->tile_h + (y % g->tile_h)) * g->tile_w + (x % g->tile_w));
 }
 
-/* Inverse map: the token index of in-tile position r of tile `tile`. */
+/* Inverse map: the token index of in-tile position r of tile `tile`, or -1
+ * when that position lies beyond the grid (an edge block of a ragged grid). */
 int64_t orc_tile_to_token(const orc_geom* g, int64_t tile, int32_t r) {
   const int64_t bt = tile / (tiles_h(g) * tiles_w(g));
   const int64_t by = (tile / tiles_w(g)) % tiles_h(g);
@@ -83,13 +86,16 @@ int64_t orc_tile_to_token(const orc_geom* g, int64_t tile, int32_t r) {
   const int64_t iy = (r / g->tile_w) % g->tile_h;
   const int64_t ix = r % g->tile_w;
   const int64_t t = bt * g->tile_t + it, y = by * g->tile_h + iy, x = bx * g->tile_w + ix;
+  if (t >= g->T || y >= g->H || x >= g->W) return -1;
   return (t * g->H + y) * g->W + x;
 }
 
-/* Gather x[b,h,N,D] (bf16 bits) into tile-major x_t[b,h,n_tiles,tile_tokens,D]. */
+/* Gather x[b,h,N,D] (bf16 bits) into tile-major x_t[b,h,n_tiles,tile_tokens,D];
+ * positions beyond a ragged grid are zero. */
 void orc_permute(const orc_geom* g, const uint16_t* x, uint16_t* x_t) {
   const int64_t N = (int64_t)g->T * g->H * g->W, D = g->head_dim;
   const int64_t BH = (int64_t)g->batch * g->heads;
+  memset(x_t, 0, sizeof(uint16_t) * (size_t)(BH * orc_n_tiles(g) * orc_tile_tokens(g) * D));
   for (int64_t bh = 0; bh < BH; ++bh)
     for (int64_t n = 0; n < N; ++n) {
       int64_t tile;
@@ -102,8 +108,10 @@ void orc_permute(const orc_geom* g, const uint16_t* x, uint16_t* x_t) {
 
 /*
  * [TR] Step 2: pooled (average) block representation.
- * pooled[b,h,i,d] = (sum over r = 0..tile_tokens-1, ascending, in fp32, of
- * x[token(i, r), d]) / tile_tokens.
+ * pooled[b,h,i,d] = (sum over the block's existing positions r, ascending, in
+ * fp32, of x[token(i, r), d]) / (number of those positions): every position
+ * of an interior block, the positions inside the grid for an edge block of a
+ * ragged grid.
  */
 void orc_pool(const orc_geom* g, const uint16_t* x, float* pooled) {
   const int64_t N = (int64_t)g->T * g->H * g->W, D = g->head_dim;
@@ -113,12 +121,16 @@ void orc_pool(const orc_geom* g, const uint16_t* x, float* pooled) {
   for (int64_t bhi = 0; bhi < BH * NT; ++bhi) {
     const int64_t bh = bhi / NT, i = bhi % NT;
     float s[1024];
+    int32_t count = 0;
     for (int64_t d = 0; d < D; ++d) s[d] = 0.0f;
     for (int32_t r = 0; r < R; ++r) {
-      const uint16_t* row = x + (bh * N + orc_tile_to_token(g, i, r)) * D;
+      const int64_t tok = orc_tile_to_token(g, i, r);
+      if (tok < 0) continue;
+      ++count;
+      const uint16_t* row = x + (bh * N + tok) * D;
       for (int64_t d = 0; d < D; ++d) s[d] = s[d] + bf16_to_f32(row[d]);
     }
-    for (int64_t d = 0; d < D; ++d) pooled[bhi * D + d] = s[d] / (float)R;
+    for (int64_t d = 0; d < D; ++d) pooled[bhi * D + d] = s[d] / (float)count;
   }
 }
 
@@ -359,16 +371,17 @@ void orc_attention(const orc_geom* g, double scale, const uint16_t* q, const uin
       int64_t m = 0;
       for (int32_t c = 0; c < cnt; ++c) {
         const int32_t j = kv_idx[row * max_kept + c];
-        for (int32_t rr = 0; rr < R; ++rr) keys[m++] = orc_tile_to_token(g, j, rr);
+        for (int32_t rr = 0; rr < R; ++rr) {
+          const int64_t tok = orc_tile_to_token(g, j, rr);
+          if (tok >= 0) keys[m++] = tok;
+        }
       }
       for (int32_t r = 0; r < R; ++r) {
         const int64_t nq = orc_tile_to_token(g, i, r);
         double* o = o_out + (a * R + r) * D;
-        for (int64_t d = 0; d < D; ++d) {
-          qv[d] = (double)bf16_to_f32(q[(bh * N + nq) * D + d]);
-          o[d] = 0.0;
-        }
-        if (m == 0) { lse_out[a * R + r] = -INFINITY; continue; }
+        for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+        if (m == 0 || nq < 0) { lse_out[a * R + r] = -INFINITY; continue; }
+        for (int64_t d = 0; d < D; ++d) qv[d] = (double)bf16_to_f32(q[(bh * N + nq) * D + d]);
         double mx = -INFINITY;
         for (int64_t t = 0; t < m; ++t) {
           const uint16_t* kr = k + (bh * N + keys[t]) * D;
@@ -462,13 +475,20 @@ static void bwd_ds(const orc_geom* g, int64_t bh, const uint16_t* v, const int64
   }
 }
 
+/* The existing key tokens of a row's kept blocks; slot[t] = c * R + rr (list
+ * position c, in-block position rr) of keys[t]. */
 static int64_t kept_keys(const orc_geom* g, int64_t row, const int32_t* kv_idx,
-                         const int32_t* kv_cnt, int32_t max_kept, int64_t* keys) {
+                         const int32_t* kv_cnt, int32_t max_kept, int64_t* keys, int64_t* slot) {
   const int32_t R = orc_tile_tokens(g);
   int64_t m = 0;
   for (int32_t c = 0; c < kv_cnt[row]; ++c) {
     const int32_t j = kv_idx[row * max_kept + c];
-    for (int32_t rr = 0; rr < R; ++rr) keys[m++] = orc_tile_to_token(g, j, rr);
+    for (int32_t rr = 0; rr < R; ++rr) {
+      const int64_t tok = orc_tile_to_token(g, j, rr);
+      if (tok < 0) continue;
+      slot[m] = (int64_t)c * R + rr;
+      keys[m++] = tok;
+    }
   }
   return m;
 }
@@ -485,6 +505,7 @@ void orc_attention_bwd(const orc_geom* g, double scale, const uint16_t* q, const
   {
     double* p = (double*)malloc(sizeof(double) * cap);
     int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * cap);
+    int64_t* slot = (int64_t*)malloc(sizeof(int64_t) * cap);
     double* qv = (double*)malloc(sizeof(double) * (size_t)D);
     double* dov = (double*)malloc(sizeof(double) * (size_t)D);
     double* o = (double*)malloc(sizeof(double) * (size_t)D);
@@ -492,14 +513,14 @@ void orc_attention_bwd(const orc_geom* g, double scale, const uint16_t* q, const
 #pragma omp for schedule(dynamic, 1)
     for (int64_t a = 0; a < n_qrows; ++a) {
       const int64_t row = q_rows[a], bh = row / n, i = row % n;
-      const int64_t m = kept_keys(g, row, kv_idx, kv_cnt, max_kept, keys);
+      const int64_t m = kept_keys(g, row, kv_idx, kv_cnt, max_kept, keys, slot);
       for (int32_t r = 0; r < R; ++r) {
         double* dq = dq_out + (a * R + r) * D;
         for (int64_t d = 0; d < D; ++d) dq[d] = 0.0;
-        if (m == 0) continue;
+        const int64_t nq = orc_tile_to_token(g, i, r);
+        if (m == 0 || nq < 0) continue;
         double da;
-        bwd_row(g, scale, bh, orc_tile_to_token(g, i, r), q, k, v, dout, keys, m, qv, dov, p,
-                o, &da);
+        bwd_row(g, scale, bh, nq, q, k, v, dout, keys, m, qv, dov, p, o, &da);
         bwd_ds(g, bh, v, keys, m, dov, da, p);
         for (int64_t t = 0; t < m; ++t) {
           const uint16_t* kr = k + (bh * N + keys[t]) * D;
@@ -521,26 +542,30 @@ void orc_attention_bwd(const orc_geom* g, double scale, const uint16_t* q, const
         for (int32_t c = 0; c < kv_cnt[row]; ++c)
           if (kv_idx[row * max_kept + c] == j) pos = c;
         if (pos < 0) continue;
-        const int64_t m = kept_keys(g, row, kv_idx, kv_cnt, max_kept, keys);
+        const int64_t m = kept_keys(g, row, kv_idx, kv_cnt, max_kept, keys, slot);
         for (int32_t r = 0; r < R; ++r) {
+          const int64_t nq = orc_tile_to_token(g, i, r);
+          if (nq < 0) continue;
           double da;
-          bwd_row(g, scale, bh, orc_tile_to_token(g, i, r), q, k, v, dout, keys, m, qv, dov,
-                  p, o, &da);
+          bwd_row(g, scale, bh, nq, q, k, v, dout, keys, m, qv, dov, p, o, &da);
           /* keep p for dv before it becomes dS */
-          for (int32_t rr = 0; rr < R; ++rr) {
-            const double pb = p[(int64_t)pos * R + rr];
-            for (int64_t d = 0; d < D; ++d) dv[rr * D + d] += pb * dov[d];
+          for (int64_t t = 0; t < m; ++t) {
+            if (slot[t] / R != pos) continue;
+            const int64_t rr = slot[t] % R;
+            for (int64_t d = 0; d < D; ++d) dv[rr * D + d] += p[t] * dov[d];
           }
           bwd_ds(g, bh, v, keys, m, dov, da, p);
-          for (int32_t rr = 0; rr < R; ++rr) {
-            const double ds = p[(int64_t)pos * R + rr];
-            for (int64_t d = 0; d < D; ++d) dk[rr * D + d] += scale * ds * qv[d];
+          for (int64_t t = 0; t < m; ++t) {
+            if (slot[t] / R != pos) continue;
+            const int64_t rr = slot[t] % R;
+            for (int64_t d = 0; d < D; ++d) dk[rr * D + d] += scale * p[t] * qv[d];
           }
         }
       }
     }
     free(p);
     free(keys);
+    free(slot);
     free(qv);
     free(dov);
     free(o);

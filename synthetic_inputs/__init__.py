@@ -91,7 +91,8 @@ class Workload:
 
     @property
     def tile_grid(self) -> tuple:
-        return (self.T // self.tile[0], self.H // self.tile[1], self.W // self.tile[2])
+        """Blocks per axis, rounded up: edge blocks of a ragged grid are partial."""
+        return tuple(-(-n // t) for n, t in zip((self.T, self.H, self.W), self.tile))
 
     @property
     def n_tiles(self) -> int:
@@ -124,9 +125,19 @@ EXTRA = {
                          dup_tiles=((5, 0), (5, 9), (5, 17), (5, 30), (12, 3), (12, 21))),
     "ragged": Workload("ragged", 2, 3, 6, 24, 40, win=(1, 0, 2), topk=5, seed=14),
     "wide-k": Workload("wide-k", 1, 2, 6, 24, 40, win=(1, 1, 1), topk=100, seed=15),
+    # grids the 2x8x8 block does not divide: partial edge blocks on t and y (5x20x24),
+    # and on x only (4x16x20)
+    "partial": Workload("partial", 1, 2, 5, 20, 24, win=(1, 1, 1), topk=4, seed=16),
+    "partial-x": Workload("partial-x", 2, 1, 4, 16, 20, win=(1, 0, 1), topk=3, seed=17),
 }
 
-ALL = {**CONFIGS, **EXTRA}
+# The real latent grid of a 10 s 720p clip (61 latent frames from 241 frames; 720/16 = 45
+# rows): ragged in t and y for the 2x8x8 block.
+LATENT = {
+    "720p-10s-latent": Workload("720p-10s-latent", 1, 16, 61, 45, 80, topk=48, seed=5),
+}
+
+ALL = {**CONFIGS, **EXTRA, **LATENT}
 
 
 def _copy_tiles(x: np.ndarray, wl: Workload) -> None:

@@ -70,17 +70,21 @@ def compare_o(o_gpu_rows: np.ndarray, o_ref: np.ndarray):
 
 
 def token_rows(wl, rows):
-    """[len(rows), 128] token indices of the query rows (b*heads+h)*n_tiles + i, in in-block order."""
+    """[len(rows), 128] token indices of the query rows (b*heads+h)*n_tiles + i, in in-block
+    order (-1 where a ragged grid has no token)."""
     n = wl.n_tiles
     return np.array([[oracle.tile_to_token(wl, int(r) % n, t) for t in range(128)] for r in rows])
 
 
 def o_rows(wl, o_tok: torch.Tensor, rows) -> np.ndarray:
-    """fp32 O rows [len(rows), 128, 128] gathered from a token-major output."""
+    """fp32 O rows [len(rows), 128, 128] gathered from a token-major output;
+    positions beyond a ragged grid (no token) read as zero."""
     o = o_tok.float().cpu().numpy().reshape(wl.batch * wl.heads, wl.n_tokens, 128)
     tok = token_rows(wl, rows)
     bh = np.asarray(rows) // wl.n_tiles
-    return o[bh[:, None], tok]
+    out = o[bh[:, None], np.maximum(tok, 0)]
+    out[tok < 0] = 0.0
+    return out
 
 
 def lse_bound(wl, q, k, rows) -> np.ndarray:

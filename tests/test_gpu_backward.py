@@ -24,7 +24,9 @@ def _rows_of(wl, t, rows):
     x = t.float().cpu().numpy().reshape(wl.batch * wl.heads, wl.n_tokens, 128)
     tok = token_rows(wl, rows)
     bh = np.asarray(rows) // wl.n_tiles
-    return x[bh[:, None], tok].astype(np.float64)
+    out = x[bh[:, None], np.maximum(tok, 0)].astype(np.float64)
+    out[tok < 0] = 0.0
+    return out
 
 
 def _check(name, got, ref):
