@@ -25,8 +25,13 @@
  *     are numbered row-major over the (T/tile_t, H/tile_h, W/tile_w) block
  *     grid, and the tokens of one block row-major over (tile_t, tile_h,
  *     tile_w).  n_tiles = (T/tile_t)(H/tile_h)(W/tile_w)  (Step 1).
- *   - Current limits: head_dim == 128, tile_t*tile_h*tile_w == 128 tokens,
- *     tile sizes divide T, H, W; ssta_score_select needs n_tiles <= 4096;
+ *   - Grids the block size does not divide are allowed: the block grid rounds
+ *     up per axis and the blocks on the far edges hold only the tokens that
+ *     exist (block means average those; attention runs over them; positions
+ *     without a token are zero in tile-major copies and outputs and have LSE
+ *     -inf).
+ *   - Current limits: head_dim == 128, tile_t*tile_h*tile_w == 128 tokens;
+ *     ssta_score_select needs n_tiles <= 4096;
  *     the attention entry points need n_tiles < 65536 (one head's blocks are
  *     addressed with 32-bit offsets).
  */
@@ -55,7 +60,7 @@ typedef enum ssta_status {
 typedef struct ssta_geom {
   int32_t batch, heads, head_dim;   /* head_dim must be 128 */
   int32_t T, H, W;                  /* latent grid, tokens row-major (t, y, x) */
-  int32_t tile_t, tile_h, tile_w;   /* block size; divides the grid; product 128 */
+  int32_t tile_t, tile_h, tile_w;   /* block size; product 128 (so powers of two) */
 } ssta_geom_t;
 
 /* Selection and attention parameters. */
@@ -90,8 +95,9 @@ typedef struct ssta_params {
  *   x_tiled out: bf16, the same values gathered block by block in `layout`
  *                (SSTA_LAYOUT_*); NULL to skip.
  *   pooled  out: fp32 [batch, heads, n_tiles, head_dim], the mean of each
- *                block's tokens: the fp32 sum over in-block tokens in
- *                ascending order divided by the token count; NULL to skip.
+ *                block's tokens: the fp32 sum over the block's existing tokens
+ *                in ascending in-block order divided by their count; NULL to skip.
+ * Positions an edge block of a ragged grid lacks are zero in x_tiled.
  * At least one of x_tiled and pooled must be non-NULL.
  */
 int ssta_tile_pool(const ssta_geom_t* g, const void* x, void* x_tiled, int32_t layout,

@@ -52,7 +52,8 @@ def _run(wl, q, k, v, do, flags=0, dense=False):
     return plan, dq, dk, dv
 
 
-@pytest.mark.parametrize("name", ["tiny", "grid32-w1-k2", "ragged", "dup-ties"])
+@pytest.mark.parametrize("name", ["tiny", "grid32-w1-k2", "ragged", "dup-ties", "partial",
+                                  "partial-x"])
 def test_backward_vs_oracle(name):
     wl = si.ALL[name]
     q, k, v = si.make_qkv(wl)
@@ -87,18 +88,19 @@ def test_backward_empty_rows():
     assert not dq.any() and not dk.any() and not dv.any()
 
 
-def test_backward_full_size_sampled():
-    wl = si.CONFIGS["720p-10s"]
+@pytest.mark.parametrize("name", ["720p-10s", "720p-10s-latent"])
+def test_backward_full_size_sampled(name):
+    wl = si.ALL[name]
     q, k, v = si.make_qkv(wl)
     do = si.generate(wl, 3)
-    print("[720p-10s] inputs ready", flush=True)
+    print("[%s] inputs ready" % name, flush=True)
     plan, dq, dk, dv = _run(wl, q, k, v, do)
-    print("[720p-10s] gpu done", flush=True)
+    print("[%s] gpu done" % name, flush=True)
     kv_idx, kv_cnt = plan.kv_idx.cpu().numpy(), plan.kv_cnt.cpu().numpy()
     rows = sample_rows(wl, 2, seed=5)[:10]
     krows = rows[:4]
     rq, rk, rv = oracle.attention_bwd(wl, q, k, v, do, kv_idx, kv_cnt, rows, krows)
-    print("[720p-10s] oracle done", flush=True)
+    print("[%s] oracle done" % name, flush=True)
     _check("dq", _rows_of(wl, dq, rows), rq)
     _check("dk", _rows_of(wl, dk, krows), rk)
     _check("dv", _rows_of(wl, dv, krows), rv)

@@ -42,7 +42,8 @@ class SstaGeom(ctypes.Structure):
 
     @property
     def n_tiles(self) -> int:
-        return (self.T // self.tile_t) * (self.H // self.tile_h) * (self.W // self.tile_w)
+        """Blocks per (batch, head); each axis rounds up (ragged grids have partial edge blocks)."""
+        return (-(-self.T // self.tile_t)) * (-(-self.H // self.tile_h)) * (-(-self.W // self.tile_w))
 
     @property
     def tile_tokens(self) -> int:

@@ -162,16 +162,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint8_t* base,
 // Token-major: the rows of the block's tokens; in-block positions are a
 // bit-field code of (t, y, x) offsets, so position 64p + r lies at token
 // offset in_block_offset(64p) + in_block_offset(r) from the block's origin.
-template <bool kTokK>
+// On a ragged grid, bit r of `valid` says whether position 64p + r of the
+// block exists; a token-major gather redirects the rows that do not to the
+// block's first token (their scores are masked later).
+template <bool kTokK, bool kRagged>
 __device__ __forceinline__ void dma_k(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, const Geo& g,
-                                      int64_t j, int p, int wave, const DmaOffsets& off) {
+                                      int64_t j, int p, int wave, int lane, uint64_t valid,
+                                      const DmaOffsets& off) {
   const uint32_t so =
       kTokK ? (block_origin32(g, (uint32_t)j) + (p ? in_block_offset(g, 64) : 0u)) * 256u
             : (uint32_t)(j * kTileBytes + p * kSlotBytes);
 #pragma unroll
-  for (int mm = 0; mm < 4; ++mm)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (4 * wave + mm) * 1024), 16,
-                                             off.k[mm], so, 0, 0);
+  for (int mm = 0; mm < 4; ++mm) {
+    uint32_t vo = off.k[mm];
+    if (kRagged && kTokK && valid != ~0ull &&
+        !((valid >> (16 * wave + 4 * mm + (lane >> 4))) & 1u))
+      vo &= 255u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (4 * wave + mm) * 1024), 16, vo,
+                                             so, 0, 0);
+  }
+}
+
+// Which of positions 64p .. 64p+63 of block j exist (all, off a ragged grid).
+template <bool kRagged>
+__device__ __forceinline__ uint64_t unit_valid(const Geo& g, int64_t j, int p, int lane) {
+  if (!kRagged) return ~0ull;
+  const BlockExtent e = block_extent(g, (uint32_t)j);
+  if (e.full) return ~0ull;
+  return __ballot(pos_exists(g, e, 64 * p + lane));
 }
 // Half p of V^T block j: bytes 128p .. 128p+127 of each 256-byte channel row.
 __device__ __forceinline__ void dma_v(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, int64_t j, int p,
@@ -207,7 +225,7 @@ __device__ __forceinline__ void scores(f32x16 (&s)[2], const uint8_t* sK, const 
 // scattered directly); otherwise Q, K and O are tile-major
 // [B, h, n_tiles, 128, 128].  V is always dim-major tiles: the P.V product
 // needs 8 consecutive keys of one channel per lane.
-template <bool kTok>
+template <bool kTok, bool kRagged>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   // K slots at 0 and 16 KB, V^T slots at 32 and 48 KB.
@@ -227,15 +245,21 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   constexpr int64_t kTileElems = kTileTokens * kHeadDim;
 
-  // qb: this lane's query row is qb + (kTok ? 0 : qrow * 128).
+  // qb: this lane's query row is qb + (kTok ? 0 : qrow * 128).  A query
+  // position an edge block of a ragged grid lacks reads the block's first
+  // token instead (its output is not written).
+  const int qrow = wave * 32 + l32;
+  const bool qvalid =
+      (unit_valid<kRagged>(g, qi, wave >> 1, lane) >> (32 * (wave & 1) + l32)) & 1u;
   const uint16_t* qb = static_cast<const uint16_t*>(a.q_t) + row * kTileElems;
   if (kTok) {
     // bh * N tokens precede this head; each lane reads its own query row.
     const uint16_t* qhead = static_cast<const uint16_t*>(a.q_t) + bh * g.N * kHeadDim;
-    qb = qhead + (block_origin(g, qi) + in_block_offset(g, wave * 32 + (lane & 31))) * kHeadDim;
+    qb = qhead + (block_origin(g, qi) + (qvalid ? in_block_offset(g, qrow) : 0u)) * kHeadDim;
   }
-  const uint8_t* kb = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(a.k_t) +
-                                                       bh * g.n_tiles * kTileElems);   // = bh * N * 128
+  // K: token-major (N rows per head) or tile-major (n_tiles blocks per head)
+  const uint8_t* kb = reinterpret_cast<const uint8_t*>(
+      static_cast<const uint16_t*>(a.k_t) + bh * (kTok ? g.N * kHeadDim : g.n_tiles * kTileElems));
   const uint8_t* vb = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(a.v_t) +
                                                        bh * g.n_tiles * kTileElems);
   const bool dense = a.kv_cnt == nullptr;
@@ -243,7 +267,6 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   const int32_t* idx = dense ? nullptr : a.kv_idx + row * a.max_kept;
 
   // B operand of S^T = K Q^T: query (32*wave + l32), channels 16*s + 8*hl .. +8.
-  const int qrow = wave * 32 + l32;
   bf16x8 qf[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s)
@@ -263,7 +286,12 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   // K and V^T rings; unit u+1 is loaded while unit u is computed.
   const int units = 2 * cnt;
   const DmaOffsets doff = dma_offsets<kTok>(g, wv, lane);
-  const __amdgpu_buffer_rsrc_t krs = head_rsrc(kb, g.n_tiles), vrs = head_rsrc(vb, g.n_tiles);
+  // token-major K spans N rows of 256 B; tiles span n_tiles x 32 KB
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kb), (short)0,
+                                        (int)(kTok ? g.N * 256 : g.n_tiles * kTileBytes),
+                                        0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(vb, g.n_tiles);
   // Kept-block ids, 64 at a time: lane i holds entry ibase + i.
   int ibase = 0;
   int ids = (!dense && lane < cnt) ? idx[lane] : 0;
@@ -275,19 +303,24 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
     }
     return __builtin_amdgcn_readlane(ids, pos - ibase);
   };
+  uint64_t valid_next = ~0ull;   // positions of the unit loaded last that exist
   if (units > 0) {
-    const int64_t j0 = block_at(0);
-    dma_k<kTok>(smem, krs, g, j0, 0, wv, doff);
-    dma_v(smem + 2 * kSlotBytes, vrs, j0, 0, wv, doff);
+    const int64_t j = block_at(0);
+    valid_next = unit_valid<kRagged>(g, j, 0, lane);
+    dma_k<kTok, kRagged>(smem, krs, g, j, 0, wv, lane, valid_next, doff);
+    dma_v(smem + 2 * kSlotBytes, vrs, j, 0, wv, doff);
   }
 
   for (int u = 0; u < units; ++u) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's loads of unit u have landed
     __syncthreads();                        // ... every wave's; and unit u-1 is done
     const int slot = u & 1;
+    const uint64_t valid = valid_next;
     if (u + 1 < units) {
       const int64_t j = block_at((u + 1) >> 1);
-      dma_k<kTok>(smem + (1 - slot) * kSlotBytes, krs, g, j, (u + 1) & 1, wv, doff);
+      valid_next = unit_valid<kRagged>(g, j, (u + 1) & 1, lane);
+      dma_k<kTok, kRagged>(smem + (1 - slot) * kSlotBytes, krs, g, j, (u + 1) & 1, wv, lane, valid_next,
+                  doff);
       dma_v(smem + (3 - slot) * kSlotBytes, vrs, j, (u + 1) & 1, wv, doff);
     }
     const uint8_t* sK = smem + slot * kSlotBytes;
@@ -315,6 +348,17 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
         kr[i % kKAhead] =
             *reinterpret_cast<const bf16x8*>(sK + swz_k(32 * (n & 1) + kperm, 2 * (n >> 1) + hl));
       __builtin_amdgcn_sched_barrier(0);
+    }
+    // Keys an edge block of a ragged grid lacks get a score far below any
+    // real one, so their probabilities vanish (position 0 always exists, so
+    // a row's first unit has a real key).
+    if (kRagged && valid != ~0ull) {
+      const uint64_t vl = valid >> (8 * hl);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!((vl >> (32 * t + 16 * (r >> 3) + (r & 7))) & 1u)) s[t][r] = -1.0e30f;
     }
 
     // V^T operands of the first kVAhead P.V products (order (t, ks, db)),
@@ -396,23 +440,29 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   }
 
   // Epilogue: lane holds query qrow, channels 32*db + 8*g4 + 4*hl + (0..3).
+  // A query position a ragged grid lacks has no output row (token order) or a
+  // zero row (tile order), and LSE -inf.
   const float lt = pair_sum(l);
-  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  const float inv = (lt > 0.0f && qvalid) ? 1.0f / lt : 0.0f;
   uint16_t* ob = static_cast<uint16_t*>(a.o_t) + row * kTileElems + qrow * kHeadDim;
   if (kTok)
     ob = static_cast<uint16_t*>(a.o_t) +
          (bh * g.N + block_origin(g, qi) + in_block_offset(g, qrow)) * kHeadDim;
+  if (!kTok || qvalid) {
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      bf16x4 w;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * g4 + e] * inv);
-      *reinterpret_cast<bf16x4*>(ob + 32 * db + 8 * g4 + 4 * hl) = w;
-    }
+        for (int e = 0; e < 4; ++e)
+          w[e] = (!kRagged || qvalid) ? (__bf16)(o[db][4 * g4 + e] * inv) : (__bf16)0.0f;
+        *reinterpret_cast<bf16x4*>(ob + 32 * db + 8 * g4 + 4 * hl) = w;
+      }
+  }
   if (a.lse != nullptr && hl == 0) {
-    const float v = lt > 0.0f ? (m + __log2f(lt)) * 0.69314718055994530942f : -INFINITY;
+    const float v =
+        (lt > 0.0f && qvalid) ? (m + __log2f(lt)) * 0.69314718055994530942f : -INFINITY;
     a.lse[row * kTileTokens + qrow] = v;
   }
 }
@@ -422,10 +472,16 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
 hipError_t launch_attention(const Geo& g, const AttnArgs& a, hipStream_t s) {
   const int64_t slice = (g.n_tiles + 7) / 8;
   const int64_t blocks = g.bh * slice * 8;
-  if (a.token_io)
-    hipLaunchKernelGGL(k_attn_fwd<true>, dim3((unsigned)blocks), dim3(256), 0, s, g, a, slice);
+  // grids the block size divides take the variant without edge-block masking
+  const dim3 grid((unsigned)blocks), block(256);
+  if (a.token_io && g.ragged)
+    hipLaunchKernelGGL((k_attn_fwd<true, true>), grid, block, 0, s, g, a, slice);
+  else if (a.token_io)
+    hipLaunchKernelGGL((k_attn_fwd<true, false>), grid, block, 0, s, g, a, slice);
+  else if (g.ragged)
+    hipLaunchKernelGGL((k_attn_fwd<false, true>), grid, block, 0, s, g, a, slice);
   else
-    hipLaunchKernelGGL(k_attn_fwd<false>, dim3((unsigned)blocks), dim3(256), 0, s, g, a, slice);
+    hipLaunchKernelGGL((k_attn_fwd<false, false>), grid, block, 0, s, g, a, slice);
   return hipGetLastError();
 }
 

@@ -102,14 +102,32 @@ __device__ __forceinline__ UnitOffsets unit_offsets(const Geo& g, int wave, int 
   }
   return o;
 }
-// Rows 32p .. 32p+31 of block j, gathered from token-major memory.
+// Which of positions 32p .. 32p+31 of block j exist (all, off a ragged grid).
+__device__ __forceinline__ uint32_t rows_valid(const Geo& g, uint32_t j, int p, int lane) {
+  if (!g.ragged) return ~0u;
+  const BlockExtent e = block_extent(g, j);
+  if (e.full) return ~0u;
+  return (uint32_t)__ballot(pos_exists(g, e, 32 * p + (lane & 31)));
+}
+
+// Rows 32p .. 32p+31 of block j, gathered from token-major memory.  A row
+// whose position does not exist (bit clear in `valid`) is read from the
+// block's first token instead, so every score it enters stays bounded by
+// the row's log-sum-exp; its dim-major column is zero, so it adds nothing.
 __device__ __forceinline__ void dma_rows(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, const Geo& g,
-                                         uint32_t j, int p, int wave, const UnitOffsets& off) {
-  const uint32_t so = (block_origin32(g, j) + in_block_offset(g, 32 * p)) * 256u;
+                                         uint32_t j, int p, int wave, int lane, uint32_t valid,
+                                         const UnitOffsets& off) {
+  const bool part = valid != ~0u;
+  const uint32_t half = in_block_offset(g, 32 * p) * 256u;
+  const uint32_t so = block_origin32(g, j) * 256u + (part ? 0u : half);
 #pragma unroll
-  for (int mm = 0; mm < 2; ++mm)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (2 * wave + mm) * 1024), 16,
-                                             off.rows[mm], so, 0, 0);
+  for (int mm = 0; mm < 2; ++mm) {
+    uint32_t vo = off.rows[mm];
+    if (part)
+      vo = ((valid >> (4 * (2 * wave + mm) + (lane >> 4))) & 1u) ? vo + half : (vo & 255u);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (2 * wave + mm) * 1024), 16, vo,
+                                             so, 0, 0);
+  }
 }
 // Columns 32p .. 32p+31 of dim-major block j.
 __device__ __forceinline__ void dma_cols(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, uint32_t j,
@@ -182,7 +200,10 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, int64_t slice) {
   const int kperm = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
   const int qrow = 32 * wv + l32;
   const int64_t head = bh * g.N;
-  const int64_t qtok = head + block_origin(g, qi) + in_block_offset(g, qrow);
+  // a query position an edge block lacks reads the block's first token and
+  // stores nothing
+  const bool qvalid = (rows_valid(g, (uint32_t)qi, wv, lane) >> l32) & 1u;
+  const int64_t qtok = head + block_origin(g, qi) + (qvalid ? in_block_offset(g, qrow) : 0u);
 
   bf16x8 qf[8], df[8];
   load_row_operand(qf, static_cast<const uint16_t*>(a.q) + qtok * kHeadDim, hl);
@@ -202,19 +223,22 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, int64_t slice) {
   IdStream ids;
   ids.init(dense ? nullptr : a.kv_idx + row * a.max_kept, cnt, dense, lane);
   const UnitOffsets off = unit_offsets(g, wv, lane);
+  // token-major: N rows of 256 B per head; dim-major: n_tiles blocks of 32 KB
+  const int64_t tok_bytes = g.N * (int64_t)(kHeadDim * 2);
   const int64_t head_bytes = g.n_tiles * (int64_t)kBlockBytes;
   const __amdgpu_buffer_rsrc_t krs = rsrc(static_cast<const uint16_t*>(a.k) + head * kHeadDim,
-                                          head_bytes);
+                                          tok_bytes);
   const __amdgpu_buffer_rsrc_t vrs = rsrc(static_cast<const uint16_t*>(a.v) + head * kHeadDim,
-                                          head_bytes);
+                                          tok_bytes);
   const __amdgpu_buffer_rsrc_t ktrs = rsrc(
       static_cast<const uint16_t*>(a.k_cols) + bh * g.n_tiles * (int64_t)kTileTokens * kHeadDim,
       head_bytes);
   auto load_unit = [&](int u, uint8_t* dst) {
     const uint32_t j = ids.at(u >> 2, lane);
     const int p = u & 3;
-    dma_rows(dst, krs, g, j, p, wv, off);
-    dma_rows(dst + kUnitBytes, vrs, g, j, p, wv, off);
+    const uint32_t valid = rows_valid(g, j, p, lane);
+    dma_rows(dst, krs, g, j, p, wv, lane, valid, off);
+    dma_rows(dst + kUnitBytes, vrs, g, j, p, wv, lane, valid, off);
     dma_cols(dst + 2 * kUnitBytes, ktrs, j, p, wv, off);
   };
 
@@ -261,7 +285,7 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, int64_t slice) {
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsf[ks], acc[db], 0, 0, 0);
       }
   }
-  store_row(static_cast<uint16_t*>(a.dq) + qtok * kHeadDim, acc, a.scale, hl);
+  if (qvalid) store_row(static_cast<uint16_t*>(a.dq) + qtok * kHeadDim, acc, a.scale, hl);
 }
 
 // ------------------------------------------------------------------ dV, dK
@@ -287,7 +311,10 @@ void k_attn_bwd_kv(Geo g, BwdArgs a, int64_t slice) {
   const int kperm = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
   const int kr = 32 * wv + l32;                  // this lane's key within the block
   const int64_t head = bh * g.N;
-  const int64_t ktok = head + block_origin(g, kj) + in_block_offset(g, kr);
+  // a key position an edge block lacks reads the block's first token and
+  // stores nothing
+  const bool kvalid = (rows_valid(g, (uint32_t)kj, wv, lane) >> l32) & 1u;
+  const int64_t ktok = head + block_origin(g, kj) + (kvalid ? in_block_offset(g, kr) : 0u);
 
   // B operands: the wave's 32 keys (and their values for dP).
   bf16x8 kf[8], vf[8];
@@ -306,11 +333,12 @@ void k_attn_bwd_kv(Geo g, BwdArgs a, int64_t slice) {
   IdStream ids;
   ids.init(dense ? nullptr : a.q_idx + krow * a.q_width, cnt, dense, lane);
   const UnitOffsets off = unit_offsets(g, wv, lane);
+  const int64_t tok_bytes = g.N * (int64_t)(kHeadDim * 2);
   const int64_t head_bytes = g.n_tiles * (int64_t)kBlockBytes;
   const __amdgpu_buffer_rsrc_t qrs = rsrc(static_cast<const uint16_t*>(a.q) + head * kHeadDim,
-                                          head_bytes);
+                                          tok_bytes);
   const __amdgpu_buffer_rsrc_t drs = rsrc(static_cast<const uint16_t*>(a.dout) + head * kHeadDim,
-                                          head_bytes);
+                                          tok_bytes);
   const int64_t cols_off = bh * g.n_tiles * (int64_t)kTileTokens * kHeadDim;
   const __amdgpu_buffer_rsrc_t crs =
       rsrc(static_cast<const uint16_t*>(kDK ? a.q_cols : a.dout_cols) + cols_off, head_bytes);
@@ -319,8 +347,9 @@ void k_attn_bwd_kv(Geo g, BwdArgs a, int64_t slice) {
   auto load_unit = [&](int u, uint8_t* dst) {
     const uint32_t i = ids.at(u >> 2, lane);
     const int p = u & 3;
-    dma_rows(dst, qrs, g, i, p, wv, off);
-    if (kDK) dma_rows(dst + kUnitBytes, drs, g, i, p, wv, off);
+    const uint32_t valid = rows_valid(g, i, p, lane);
+    dma_rows(dst, qrs, g, i, p, wv, lane, valid, off);
+    if (kDK) dma_rows(dst + kUnitBytes, drs, g, i, p, wv, lane, valid, off);
     dma_cols(dst + (kParts - 1) * kUnitBytes, crs, i, p, wv, off);
     if (wv == 0 && lane < 16)   // 32 (lse2, D) pairs = 256 B
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -384,20 +413,32 @@ void k_attn_bwd_kv(Geo g, BwdArgs a, int64_t slice) {
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca, bf[ks], acc[db], 0, 0, 0);
       }
   }
-  store_row(static_cast<uint16_t*>(kDK ? a.dk : a.dv) + ktok * kHeadDim, acc,
-            kDK ? a.scale : 1.0f, hl);
+  if (kvalid)
+    store_row(static_cast<uint16_t*>(kDK ? a.dk : a.dv) + ktok * kHeadDim, acc,
+              kDK ? a.scale : 1.0f, hl);
 }
 
 // ------------------------------------------------------------------ helpers
 
 // (lse * log2 e, D = dO . O) per query, tile-major like the LSE: one
 // workgroup per (batch*head, block), two threads per token (64 channels each).
+// A position an edge block of a ragged grid lacks gets the block's first
+// query's lse and D = 0: the products then read that query in its place.
 __global__ __launch_bounds__(256) void k_attn_bwd_prep(Geo g, const uint16_t* __restrict__ o,
                                                        const uint16_t* __restrict__ dout,
                                                        const float* __restrict__ lse,
                                                        float* __restrict__ ld) {
   const int64_t blk = blockIdx.x, bh = blk / g.n_tiles, tile = blk % g.n_tiles;
   const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const BlockExtent ext = block_extent(g, (uint32_t)tile);
+  if (!ext.full && !pos_exists(g, ext, r)) {
+    if (half == 0) {
+      const int64_t qi = blk * kTileTokens + r;
+      ld[qi * 2] = lse[blk * kTileTokens] * kLog2e;
+      ld[qi * 2 + 1] = 0.0f;
+    }
+    return;
+  }
   const int64_t tok = bh * g.N + tile_token(g, tile, r);
   const uint16_t* orow = o + tok * kHeadDim + 64 * half;
   const uint16_t* drow = dout + tok * kHeadDim + 64 * half;

@@ -11,7 +11,8 @@
 // dim-major copy used for V.
 //
 // HBM traffic per block and tensor: 32 KB read + 32 KB written (+512 B of
-// means); the kernel is bound by HBM bandwidth.
+// means); the kernel is bound by HBM bandwidth.  Edge blocks of a ragged grid
+// (a grid the block size does not divide) read only the tokens that exist.
 #include "ssta_internal.h"
 
 #pragma clang fp contract(off)
@@ -34,13 +35,18 @@ __global__ __launch_bounds__(256) void k_tile_pool(Geo g, const uint16_t* __rest
   const int t = threadIdx.x;
   const int ch = t & 15;                          // 16-byte chunk = 8 channels
   const uint16_t* xb = x + bh * g.N * kHeadDim;
+  // An edge block of a ragged grid lacks some positions: they read as zero
+  // and do not enter the mean.
+  const BlockExtent ext = block_extent(g, tile);
 
   u32x4 v[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
     const int r = (t >> 4) + 16 * m;
-    const int64_t tok = tile_token(g, tile, r);
+    const bool ok = ext.full || pos_exists(g, ext, r);
+    const int64_t tok = ok ? tile_token(g, tile, r) : 0;   // a real row either way
     v[m] = *reinterpret_cast<const u32x4*>(xb + tok * kHeadDim + ch * 8);
+    if (!ok) v[m] = u32x4{0u, 0u, 0u, 0u};
   }
   if (xt != nullptr && layout == 0) {
     uint16_t* ob = xt + blk * (int64_t)(kTileTokens * kHeadDim);
@@ -59,9 +65,12 @@ __global__ __launch_bounds__(256) void k_tile_pool(Geo g, const uint16_t* __rest
   }
   __syncthreads();
   if (pooled != nullptr && t < kHeadDim) {
+    // missing positions hold +0 in LDS, which leaves the running sum exact
     float s = 0.0f;
+#pragma unroll 16
     for (int r = 0; r < kTileTokens; ++r) s = s + bf16_bits_to_f32(lds[r * kHeadDim + t]);
-    pooled[blk * kHeadDim + t] = s / (float)kTileTokens;
+    const int count = ext.full ? kTileTokens : ext.lt * ext.ly * ext.lx;
+    pooled[blk * kHeadDim + t] = s / (float)count;
   }
   if (xt != nullptr && layout == 1) {
     // dim-major: thread owns channel d and 64 consecutive tokens
@@ -90,6 +99,7 @@ __global__ __launch_bounds__(256) void k_tile_unpermute(Geo g, const uint16_t* _
   const int ch = t & 15;
   const uint16_t* ib = xt + blk * (int64_t)(kTileTokens * kHeadDim);
   uint16_t* ob = x + bh * g.N * kHeadDim;
+  const BlockExtent ext = block_extent(g, tile);
   u32x4 v[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
@@ -99,7 +109,8 @@ __global__ __launch_bounds__(256) void k_tile_unpermute(Geo g, const uint16_t* _
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
     const int r = (t >> 4) + 16 * m;
-    *reinterpret_cast<u32x4*>(ob + tile_token(g, tile, r) * kHeadDim + ch * 8) = v[m];
+    if (ext.full || pos_exists(g, ext, r))
+      *reinterpret_cast<u32x4*>(ob + tile_token(g, tile, r) * kHeadDim + ch * 8) = v[m];
   }
 }
 

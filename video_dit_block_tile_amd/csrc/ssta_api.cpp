@@ -36,11 +36,14 @@ int check_geom(const ssta_geom_t* g, Geo* out) {
       g->tile_t < 1 || g->tile_h < 1 || g->tile_w < 1)
     return SSTA_ERR_ARG;
   if (g->head_dim != ssta::kHeadDim) return SSTA_ERR_SHAPE;
-  if (g->T % g->tile_t || g->H % g->tile_h || g->W % g->tile_w) return SSTA_ERR_SHAPE;
   if ((int64_t)g->tile_t * g->tile_h * g->tile_w != ssta::kTileTokens) return SSTA_ERR_SHAPE;
   const int64_t N = (int64_t)g->T * g->H * g->W;
   const int64_t bh = (int64_t)g->batch * g->heads;
-  const int64_t nt = g->T / g->tile_t, ny = g->H / g->tile_h, nx = g->W / g->tile_w;
+  // The block grid rounds up: a grid the block size does not divide has
+  // partial blocks on its far edges.
+  const int64_t nt = (g->T + g->tile_t - 1) / g->tile_t;
+  const int64_t ny = (g->H + g->tile_h - 1) / g->tile_h;
+  const int64_t nx = (g->W + g->tile_w - 1) / g->tile_w;
   const int64_t n = nt * ny * nx;
   // Every element offset must fit in int64 and every grid in 31 bits.
   if (N > (int64_t(1) << 40) / bh) return SSTA_ERR_SHAPE;
@@ -61,6 +64,7 @@ int check_geom(const ssta_geom_t* g, Geo* out) {
   out->N = N;
   out->n_tiles = n;
   out->bh = bh;
+  out->ragged = (g->T % g->tile_t || g->H % g->tile_h || g->W % g->tile_w) ? 1 : 0;
   return SSTA_OK;
 }
 

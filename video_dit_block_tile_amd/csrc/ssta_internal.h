@@ -20,6 +20,8 @@ struct Geo {
   int64_t N;                // tokens per (batch, head)
   int64_t n_tiles;          // blocks per (batch, head)
   int64_t bh;               // batch * heads
+  int32_t ragged;           // some axis is not a multiple of its block size: the blocks on
+                            // the far edges of that axis hold fewer tokens
 };
 
 // Maps a linear workgroup id so that the ids one XCD receives (the hardware
@@ -31,7 +33,32 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblocks) {
   return xcd < r ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
 }
 
-// Token index (within one batch/head) of in-block position r of block `tile`.
+// Extent of block `tile` along each axis: the block size, except at the far
+// edges of a ragged grid.
+struct BlockExtent {
+  int32_t lt, ly, lx;
+  bool full;
+};
+__device__ __forceinline__ BlockExtent block_extent(const Geo& g, uint32_t tile) {
+  // a head's block grid holds fewer than 2^28 blocks: 32-bit arithmetic
+  const uint32_t nyx = (uint32_t)g.ny * (uint32_t)g.nx;
+  const uint32_t bt = tile / nyx, rem = tile - bt * nyx;
+  const uint32_t by = rem / (uint32_t)g.nx, bx = rem - by * (uint32_t)g.nx;
+  BlockExtent e;
+  e.lt = min(g.tt, g.T - (int32_t)bt * g.tt);
+  e.ly = min(g.th, g.H - (int32_t)by * g.th);
+  e.lx = min(g.tw, g.W - (int32_t)bx * g.tw);
+  e.full = e.lt == g.tt && e.ly == g.th && e.lx == g.tw;
+  return e;
+}
+// Whether in-block position r exists (block sizes are powers of two).
+__device__ __forceinline__ bool pos_exists(const Geo& g, const BlockExtent& e, int r) {
+  const int ltw = __builtin_ctz(g.tw), lth = __builtin_ctz(g.th);
+  return (r >> (ltw + lth)) < e.lt && ((r >> ltw) & (g.th - 1)) < e.ly && (r & (g.tw - 1)) < e.lx;
+}
+
+// Token index (within one batch/head) of in-block position r of block `tile`
+// (beyond the grid for a position that does not exist: check pos_exists).
 __device__ __forceinline__ int64_t tile_token(const Geo& g, int64_t tile, int r) {
   const int64_t bt = tile / ((int64_t)g.ny * g.nx);
   const int64_t by = (tile / g.nx) % g.ny;
