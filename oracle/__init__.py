@@ -62,11 +62,13 @@ def build(force: bool = True) -> str:
 
 class _Geom(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("batch", "heads", "head_dim", "T", "H", "W", "tile_t", "tile_h", "tile_w")]
+                ("batch", "heads", "head_dim", "T", "H", "W", "tile_t", "tile_h", "tile_w",
+                 "text_len")]
 
 
 def _geom(wl) -> _Geom:
-    return _Geom(wl.batch, wl.heads, wl.head_dim, wl.T, wl.H, wl.W, *wl.tile)
+    return _Geom(wl.batch, wl.heads, wl.head_dim, wl.T, wl.H, wl.W, *wl.tile,
+                 getattr(wl, "text_len", 0))
 
 
 def _p(a: np.ndarray):
@@ -84,6 +86,7 @@ def _load():
                                        ctypes.c_float, ctypes.c_double, ctypes.c_uint32)
         sig = {
             "orc_n_tiles": (i64, [G]),
+            "orc_n_rows": (i64, [G]),
             "orc_tile_tokens": (i32, [G]),
             "orc_token_to_tile": (None, [G, i64, vp, vp]),
             "orc_tile_to_token": (i64, [G, i64, i32]),
@@ -112,6 +115,13 @@ def _load():
 def n_tiles(wl) -> int:
     """[TR] Step 1: number of 3D blocks."""
     return int(_load().orc_n_tiles(ctypes.byref(_geom(wl))))
+
+
+def n_rows(wl) -> int:
+    """Blocks per (batch, head) of a joint sequence: the clip's n_tiles, then
+    ceil(text_len / tile_tokens) text blocks ([BLOG] "Architecture: From Prompt
+    to Video": single-stream blocks concatenate text and video tokens)."""
+    return int(_load().orc_n_rows(ctypes.byref(_geom(wl))))
 
 
 def tile_tokens(wl) -> int:
@@ -159,15 +169,17 @@ def max_kept(wl, topk=None, flags: int = 0) -> int:
 # ---------------------------------------------------------------- steps
 
 def permute(wl, x: np.ndarray) -> np.ndarray:
-    """Token-major [B,h,N,D] -> tile-major [B,h,n_tiles,tile_tokens,D] (bf16 bits)."""
+    """Token-major [B,h,S,D] -> tile-major [B,h,n_rows,tile_tokens,D] (bf16 bits):
+    the clip's blocks, then the text's (S = N + text_len; n_rows = n_tiles without text)."""
     x = np.ascontiguousarray(x, dtype=np.uint16)
-    out = np.empty((wl.batch, wl.heads, n_tiles(wl), tile_tokens(wl), wl.head_dim), np.uint16)
+    out = np.empty((wl.batch, wl.heads, n_rows(wl), tile_tokens(wl), wl.head_dim), np.uint16)
     _load().orc_permute(ctypes.byref(_geom(wl)), _p(x), _p(out))
     return out
 
 
 def pool(wl, x: np.ndarray) -> np.ndarray:
-    """[TR] Step 2: fp32 block means [B,h,n_tiles,D] of token-major bf16 bits."""
+    """[TR] Step 2: fp32 block means [B,h,n_tiles,D] of token-major bf16 bits
+    (clip blocks only: [BLOG] text masking keeps the text out of scoring)."""
     x = np.ascontiguousarray(x, dtype=np.uint16)
     out = np.empty((wl.batch, wl.heads, n_tiles(wl), wl.head_dim), np.float32)
     _load().orc_pool(ctypes.byref(_geom(wl)), _p(x), _p(out))
@@ -244,11 +256,13 @@ def default_scale(wl) -> float:
 def attention(wl, q, k, v, kv_idx, kv_cnt, rows=None, scale=None):
     """[TR] Step 4: block-sparse softmax attention over the kept blocks.
 
-    ``rows``: flat row ids (b*heads + h)*n_tiles + i to compute (default: all).
+    ``rows``: flat row ids (b*heads + h)*n_rows + i to compute (default: all);
+    on a joint sequence rows i >= n_tiles are text query blocks, every clip row
+    also keeps every text block and a text row keeps every block.
     Returns (o [len(rows), tile_tokens, D] fp64, lse [len(rows), tile_tokens] fp64),
     rows of o in in-tile token order.
     """
-    n = n_tiles(wl)
+    n = n_rows(wl)
     R = tile_tokens(wl)
     if rows is None:
         rows = np.arange(wl.batch * wl.heads * n, dtype=np.int64)
@@ -271,12 +285,12 @@ def attention_bwd(wl, q, k, v, dout, kv_idx, kv_cnt, q_rows=None, k_rows=None, s
     attention equation, Step 4 and the paragraph on integrating SSTA during
     distillation training).
 
-    ``q_rows``: flat query-block rows (b*heads + h)*n_tiles + i whose dq is
+    ``q_rows``: flat query-block rows (b*heads + h)*n_rows + i whose dq is
     wanted; ``k_rows``: key-block rows whose dk, dv are wanted (defaults: all).
     Returns (dq [len(q_rows), R, D], dk [len(k_rows), R, D], dv [len(k_rows), R, D])
     in fp64, rows in in-block token order.
     """
-    n = n_tiles(wl)
+    n = n_rows(wl)
     R = tile_tokens(wl)
     allrows = np.arange(wl.batch * wl.heads * n, dtype=np.int64)
     q_rows = allrows if q_rows is None else np.ascontiguousarray(q_rows, dtype=np.int64)

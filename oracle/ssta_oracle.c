@@ -29,6 +29,16 @@
  *   - attention uses the exact fp32 widening of the bf16 inputs, fp64
  *     accumulation and a two-pass softmax (max, then sum).
  *
+ * Joint video + text sequences ([BLOG] section "Architecture: From Prompt to
+ * Video": single-stream blocks concatenate text and video tokens; section
+ * "Under the Hood: SSTA and Muon in Detail": the selection supports text
+ * masking, so scoring skips the text tokens).  Readings: each (batch, head)
+ * holds the N = T*H*W clip tokens followed by text_len text tokens; the
+ * text is cut into blocks of tile_tokens consecutive tokens (the last one
+ * partial) numbered after the clip's blocks; only clip blocks are pooled,
+ * scored and selected; every clip query block also keeps every text block;
+ * a text query block keeps every block.
+ *
  * Parity pins: every function here is pinned by tests (closed forms,
  * brute force, library special cases); see the tests for each.
  */
@@ -41,6 +51,7 @@ typedef struct {
   int32_t batch, heads, head_dim;
   int32_t T, H, W;
   int32_t tile_t, tile_h, tile_w;
+  int32_t text_len;   /* text tokens after the clip's tokens (joint sequence) */
 } orc_geom;
 
 enum { ORC_COMBINE_AND = 1u << 0, ORC_TOPK_EXCLUDE_WINDOW = 1u << 1 };
@@ -63,6 +74,17 @@ int64_t orc_n_tiles(const orc_geom* g) { return tiles_t(g) * tiles_h(g) * tiles_
 
 int32_t orc_tile_tokens(const orc_geom* g) { return g->tile_t * g->tile_h * g->tile_w; }
 
+/* Tokens per (batch, head): the clip's, then the text's. */
+static int64_t seq_len(const orc_geom* g) {
+  return (int64_t)g->T * g->H * g->W + g->text_len;
+}
+
+/* Blocks per (batch, head): the clip's blocks, then ceil(text_len / tile_tokens) text blocks. */
+int64_t orc_n_rows(const orc_geom* g) {
+  const int64_t R = orc_tile_tokens(g);
+  return orc_n_tiles(g) + (g->text_len + R - 1) / R;
+}
+
 /*
  * [TR] Step 1: tokens are grouped into contiguous 3D blocks.
  * Reading: blocks are numbered row-major over the (t, h, w) block grid and
@@ -77,8 +99,15 @@ void orc_token_to_tile(const orc_geom* g, int64_t n, int64_t* tile, int32_t* r) 
 }
 
 /* Inverse map: the token index of in-tile position r of tile `tile`, or -1
- * when that position lies beyond the grid (an edge block of a ragged grid). */
+ * when that position lies beyond the grid (an edge block of a ragged grid).
+ * Blocks from n_tiles on are text blocks: position r of text block u is text
+ * token u*tile_tokens + r, i.e. token N + u*tile_tokens + r (-1 past the text). */
 int64_t orc_tile_to_token(const orc_geom* g, int64_t tile, int32_t r) {
+  const int64_t n_clip = orc_n_tiles(g);
+  if (tile >= n_clip) {
+    const int64_t u = (tile - n_clip) * orc_tile_tokens(g) + r;
+    return u < g->text_len ? (int64_t)g->T * g->H * g->W + u : -1;
+  }
   const int64_t bt = tile / (tiles_h(g) * tiles_w(g));
   const int64_t by = (tile / tiles_w(g)) % tiles_h(g);
   const int64_t bx = tile % tiles_w(g);
@@ -90,19 +119,26 @@ int64_t orc_tile_to_token(const orc_geom* g, int64_t tile, int32_t r) {
   return (t * g->H + y) * g->W + x;
 }
 
-/* Gather x[b,h,N,D] (bf16 bits) into tile-major x_t[b,h,n_tiles,tile_tokens,D];
- * positions beyond a ragged grid are zero. */
+/* Gather x[b,h,S,D] (bf16 bits; S = N + text_len) into tile-major
+ * x_t[b,h,n_rows,tile_tokens,D], clip blocks then text blocks; positions
+ * beyond a ragged grid or past the text are zero. */
 void orc_permute(const orc_geom* g, const uint16_t* x, uint16_t* x_t) {
-  const int64_t N = (int64_t)g->T * g->H * g->W, D = g->head_dim;
-  const int64_t BH = (int64_t)g->batch * g->heads;
-  memset(x_t, 0, sizeof(uint16_t) * (size_t)(BH * orc_n_tiles(g) * orc_tile_tokens(g) * D));
+  const int64_t N = (int64_t)g->T * g->H * g->W, S = seq_len(g), D = g->head_dim;
+  const int64_t BH = (int64_t)g->batch * g->heads, NR = orc_n_rows(g);
+  const int64_t R = orc_tile_tokens(g);
+  memset(x_t, 0, sizeof(uint16_t) * (size_t)(BH * NR * R * D));
   for (int64_t bh = 0; bh < BH; ++bh)
-    for (int64_t n = 0; n < N; ++n) {
+    for (int64_t n = 0; n < S; ++n) {
       int64_t tile;
       int32_t r;
-      orc_token_to_tile(g, n, &tile, &r);
-      memcpy(x_t + ((bh * orc_n_tiles(g) + tile) * orc_tile_tokens(g) + r) * D,
-             x + (bh * N + n) * D, (size_t)D * sizeof(uint16_t));
+      if (n < N) {
+        orc_token_to_tile(g, n, &tile, &r);
+      } else {
+        tile = orc_n_tiles(g) + (n - N) / R;
+        r = (int32_t)((n - N) % R);
+      }
+      memcpy(x_t + ((bh * NR + tile) * R + r) * D, x + (bh * S + n) * D,
+             (size_t)D * sizeof(uint16_t));
     }
 }
 
@@ -114,7 +150,7 @@ void orc_permute(const orc_geom* g, const uint16_t* x, uint16_t* x_t) {
  * ragged grid.
  */
 void orc_pool(const orc_geom* g, const uint16_t* x, float* pooled) {
-  const int64_t N = (int64_t)g->T * g->H * g->W, D = g->head_dim;
+  const int64_t S = seq_len(g), D = g->head_dim;   /* text tokens are not pooled */
   const int64_t BH = (int64_t)g->batch * g->heads, NT = orc_n_tiles(g);
   const int32_t R = orc_tile_tokens(g);
 #pragma omp parallel for schedule(static)
@@ -127,7 +163,7 @@ void orc_pool(const orc_geom* g, const uint16_t* x, float* pooled) {
       const int64_t tok = orc_tile_to_token(g, i, r);
       if (tok < 0) continue;
       ++count;
-      const uint16_t* row = x + (bh * N + tok) * D;
+      const uint16_t* row = x + (bh * S + tok) * D;
       for (int64_t d = 0; d < D; ++d) s[d] = s[d] + bf16_to_f32(row[d]);
     }
     for (int64_t d = 0; d < D; ++d) pooled[bhi * D + d] = s[d] / (float)count;
@@ -345,46 +381,78 @@ int orc_build_lists(const orc_geom* g, int32_t wt, int32_t wh, int32_t ww, uint3
 }
 
 /*
+ * The key tokens of query block i of head bh ([TR] Step 4: the tokens of the
+ * kept blocks; on a joint sequence also every text block, and every block
+ * for a text query block).  Blocks in list order -- a clip row's kept list,
+ * then the text blocks; a text row's blocks 0 .. n_rows-1 -- and tokens in
+ * in-block order, positions without a token skipped.  blk[t] and pos[t] are
+ * the block and in-block position of keys[t].
+ */
+static int64_t row_keys(const orc_geom* g, int64_t bh, int64_t i, const int32_t* kv_idx,
+                        const int32_t* kv_cnt, int32_t max_kept, int64_t* keys, int64_t* blk,
+                        int32_t* pos) {
+  const int64_t n = orc_n_tiles(g), NR = orc_n_rows(g);
+  const int32_t R = orc_tile_tokens(g);
+  const int64_t clip_row = bh * n + i;
+  const int64_t listed = i < n ? kv_cnt[clip_row] : 0;
+  const int64_t nb = i < n ? listed + (NR - n) : NR;
+  int64_t m = 0;
+  for (int64_t c = 0; c < nb; ++c) {
+    int64_t j;
+    if (i >= n)
+      j = c;                                    /* text query block: every block */
+    else if (c < listed)
+      j = kv_idx[clip_row * max_kept + c];      /* the kept clip blocks */
+    else
+      j = n + (c - listed);                     /* the text blocks, always kept */
+    for (int32_t rr = 0; rr < R; ++rr) {
+      const int64_t tok = orc_tile_to_token(g, j, rr);
+      if (tok < 0) continue;
+      keys[m] = tok;
+      blk[m] = j;
+      pos[m] = rr;
+      ++m;
+    }
+  }
+  return m;
+}
+
+/*
  * [TR] the attention equation and Step 4 (flex_block_attention): softmax of
  * scale * q.k over the keys of the kept blocks only, then the weighted sum
  * of their values; full attention inside a kept block (Step 1).
- * For each selected row (b*heads + h)*n_tiles + i, writes o[sel][r][d] for
- * the query at in-tile position r (fp64) and lse[sel][r] = log sum exp.
- * Inputs are token-major bf16 bits [b, h, N, D].  An empty kept list gives
- * o = 0 and lse = -inf.
+ * For each selected row (b*heads + h)*n_rows + i (n_rows = n_tiles without
+ * text), writes o[sel][r][d] for the query at in-block position r (fp64) and
+ * lse[sel][r] = log sum exp.  Inputs are token-major bf16 bits [b, h, S, D].
+ * An empty key set, or a position without a token, gives o = 0 and lse = -inf.
  */
 void orc_attention(const orc_geom* g, double scale, const uint16_t* q, const uint16_t* k,
                    const uint16_t* v, const int32_t* kv_idx, const int32_t* kv_cnt,
                    int32_t max_kept, int64_t n_sel, const int64_t* sel_rows, double* o_out,
                    double* lse_out) {
-  const int64_t N = (int64_t)g->T * g->H * g->W, D = g->head_dim, n = orc_n_tiles(g);
+  const int64_t S = seq_len(g), D = g->head_dim, NR = orc_n_rows(g);
   const int32_t R = orc_tile_tokens(g);
+  const size_t cap = (size_t)NR * R + 8;
 #pragma omp parallel
   {
-    double* s = (double*)malloc(sizeof(double) * (size_t)max_kept * R + 8);
+    double* s = (double*)malloc(sizeof(double) * cap);
     double* qv = (double*)malloc(sizeof(double) * (size_t)D);
-    int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)max_kept * R + 8);
+    int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * cap);
+    int64_t* blk = (int64_t*)malloc(sizeof(int64_t) * cap);
+    int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * cap);
 #pragma omp for schedule(dynamic, 1)
     for (int64_t a = 0; a < n_sel; ++a) {
-      const int64_t row = sel_rows[a], bh = row / n, i = row % n;
-      const int32_t cnt = kv_cnt[row];
-      int64_t m = 0;
-      for (int32_t c = 0; c < cnt; ++c) {
-        const int32_t j = kv_idx[row * max_kept + c];
-        for (int32_t rr = 0; rr < R; ++rr) {
-          const int64_t tok = orc_tile_to_token(g, j, rr);
-          if (tok >= 0) keys[m++] = tok;
-        }
-      }
+      const int64_t row = sel_rows[a], bh = row / NR, i = row % NR;
+      const int64_t m = row_keys(g, bh, i, kv_idx, kv_cnt, max_kept, keys, blk, pos);
       for (int32_t r = 0; r < R; ++r) {
         const int64_t nq = orc_tile_to_token(g, i, r);
         double* o = o_out + (a * R + r) * D;
         for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
         if (m == 0 || nq < 0) { lse_out[a * R + r] = -INFINITY; continue; }
-        for (int64_t d = 0; d < D; ++d) qv[d] = (double)bf16_to_f32(q[(bh * N + nq) * D + d]);
+        for (int64_t d = 0; d < D; ++d) qv[d] = (double)bf16_to_f32(q[(bh * S + nq) * D + d]);
         double mx = -INFINITY;
         for (int64_t t = 0; t < m; ++t) {
-          const uint16_t* kr = k + (bh * N + keys[t]) * D;
+          const uint16_t* kr = k + (bh * S + keys[t]) * D;
           double acc = 0.0;
           for (int64_t d = 0; d < D; ++d) acc += qv[d] * (double)bf16_to_f32(kr[d]);
           s[t] = acc * scale;
@@ -396,7 +464,7 @@ void orc_attention(const orc_geom* g, double scale, const uint16_t* q, const uin
           l += s[t];
         }
         for (int64_t t = 0; t < m; ++t) {
-          const uint16_t* vr = v + (bh * N + keys[t]) * D;
+          const uint16_t* vr = v + (bh * S + keys[t]) * D;
           const double p = s[t] / l;
           for (int64_t d = 0; d < D; ++d) o[d] += p * (double)bf16_to_f32(vr[d]);
         }
@@ -406,6 +474,8 @@ void orc_attention(const orc_geom* g, double scale, const uint16_t* q, const uin
     free(s);
     free(qv);
     free(keys);
+    free(blk);
+    free(pos);
   }
 }
 
@@ -416,17 +486,16 @@ void orc_attention(const orc_geom* g, double scale, const uint16_t* q, const uin
  * trained during distillation, so gradients flow through the sparse attention
  * with the kept lists held fixed -- the selection is an integer and carries none).
  *
- * For a query token a of block i with kept key tokens b (the tokens of the
- * blocks in kv_idx[i]):  s_ab = scale q_a.k_b,  p_ab = softmax_b(s_ab),
- * o_a = sum_b p_ab v_b.  Given dO:
+ * For a query token a of block i with key tokens b (row_keys):
+ * s_ab = scale q_a.k_b,  p_ab = softmax_b(s_ab),  o_a = sum_b p_ab v_b.  Given dO:
  *   D_a   = dO_a . o_a
  *   dS_ab = p_ab (dO_a . v_b - D_a)
  *   dq_a  = scale sum_b dS_ab k_b
- *   dk_b  = scale sum_a dS_ab q_a      (over every query token a that keeps b)
+ *   dk_b  = scale sum_a dS_ab q_a      (over every query token a whose keys hold b)
  *   dv_b  = sum_a p_ab dO_a
  * Everything in fp64 from the exact widening of the bf16 inputs.
  * dq is returned for the query-block rows q_rows, dk and dv for the key-block
- * rows k_rows (flat ids (b*heads + h)*n_tiles + block), in in-block token order.
+ * rows k_rows (flat ids (b*heads + h)*n_rows + block), in in-block token order.
  */
 
 /* Softmax row of query token (bh, nq) over the key tokens keys[0..m): p (m), o (D), D_a. */
@@ -434,15 +503,15 @@ static void bwd_row(const orc_geom* g, double scale, int64_t bh, int64_t nq, con
                     const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                     const int64_t* keys, int64_t m, double* qv, double* dov, double* p,
                     double* o, double* dsum) {
-  const int64_t N = (int64_t)g->T * g->H * g->W, D = g->head_dim;
+  const int64_t S = seq_len(g), D = g->head_dim;
   for (int64_t d = 0; d < D; ++d) {
-    qv[d] = (double)bf16_to_f32(q[(bh * N + nq) * D + d]);
-    dov[d] = (double)bf16_to_f32(dout[(bh * N + nq) * D + d]);
+    qv[d] = (double)bf16_to_f32(q[(bh * S + nq) * D + d]);
+    dov[d] = (double)bf16_to_f32(dout[(bh * S + nq) * D + d]);
     o[d] = 0.0;
   }
   double mx = -INFINITY;
   for (int64_t t = 0; t < m; ++t) {
-    const uint16_t* kr = k + (bh * N + keys[t]) * D;
+    const uint16_t* kr = k + (bh * S + keys[t]) * D;
     double acc = 0.0;
     for (int64_t d = 0; d < D; ++d) acc += qv[d] * (double)bf16_to_f32(kr[d]);
     p[t] = acc * scale;
@@ -455,7 +524,7 @@ static void bwd_row(const orc_geom* g, double scale, int64_t bh, int64_t nq, con
   }
   for (int64_t t = 0; t < m; ++t) {
     p[t] /= l;
-    const uint16_t* vr = v + (bh * N + keys[t]) * D;
+    const uint16_t* vr = v + (bh * S + keys[t]) * D;
     for (int64_t d = 0; d < D; ++d) o[d] += p[t] * (double)bf16_to_f32(vr[d]);
   }
   double da = 0.0;
@@ -466,31 +535,13 @@ static void bwd_row(const orc_geom* g, double scale, int64_t bh, int64_t nq, con
 /* dS_ab for the row (p holds the probabilities, overwritten with dS). */
 static void bwd_ds(const orc_geom* g, int64_t bh, const uint16_t* v, const int64_t* keys,
                    int64_t m, const double* dov, double da, double* p) {
-  const int64_t N = (int64_t)g->T * g->H * g->W, D = g->head_dim;
+  const int64_t S = seq_len(g), D = g->head_dim;
   for (int64_t t = 0; t < m; ++t) {
-    const uint16_t* vr = v + (bh * N + keys[t]) * D;
+    const uint16_t* vr = v + (bh * S + keys[t]) * D;
     double dp = 0.0;
     for (int64_t d = 0; d < D; ++d) dp += dov[d] * (double)bf16_to_f32(vr[d]);
     p[t] = p[t] * (dp - da);
   }
-}
-
-/* The existing key tokens of a row's kept blocks; slot[t] = c * R + rr (list
- * position c, in-block position rr) of keys[t]. */
-static int64_t kept_keys(const orc_geom* g, int64_t row, const int32_t* kv_idx,
-                         const int32_t* kv_cnt, int32_t max_kept, int64_t* keys, int64_t* slot) {
-  const int32_t R = orc_tile_tokens(g);
-  int64_t m = 0;
-  for (int32_t c = 0; c < kv_cnt[row]; ++c) {
-    const int32_t j = kv_idx[row * max_kept + c];
-    for (int32_t rr = 0; rr < R; ++rr) {
-      const int64_t tok = orc_tile_to_token(g, j, rr);
-      if (tok < 0) continue;
-      slot[m] = (int64_t)c * R + rr;
-      keys[m++] = tok;
-    }
-  }
-  return m;
 }
 
 void orc_attention_bwd(const orc_geom* g, double scale, const uint16_t* q, const uint16_t* k,
@@ -498,22 +549,23 @@ void orc_attention_bwd(const orc_geom* g, double scale, const uint16_t* q, const
                        const int32_t* kv_cnt, int32_t max_kept, int64_t n_qrows,
                        const int64_t* q_rows, double* dq_out, int64_t n_krows,
                        const int64_t* k_rows, double* dk_out, double* dv_out) {
-  const int64_t N = (int64_t)g->T * g->H * g->W, D = g->head_dim, n = orc_n_tiles(g);
+  const int64_t S = seq_len(g), D = g->head_dim, NR = orc_n_rows(g);
   const int32_t R = orc_tile_tokens(g);
-  const size_t cap = (size_t)max_kept * R + 8;
+  const size_t cap = (size_t)NR * R + 8;
 #pragma omp parallel
   {
     double* p = (double*)malloc(sizeof(double) * cap);
     int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * cap);
-    int64_t* slot = (int64_t*)malloc(sizeof(int64_t) * cap);
+    int64_t* blk = (int64_t*)malloc(sizeof(int64_t) * cap);
+    int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * cap);
     double* qv = (double*)malloc(sizeof(double) * (size_t)D);
     double* dov = (double*)malloc(sizeof(double) * (size_t)D);
     double* o = (double*)malloc(sizeof(double) * (size_t)D);
     /* dq: one selected query-block row per iteration */
 #pragma omp for schedule(dynamic, 1)
     for (int64_t a = 0; a < n_qrows; ++a) {
-      const int64_t row = q_rows[a], bh = row / n, i = row % n;
-      const int64_t m = kept_keys(g, row, kv_idx, kv_cnt, max_kept, keys, slot);
+      const int64_t row = q_rows[a], bh = row / NR, i = row % NR;
+      const int64_t m = row_keys(g, bh, i, kv_idx, kv_cnt, max_kept, keys, blk, pos);
       for (int32_t r = 0; r < R; ++r) {
         double* dq = dq_out + (a * R + r) * D;
         for (int64_t d = 0; d < D; ++d) dq[d] = 0.0;
@@ -523,26 +575,24 @@ void orc_attention_bwd(const orc_geom* g, double scale, const uint16_t* q, const
         bwd_row(g, scale, bh, nq, q, k, v, dout, keys, m, qv, dov, p, o, &da);
         bwd_ds(g, bh, v, keys, m, dov, da, p);
         for (int64_t t = 0; t < m; ++t) {
-          const uint16_t* kr = k + (bh * N + keys[t]) * D;
+          const uint16_t* kr = k + (bh * S + keys[t]) * D;
           for (int64_t d = 0; d < D; ++d) dq[d] += scale * p[t] * (double)bf16_to_f32(kr[d]);
         }
       }
     }
     /* dk, dv: one selected key-block row per iteration; every query block of
-       the head that keeps it contributes, in ascending block order */
+       the head whose keys hold it contributes, in ascending block order */
 #pragma omp for schedule(dynamic, 1)
     for (int64_t a = 0; a < n_krows; ++a) {
-      const int64_t krow = k_rows[a], bh = krow / n, j = krow % n;
+      const int64_t krow = k_rows[a], bh = krow / NR, j = krow % NR;
       double* dk = dk_out + a * R * D;
       double* dv = dv_out + a * R * D;
       for (int64_t e = 0; e < (int64_t)R * D; ++e) dk[e] = dv[e] = 0.0;
-      for (int64_t i = 0; i < n; ++i) {
-        const int64_t row = bh * n + i;
-        int32_t pos = -1;
-        for (int32_t c = 0; c < kv_cnt[row]; ++c)
-          if (kv_idx[row * max_kept + c] == j) pos = c;
-        if (pos < 0) continue;
-        const int64_t m = kept_keys(g, row, kv_idx, kv_cnt, max_kept, keys, slot);
+      for (int64_t i = 0; i < NR; ++i) {
+        const int64_t m = row_keys(g, bh, i, kv_idx, kv_cnt, max_kept, keys, blk, pos);
+        int found = 0;
+        for (int64_t t = 0; t < m && !found; ++t) found = blk[t] == j;
+        if (!found) continue;
         for (int32_t r = 0; r < R; ++r) {
           const int64_t nq = orc_tile_to_token(g, i, r);
           if (nq < 0) continue;
@@ -550,22 +600,21 @@ void orc_attention_bwd(const orc_geom* g, double scale, const uint16_t* q, const
           bwd_row(g, scale, bh, nq, q, k, v, dout, keys, m, qv, dov, p, o, &da);
           /* keep p for dv before it becomes dS */
           for (int64_t t = 0; t < m; ++t) {
-            if (slot[t] / R != pos) continue;
-            const int64_t rr = slot[t] % R;
-            for (int64_t d = 0; d < D; ++d) dv[rr * D + d] += p[t] * dov[d];
+            if (blk[t] != j) continue;
+            for (int64_t d = 0; d < D; ++d) dv[pos[t] * D + d] += p[t] * dov[d];
           }
           bwd_ds(g, bh, v, keys, m, dov, da, p);
           for (int64_t t = 0; t < m; ++t) {
-            if (slot[t] / R != pos) continue;
-            const int64_t rr = slot[t] % R;
-            for (int64_t d = 0; d < D; ++d) dk[rr * D + d] += scale * p[t] * qv[d];
+            if (blk[t] != j) continue;
+            for (int64_t d = 0; d < D; ++d) dk[pos[t] * D + d] += scale * p[t] * qv[d];
           }
         }
       }
     }
     free(p);
     free(keys);
-    free(slot);
+    free(blk);
+    free(pos);
     free(qv);
     free(dov);
     free(o);

@@ -11,6 +11,9 @@ Generator recipe (the C file beside this one implements it):
     phi ~ U[0, 2*pi) per (batch, head, channel).
   * Philox4x32-10 counters keyed by (seed, tensor id), tensor id 0/1/2 = Q/K/V.
   * value -> fp32 -> bf16 round-to-nearest-even.
+  * Joint sequences (text_len > 0): the clip's tokens are followed by text_len
+    text tokens, drawn i.i.d. N(0, 1) with tensor id 16 + (the clip tensor's id),
+    so the layout is [batch, heads, T*H*W + text_len, head_dim].
 """
 from __future__ import annotations
 
@@ -84,10 +87,26 @@ class Workload:
     noise_std: float = 0.5
     seed: int = 0
     dup_tiles: tuple = field(default=())   # ((src_tile, dst_tile), ...) copies for exact ties
+    text_len: int = 0         # text tokens after the clip's tokens
 
     @property
     def n_tokens(self) -> int:
+        """Clip tokens per (batch, head)."""
         return self.T * self.H * self.W
+
+    @property
+    def seq_len(self) -> int:
+        """Tokens per (batch, head): the clip's, then the text's."""
+        return self.n_tokens + self.text_len
+
+    @property
+    def n_text_blocks(self) -> int:
+        return -(-self.text_len // (self.tile[0] * self.tile[1] * self.tile[2]))
+
+    @property
+    def n_rows(self) -> int:
+        """Blocks per (batch, head): clip blocks, then text blocks."""
+        return self.n_tiles + self.n_text_blocks
 
     @property
     def tile_grid(self) -> tuple:
@@ -137,7 +156,21 @@ LATENT = {
     "720p-10s-latent": Workload("720p-10s-latent", 1, 16, 61, 45, 80, topk=48, seed=5),
 }
 
-ALL = {**CONFIGS, **EXTRA, **LATENT}
+# Joint video + text sequences: clip tokens followed by text tokens (a single-stream
+# block's input).  Text lengths: a partial text block (77), two full blocks (256), and a
+# ragged grid with a text tail of one full block plus 2 tokens (130).
+JOINT = {
+    "joint-tiny": Workload("joint-tiny", 1, 2, 4, 16, 16, topk=2, kind=0, noise_std=1.0,
+                           seed=20, text_len=77),
+    "joint-grid32": Workload("joint-grid32", 1, 2, 4, 32, 32, win=(1, 1, 1), topk=2, seed=21,
+                             text_len=256),
+    "joint-partial": Workload("joint-partial", 2, 1, 5, 20, 24, win=(1, 0, 1), topk=3,
+                              seed=22, text_len=130),
+    "720p-10s-text": Workload("720p-10s-text", 1, 16, 60, 48, 80, topk=48, seed=23,
+                              text_len=256),
+}
+
+ALL = {**CONFIGS, **EXTRA, **LATENT, **JOINT}
 
 
 def _copy_tiles(x: np.ndarray, wl: Workload) -> None:
@@ -153,7 +186,8 @@ def _copy_tiles(x: np.ndarray, wl: Workload) -> None:
 
 
 def generate(wl: Workload, tensor: int) -> np.ndarray:
-    """bf16 bits [batch, heads, N, head_dim] for tensor 0/1/2 (Q/K/V) of workload ``wl``."""
+    """bf16 bits [batch, heads, N + text_len, head_dim] for tensor 0/1/2 (Q/K/V) of
+    workload ``wl`` (other ids: other tensors of the same shape, e.g. 3 for dO)."""
     lib = _load()
     out = np.empty((wl.batch, wl.heads, wl.n_tokens, wl.head_dim), dtype=np.uint16)
     rc = lib.synth_generate(out.ctypes.data, wl.batch, wl.heads, wl.T, wl.H, wl.W, wl.head_dim,
@@ -162,7 +196,14 @@ def generate(wl: Workload, tensor: int) -> np.ndarray:
         raise ValueError("synth_generate rejected workload %r" % (wl,))
     if wl.dup_tiles:
         _copy_tiles(out, wl)
-    return out
+    if wl.text_len == 0:
+        return out
+    txt = np.empty((wl.batch, wl.heads, wl.text_len, wl.head_dim), dtype=np.uint16)
+    rc = lib.synth_generate(txt.ctypes.data, wl.batch, wl.heads, 1, 1, wl.text_len,
+                            wl.head_dim, 0, wl.seed, 16 + tensor, 1.0, 0.5, 2.0)
+    if rc != 0:
+        raise ValueError("synth_generate rejected the text of workload %r" % (wl,))
+    return np.concatenate([out, txt], axis=2)
 
 
 def make_qkv(wl: Workload):
