@@ -30,9 +30,20 @@
  *     exist (block means average those; attention runs over them; positions
  *     without a token are zero in tile-major copies and outputs and have LSE
  *     -inf).
+ *   - Joint video + text sequences ("HunyuanVideo-1.5: An 8.3B-Parameter
+ *     Video Diffusion Model Built for Consumer GPUs" page: section
+ *     "Architecture: From Prompt to Video", single-stream blocks concatenate
+ *     text and video tokens; section "Under the Hood: SSTA and Muon in
+ *     Detail", text masking keeps the text out of scoring): with text_len > 0
+ *     each (batch, head) holds S = T*H*W + text_len tokens, the clip's first.
+ *     The text is cut into ceil(text_len/tile_tokens) blocks of consecutive
+ *     tokens, numbered after the clip's n_tiles blocks: n_rows = n_tiles +
+ *     text blocks (ssta_block_rows).  Only clip blocks are pooled, scored and
+ *     selected; in attention every clip query block also keeps every text
+ *     block and a text query block keeps every block.
  *   - Current limits: head_dim == 128, tile_t*tile_h*tile_w == 128 tokens;
  *     ssta_score_select needs n_tiles <= 4096;
- *     the attention entry points need n_tiles < 65536 (one head's blocks are
+ *     the attention entry points need n_rows < 65536 (one head's blocks are
  *     addressed with 32-bit offsets).
  */
 #ifndef SSTA_H
@@ -56,11 +67,12 @@ typedef enum ssta_status {
   SSTA_ERR_WORKSPACE = -7   /* workspace missing or smaller than ssta_workspace_bytes() */
 } ssta_status;
 
-/* Clip geometry.  All fields >= 1. */
+/* Clip geometry.  All fields >= 1 except text_len. */
 typedef struct ssta_geom {
   int32_t batch, heads, head_dim;   /* head_dim must be 128 */
   int32_t T, H, W;                  /* latent grid, tokens row-major (t, y, x) */
   int32_t tile_t, tile_h, tile_w;   /* block size; product 128 (so powers of two) */
+  int32_t text_len;                 /* >= 0 text tokens after the clip's (0: clip only) */
 } ssta_geom_t;
 
 /* Selection and attention parameters. */
@@ -86,26 +98,32 @@ typedef struct ssta_params {
 #define SSTA_TOPK_EXCLUDE_WINDOW (1u << 1)
 
 /* Layouts of a tiled tensor written by ssta_tile_pool. */
-#define SSTA_LAYOUT_TOKEN_MAJOR 0   /* [batch, heads, n_tiles, tile_tokens, head_dim] */
-#define SSTA_LAYOUT_DIM_MAJOR 1     /* [batch, heads, n_tiles, head_dim, tile_tokens] */
+#define SSTA_LAYOUT_TOKEN_MAJOR 0   /* [batch, heads, n_rows, tile_tokens, head_dim] */
+#define SSTA_LAYOUT_DIM_MAJOR 1     /* [batch, heads, n_rows, head_dim, tile_tokens] */
+
+/* Blocks per (batch, head), n_rows: the clip's n_tiles plus
+ * ceil(text_len / tile_tokens) text blocks.  < 0 on a bad argument. */
+int64_t ssta_block_rows(const ssta_geom_t* g);
 
 /*
  * Step 1 (3D block partition) and the block means of Step 2.
- *   x       in : bf16 [batch, heads, T*H*W, head_dim], token-major.
+ *   x       in : bf16 [batch, heads, S, head_dim], token-major (S = T*H*W + text_len).
  *   x_tiled out: bf16, the same values gathered block by block in `layout`
- *                (SSTA_LAYOUT_*); NULL to skip.
+ *                (SSTA_LAYOUT_*), clip blocks then text blocks; NULL to skip.
  *   pooled  out: fp32 [batch, heads, n_tiles, head_dim], the mean of each
- *                block's tokens: the fp32 sum over the block's existing tokens
- *                in ascending in-block order divided by their count; NULL to skip.
- * Positions an edge block of a ragged grid lacks are zero in x_tiled.
- * At least one of x_tiled and pooled must be non-NULL.
+ *                clip block's tokens: the fp32 sum over the block's existing
+ *                tokens in ascending in-block order divided by their count;
+ *                NULL to skip.  Text blocks have no mean.
+ * Positions an edge block of a ragged grid lacks, and positions past the
+ * text, are zero in x_tiled.  At least one of x_tiled and pooled must be
+ * non-NULL.
  */
 int ssta_tile_pool(const ssta_geom_t* g, const void* x, void* x_tiled, int32_t layout,
                    float* pooled, void* stream);
 
 /*
- * Inverse of the token-major gather: x_tiled bf16 [batch, heads, n_tiles,
- * tile_tokens, head_dim] -> x bf16 [batch, heads, T*H*W, head_dim].
+ * Inverse of the token-major gather: x_tiled bf16 [batch, heads, n_rows,
+ * tile_tokens, head_dim] -> x bf16 [batch, heads, S, head_dim].
  */
 int ssta_tile_unpermute(const ssta_geom_t* g, const void* x_tiled, void* x, void* stream);
 
@@ -164,14 +182,16 @@ int ssta_build_mask(const ssta_geom_t* g, const ssta_params_t* p, const int32_t*
 /*
  * Step 4 (block-sparse attention): for every query token of block i, softmax
  * of scale*q.k over the tokens of the kept key blocks of i only, then the
- * weighted sum of their values; full attention inside a kept block.
- *   q_t, k_t in : bf16 [batch, heads, n_tiles, tile_tokens, head_dim] (token-major tiles).
- *   v_t      in : bf16 [batch, heads, n_tiles, head_dim, tile_tokens] (dim-major tiles).
- *   kv_idx, kv_cnt in: as written by ssta_build_mask; kv_idx row stride max_kept
- *                 (>= 1).  Pass kv_idx = kv_cnt = NULL and max_kept = 0 for dense
- *                 attention (every block kept).
- *   o_t     out : bf16 [batch, heads, n_tiles, tile_tokens, head_dim] (token-major tiles).
- *   lse     out : fp32 [batch, heads, n_tiles, tile_tokens], natural-log
+ * weighted sum of their values; full attention inside a kept block.  On a
+ * joint sequence the kept blocks of a clip query block are its list plus
+ * every text block, and a text query block keeps every block.
+ *   q_t, k_t in : bf16 [batch, heads, n_rows, tile_tokens, head_dim] (token-major tiles).
+ *   v_t      in : bf16 [batch, heads, n_rows, head_dim, tile_tokens] (dim-major tiles).
+ *   kv_idx, kv_cnt in: as written by ssta_build_mask (clip blocks only);
+ *                 kv_idx row stride max_kept (>= 1).  Pass kv_idx = kv_cnt =
+ *                 NULL and max_kept = 0 for dense attention (every block kept).
+ *   o_t     out : bf16 [batch, heads, n_rows, tile_tokens, head_dim] (token-major tiles).
+ *   lse     out : fp32 [batch, heads, n_rows, tile_tokens], natural-log
  *                 log-sum-exp of the scaled scores; NULL to skip.
  * Arithmetic: bf16 products on the matrix cores, fp32 accumulation, fp32
  * online softmax.  A row with no kept block yields o = 0, lse = -inf.
@@ -188,11 +208,11 @@ int ssta_attention_fwd(const ssta_geom_t* g, const ssta_params_t* p, const void*
  * tile-major copy and O no unpermute (each kept key block is gathered token
  * row by token row straight into LDS).  V keeps its dim-major block layout:
  * the P.V product needs 8 consecutive keys of one channel per lane.
- *   q        in : bf16 [batch, heads, T*H*W, head_dim] (token-major).
- *   k        in : bf16 [batch, heads, T*H*W, head_dim] (token-major).
- *   v_t      in : bf16 [batch, heads, n_tiles, head_dim, tile_tokens] (dim-major tiles).
+ *   q        in : bf16 [batch, heads, S, head_dim] (token-major).
+ *   k        in : bf16 [batch, heads, S, head_dim] (token-major).
+ *   v_t      in : bf16 [batch, heads, n_rows, head_dim, tile_tokens] (dim-major tiles).
  *   kv_idx, kv_cnt, max_kept, lse: as for ssta_attention_fwd (LSE stays tile-major).
- *   o       out : bf16 [batch, heads, T*H*W, head_dim] (token-major).
+ *   o       out : bf16 [batch, heads, S, head_dim] (token-major).
  * Results are bit-identical to permuting Q and K with ssta_tile_pool,
  * ssta_attention_fwd and ssta_tile_unpermute.
  */

@@ -32,7 +32,8 @@ def bits(t: torch.Tensor) -> np.ndarray:
 
 def geom_of(wl):
     import video_dit_block_tile_amd as m
-    return m.make_geom(wl.batch, wl.heads, wl.T, wl.H, wl.W, tile=wl.tile, head_dim=wl.head_dim)
+    return m.make_geom(wl.batch, wl.heads, wl.T, wl.H, wl.W, tile=wl.tile, head_dim=wl.head_dim,
+                       text_len=wl.text_len)
 
 
 def params_of(wl, flags=0, topk=None, lambda_=None, beta=None):
@@ -45,10 +46,11 @@ def params_of(wl, flags=0, topk=None, lambda_=None, beta=None):
 
 def sample_rows(wl, count: int, seed: int = 0) -> np.ndarray:
     """Deterministic sample of (batch*head, query block) rows: every corner and
-    edge-centre block of the block grid in the first and last head, plus random rows."""
+    edge-centre block of the block grid and every text block, in the first and
+    last head, plus random rows.  Rows are (b*heads + h)*n_rows + block."""
     nt, ny, nx = wl.tile_grid
-    n = wl.n_tiles
-    special = set()
+    n = wl.n_rows
+    special = set(range(wl.n_tiles, n))
     for t in {0, nt // 2, nt - 1}:
         for y in {0, ny // 2, ny - 1}:
             for x in {0, nx // 2, nx - 1}:
@@ -70,18 +72,18 @@ def compare_o(o_gpu_rows: np.ndarray, o_ref: np.ndarray):
 
 
 def token_rows(wl, rows):
-    """[len(rows), 128] token indices of the query rows (b*heads+h)*n_tiles + i, in in-block
-    order (-1 where a ragged grid has no token)."""
-    n = wl.n_tiles
+    """[len(rows), 128] token indices of the query rows (b*heads+h)*n_rows + i, in in-block
+    order (-1 where a ragged grid or the text has no token)."""
+    n = wl.n_rows
     return np.array([[oracle.tile_to_token(wl, int(r) % n, t) for t in range(128)] for r in rows])
 
 
 def o_rows(wl, o_tok: torch.Tensor, rows) -> np.ndarray:
     """fp32 O rows [len(rows), 128, 128] gathered from a token-major output;
     positions beyond a ragged grid (no token) read as zero."""
-    o = o_tok.float().cpu().numpy().reshape(wl.batch * wl.heads, wl.n_tokens, 128)
+    o = o_tok.float().cpu().numpy().reshape(wl.batch * wl.heads, wl.seq_len, 128)
     tok = token_rows(wl, rows)
-    bh = np.asarray(rows) // wl.n_tiles
+    bh = np.asarray(rows) // wl.n_rows
     out = o[bh[:, None], np.maximum(tok, 0)]
     out[tok < 0] = 0.0
     return out
@@ -101,12 +103,12 @@ def lse_bound(wl, q, k, rows) -> np.ndarray:
     - fp32 exp2/log2, the scaling fma and the fp32 running sum: at most 2^-12.
     """
     bh_all = wl.batch * wl.heads
-    qn = np.linalg.norm(si.bf16_bits_to_f32(q).reshape(bh_all, wl.n_tokens, 128)
+    qn = np.linalg.norm(si.bf16_bits_to_f32(q).reshape(bh_all, wl.seq_len, 128)
                         .astype(np.float64), axis=-1)
-    kmax = np.linalg.norm(si.bf16_bits_to_f32(k).reshape(bh_all, wl.n_tokens, 128)
+    kmax = np.linalg.norm(si.bf16_bits_to_f32(k).reshape(bh_all, wl.seq_len, 128)
                           .astype(np.float64), axis=-1).max(axis=-1)
     rows = np.asarray(rows)
-    bh = rows // wl.n_tiles
+    bh = rows // wl.n_rows
     tok = token_rows(wl, rows)
     scale = oracle.default_scale(wl)
     return (np.log1p(2.0 ** -9) + 2.0 ** -16 * scale * qn[bh[:, None], tok] * kmax[bh][:, None]

@@ -61,6 +61,23 @@ def test_geometry_validation():
     assert lib.ssta_tile_pool(None, good, good, 0, None, None) == ARG
 
 
+def test_block_rows_of_joint_sequences():
+    """Text blocks follow the clip's blocks, 128 tokens each; the selection
+    sizes do not see the text."""
+    lib = m.load()
+    assert m.ssta_block_rows(m.make_geom(1, 2, 4, 16, 16)) == 8
+    assert m.ssta_block_rows(m.make_geom(1, 2, 4, 16, 16, text_len=77)) == 9
+    assert m.ssta_block_rows(m.make_geom(1, 2, 4, 16, 16, text_len=256)) == 10
+    assert m.ssta_block_rows(m.make_geom(1, 2, 4, 16, 16, text_len=257)) == 11
+    assert m.ssta_block_rows(m.make_geom(1, 2, 5, 20, 24, text_len=1)) == 28   # ragged grid
+    g = m.make_geom(1, 16, 60, 48, 80, text_len=256)
+    p = m.make_params(topk=48)
+    assert m.ssta_topk_width(g, p) == 48 and m.ssta_max_kept(g, p) == 27 + 48
+    bad = m.make_geom(1, 2, 4, 16, 16, text_len=-1)
+    assert lib.ssta_block_rows(ctypes.byref(bad)) == ARG
+    assert lib.ssta_tile_pool(ctypes.byref(bad), 16, 16, 0, None, None) == ARG
+
+
 def test_pointer_validation():
     lib = m.load()
     g = _g()

@@ -21,9 +21,9 @@ MEAN_REL = 5e-3
 
 def _rows_of(wl, t, rows):
     """fp32 [len(rows), 128, 128] block rows of a token-major device tensor."""
-    x = t.float().cpu().numpy().reshape(wl.batch * wl.heads, wl.n_tokens, 128)
+    x = t.float().cpu().numpy().reshape(wl.batch * wl.heads, wl.seq_len, 128)
     tok = token_rows(wl, rows)
-    bh = np.asarray(rows) // wl.n_tiles
+    bh = np.asarray(rows) // wl.n_rows
     out = x[bh[:, None], np.maximum(tok, 0)].astype(np.float64)
     out[tok < 0] = 0.0
     return out
@@ -62,7 +62,7 @@ def test_backward_vs_oracle(name):
     plan, dq, dk, dv = _run(wl, q, k, v, do)
     sel = oracle.select(wl, q, k)
     assert np.array_equal(plan.kv_idx.cpu().numpy(), sel["kv_idx"])
-    rows = np.arange(wl.batch * wl.heads * wl.n_tiles)
+    rows = np.arange(wl.batch * wl.heads * wl.n_rows)
     rq, rk, rv = oracle.attention_bwd(wl, q, k, v, do, sel["kv_idx"], sel["kv_cnt"])
     _check("dq", _rows_of(wl, dq, rows), rq)
     _check("dk", _rows_of(wl, dk, rows), rk)

@@ -1,7 +1,8 @@
 """GPU parity of every step of the SSTA forward against the CPU oracle, through
 the C ABI, on small workloads that span several blocks, odd block grids,
 batch > 1, exact score ties, window 0, k = 0, k above the block count, and
-grids the block size does not divide (partial edge blocks).
+grids the block size does not divide (partial edge blocks), and joint video +
+text sequences (text blocks always kept, text query blocks dense).
 
 Bit-exact: tile copies (both layouts), block means, Score_r, Score_i, top-k
 ids, kept lists, bitmasks.  Within tolerance (tests/_helpers.py): the bf16
@@ -19,7 +20,7 @@ from _helpers import (O_MAX_ABS, O_MEAN_ABS, bits, check_lse, compare_o, geom_of
 pytestmark = pytest.mark.gpu
 
 SMALL = ["tiny", "grid32-w1-k2", "grid32-w0-k3", "grid32-w0-k0", "dup-ties", "ragged", "wide-k",
-         "partial", "partial-x"]
+         "partial", "partial-x", "joint-tiny", "joint-grid32", "joint-partial"]
 _cache = {}
 
 
@@ -46,7 +47,7 @@ def test_tile_pool_bit_exact(name):
     g = geom_of(wl)
     for x in (q, v):
         xd = to_dev(x)
-        tok = torch.empty(wl.batch, wl.heads, wl.n_tiles, 128, 128, dtype=torch.bfloat16,
+        tok = torch.empty(wl.batch, wl.heads, wl.n_rows, 128, 128, dtype=torch.bfloat16,
                           device="cuda")
         dim = torch.empty_like(tok)
         pooled = torch.empty(wl.batch, wl.heads, wl.n_tiles, 128, dtype=torch.float32,
@@ -61,13 +62,14 @@ def test_tile_pool_bit_exact(name):
                               oracle.pool(wl, x).view(np.uint32))
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged", "partial", "partial-x"])
+@pytest.mark.parametrize("name", ["tiny", "ragged", "partial", "partial-x", "joint-tiny",
+                                  "joint-partial"])
 def test_unpermute_inverts(name):
     import video_dit_block_tile_amd as m
     wl, q, k, v, sel = _case(name)
     g = geom_of(wl)
     xt = to_dev(oracle.permute(wl, k))
-    out = torch.empty(wl.batch, wl.heads, wl.n_tokens, 128, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(wl.batch, wl.heads, wl.seq_len, 128, dtype=torch.bfloat16, device="cuda")
     m.ssta_tile_unpermute(g, xt, out)
     torch.cuda.synchronize()
     assert np.array_equal(bits(out), k)
@@ -126,10 +128,10 @@ def test_attention_vs_oracle(name, fused):
     _check_attention(wl, q, k, v, sel, plan, rows)
     if not fused:
         # the tile-major output holds the same bits as the token-major one
-        o_tok = bits(plan.o).reshape(wl.batch * wl.heads, wl.n_tokens, 128)
+        o_tok = bits(plan.o).reshape(wl.batch * wl.heads, wl.seq_len, 128)
         o_til = bits(plan.o_t).reshape(-1, 128, 128)
         for row in rows[:8]:
-            bh, i = divmod(int(row), wl.n_tiles)
+            bh, i = divmod(int(row), wl.n_rows)
             toks = np.array([oracle.tile_to_token(wl, i, r) for r in range(128)])
             there = toks >= 0        # an edge block of a ragged grid holds zero rows
             assert np.array_equal(o_tok[bh][toks[there]], o_til[row][there])
@@ -137,7 +139,7 @@ def test_attention_vs_oracle(name, fused):
 
 
 @pytest.mark.parametrize("name", ["grid32-w1-k2", "ragged", "dup-ties", "wide-k", "partial",
-                                  "partial-x"])
+                                  "partial-x", "joint-tiny", "joint-grid32", "joint-partial"])
 def test_fused_io_matches_materialised(name):
     """Gathering blocks inside the kernel gives the same bits as permuting first."""
     wl, q, k, v, sel = _case(name)
@@ -228,6 +230,21 @@ def test_flag_variants(flags):
     if flags == oracle.COMBINE_AND | oracle.TOPK_EXCLUDE_WINDOW:
         # selection outside the window intersected with the window: nothing is kept
         assert np.all(sel["kv_cnt"] == 0) and np.all(o_t == 0)
+
+
+def test_joint_text_with_nothing_kept():
+    """AND of the window with a selection outside it keeps no clip block; clip
+    rows still attend to the text, and text rows to everything."""
+    flags = oracle.COMBINE_AND | oracle.TOPK_EXCLUDE_WINDOW
+    wl, q, k, v, sel = _case("joint-grid32", flags)
+    assert np.all(sel["kv_cnt"] == 0)
+    plan = _plan(wl, flags)
+    plan.run(to_dev(q), to_dev(k), to_dev(v))
+    torch.cuda.synchronize()
+    assert np.array_equal(plan.kv_cnt.cpu().numpy(), sel["kv_cnt"])
+    rows = np.arange(wl.batch * wl.heads * wl.n_rows)
+    _check_attention(wl, q, k, v, sel, plan, rows)
+    assert np.all(np.isfinite(plan.lse.cpu().numpy()[..., :wl.n_tiles, :]))
 
 
 def test_device_argument_errors():

@@ -34,11 +34,23 @@ _vp, _i32, _i64, _u32, _f = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ct
 class SstaGeom(ctypes.Structure):
     """ssta_geom_t"""
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("batch", "heads", "head_dim", "T", "H", "W", "tile_t", "tile_h", "tile_w")]
+                ("batch", "heads", "head_dim", "T", "H", "W", "tile_t", "tile_h", "tile_w",
+                 "text_len")]
 
     @property
     def n_tokens(self) -> int:
+        """Clip tokens per (batch, head)."""
         return self.T * self.H * self.W
+
+    @property
+    def seq_len(self) -> int:
+        """Tokens per (batch, head) of the token-major tensors: the clip's, then the text's."""
+        return self.n_tokens + self.text_len
+
+    @property
+    def n_rows(self) -> int:
+        """Blocks per (batch, head): the clip's n_tiles, then the text's 128-token blocks."""
+        return self.n_tiles + -(-self.text_len // self.tile_tokens)
 
     @property
     def n_tiles(self) -> int:
@@ -59,6 +71,7 @@ class SstaParams(ctypes.Structure):
 _G = ctypes.POINTER(SstaGeom)
 _P = ctypes.POINTER(SstaParams)
 SIGNATURES = {
+    "ssta_block_rows": (_i64, [_G]),
     "ssta_tile_pool": (ctypes.c_int, [_G, _vp, _vp, _i32, _vp, _vp]),
     "ssta_tile_unpermute": (ctypes.c_int, [_G, _vp, _vp, _vp]),
     "ssta_topk_width": (_i32, [_G, _P]),
@@ -115,8 +128,8 @@ def load():
 
 # ------------------------------------------------------------------ helpers
 
-def make_geom(batch, heads, T, H, W, tile=(2, 8, 8), head_dim=128) -> SstaGeom:
-    return SstaGeom(batch, heads, head_dim, T, H, W, *tile)
+def make_geom(batch, heads, T, H, W, tile=(2, 8, 8), head_dim=128, text_len=0) -> SstaGeom:
+    return SstaGeom(batch, heads, head_dim, T, H, W, *tile, text_len)
 
 
 def make_params(win=(1, 1, 1), topk=0, lambda_=0.9, beta=None, scale=None, flags=0,
@@ -165,10 +178,19 @@ def _call(name, *args):
 
 
 def _tiled_shape(g):
-    return (g.batch, g.heads, g.n_tiles, g.tile_tokens, g.head_dim)
+    """Tile-major copies hold the clip's blocks, then the text's."""
+    return (g.batch, g.heads, g.n_rows, g.tile_tokens, g.head_dim)
 
 
 # ------------------------------------------------------------------ entry points
+
+def ssta_block_rows(g: SstaGeom) -> int:
+    """Blocks per (batch, head): clip blocks, then text blocks."""
+    v = load().ssta_block_rows(ctypes.byref(g))
+    if v < 0:
+        raise SstaError("ssta_block_rows", v)
+    return v
+
 
 def ssta_topk_width(g: SstaGeom, p: SstaParams) -> int:
     v = load().ssta_topk_width(ctypes.byref(g), ctypes.byref(p))
@@ -193,10 +215,10 @@ def ssta_workspace_bytes(g: SstaGeom, p: SstaParams) -> int:
 
 def ssta_tile_pool(g: SstaGeom, x, x_tiled=None, layout=LAYOUT_TOKEN_MAJOR, pooled=None,
                    stream=None):
-    _expect("x", x, (g.batch, g.heads, g.n_tokens, g.head_dim), torch.bfloat16)
+    _expect("x", x, (g.batch, g.heads, g.seq_len, g.head_dim), torch.bfloat16)
     shp = _tiled_shape(g)
     if layout == LAYOUT_DIM_MAJOR:
-        shp = (g.batch, g.heads, g.n_tiles, g.head_dim, g.tile_tokens)
+        shp = (g.batch, g.heads, g.n_rows, g.head_dim, g.tile_tokens)
     _expect("x_tiled", x_tiled, shp, torch.bfloat16, allow_none=True)
     _expect("pooled", pooled, (g.batch, g.heads, g.n_tiles, g.head_dim), torch.float32,
             allow_none=True)
@@ -206,7 +228,7 @@ def ssta_tile_pool(g: SstaGeom, x, x_tiled=None, layout=LAYOUT_TOKEN_MAJOR, pool
 
 def ssta_tile_unpermute(g: SstaGeom, x_tiled, x, stream=None):
     _expect("x_tiled", x_tiled, _tiled_shape(g), torch.bfloat16)
-    _expect("x", x, (g.batch, g.heads, g.n_tokens, g.head_dim), torch.bfloat16)
+    _expect("x", x, (g.batch, g.heads, g.seq_len, g.head_dim), torch.bfloat16)
     _call("ssta_tile_unpermute", ctypes.byref(g), _ptr(x_tiled), _ptr(x), _stream(stream))
 
 
@@ -251,10 +273,10 @@ def ssta_attention_fwd(g: SstaGeom, p: SstaParams, q_t, k_t, v_t, kv_idx, kv_cnt
     """kv_idx = kv_cnt = None runs dense attention (every block kept)."""
     _expect("q_t", q_t, _tiled_shape(g), torch.bfloat16)
     _expect("k_t", k_t, _tiled_shape(g), torch.bfloat16)
-    _expect("v_t", v_t, (g.batch, g.heads, g.n_tiles, g.head_dim, g.tile_tokens),
+    _expect("v_t", v_t, (g.batch, g.heads, g.n_rows, g.head_dim, g.tile_tokens),
             torch.bfloat16)
     _expect("o_t", o_t, _tiled_shape(g), torch.bfloat16)
-    _expect("lse", lse, (g.batch, g.heads, g.n_tiles, g.tile_tokens), torch.float32,
+    _expect("lse", lse, (g.batch, g.heads, g.n_rows, g.tile_tokens), torch.float32,
             allow_none=True)
     if kv_cnt is None:
         if kv_idx is not None:
@@ -272,13 +294,13 @@ def ssta_attention_fwd_tokens(g: SstaGeom, p: SstaParams, q, k, v_t, kv_idx, kv_
                               lse=None, stream=None):
     """Attention with token-major q, k and o (block gathers and output scatter
     inside the kernel); v_t dim-major tiles."""
-    tok = (g.batch, g.heads, g.n_tokens, g.head_dim)
+    tok = (g.batch, g.heads, g.seq_len, g.head_dim)
     _expect("q", q, tok, torch.bfloat16)
     _expect("k", k, tok, torch.bfloat16)
-    _expect("v_t", v_t, (g.batch, g.heads, g.n_tiles, g.head_dim, g.tile_tokens),
+    _expect("v_t", v_t, (g.batch, g.heads, g.n_rows, g.head_dim, g.tile_tokens),
             torch.bfloat16)
     _expect("o", o, tok, torch.bfloat16)
-    _expect("lse", lse, (g.batch, g.heads, g.n_tiles, g.tile_tokens), torch.float32,
+    _expect("lse", lse, (g.batch, g.heads, g.n_rows, g.tile_tokens), torch.float32,
             allow_none=True)
     if kv_cnt is None:
         if kv_idx is not None:
@@ -311,11 +333,11 @@ def ssta_attention_bwd(g: SstaGeom, p: SstaParams, q, k, v, o, dout, lse, kv_idx
                        dv, workspace, stream=None):
     """Gradients of the block-sparse attention with the kept lists fixed; all
     tensors token-major bf16 [B, h, N, 128] except lse (tile-major fp32)."""
-    tok = (g.batch, g.heads, g.n_tokens, g.head_dim)
+    tok = (g.batch, g.heads, g.seq_len, g.head_dim)
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
                     ("dk", dk), ("dv", dv)):
         _expect(name, t, tok, torch.bfloat16)
-    _expect("lse", lse, (g.batch, g.heads, g.n_tiles, g.tile_tokens), torch.float32)
+    _expect("lse", lse, (g.batch, g.heads, g.n_rows, g.tile_tokens), torch.float32)
     if kv_cnt is None:
         if kv_idx is not None:
             raise ValueError("dense attention takes neither kv_idx nor kv_cnt")

@@ -162,31 +162,41 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint8_t* base,
 // Token-major: the rows of the block's tokens; in-block positions are a
 // bit-field code of (t, y, x) offsets, so position 64p + r lies at token
 // offset in_block_offset(64p) + in_block_offset(r) from the block's origin.
-// On a ragged grid, bit r of `valid` says whether position 64p + r of the
-// block exists; a token-major gather redirects the rows that do not to the
-// block's first token (their scores are masked later).
-template <bool kTokK, bool kRagged>
+// kGen (ragged grids, joint text): bit r of `valid` says whether position
+// 64p + r of the block exists; a token-major gather redirects the rows that do
+// not to an existing row (their scores are masked later).  Blocks from n_tiles
+// on are text blocks, whose positions are consecutive tokens after the clip's.
+template <bool kTokK, bool kGen>
 __device__ __forceinline__ void dma_k(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, const Geo& g,
                                       int64_t j, int p, int wave, int lane, uint64_t valid,
                                       const DmaOffsets& off) {
-  const uint32_t so =
+  const bool text = kGen && kTokK && j >= g.n_tiles;
+  uint32_t so =
       kTokK ? (block_origin32(g, (uint32_t)j) + (p ? in_block_offset(g, 64) : 0u)) * 256u
             : (uint32_t)(j * kTileBytes + p * kSlotBytes);
+  if (text) so = (uint32_t)((g.N + (j - g.n_tiles) * kTileTokens + 64 * p) * 256);
 #pragma unroll
   for (int mm = 0; mm < 4; ++mm) {
     uint32_t vo = off.k[mm];
-    if (kRagged && kTokK && valid != ~0ull &&
-        !((valid >> (16 * wave + 4 * mm + (lane >> 4))) & 1u))
-      vo &= 255u;
+    const int r = 16 * wave + 4 * mm + (lane >> 4);
+    if (text) vo = r * 256 + (((lane & 15) ^ (r & 15)) << 4);
+    if (kGen && kTokK && valid != ~0ull && !((valid >> r) & 1u)) vo &= 255u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (4 * wave + mm) * 1024), 16, vo,
                                              so, 0, 0);
   }
 }
 
-// Which of positions 64p .. 64p+63 of block j exist (all, off a ragged grid).
-template <bool kRagged>
+// Which of positions 64p .. 64p+63 of block j exist: all of them unless the
+// block is an edge block of a ragged grid or the last, partial text block.
+template <bool kGen>
 __device__ __forceinline__ uint64_t unit_valid(const Geo& g, int64_t j, int p, int lane) {
-  if (!kRagged) return ~0ull;
+  if (!kGen) return ~0ull;
+  if (j >= g.n_tiles) {
+    const int64_t u0 = (j - g.n_tiles) * kTileTokens + 64 * p;   // first text token
+    if (u0 + 64 <= g.L) return ~0ull;
+    return __ballot(u0 + lane < g.L);
+  }
+  if (!g.ragged) return ~0ull;
   const BlockExtent e = block_extent(g, (uint32_t)j);
   if (e.full) return ~0ull;
   return __ballot(pos_exists(g, e, 64 * p + lane));
@@ -220,12 +230,15 @@ __device__ __forceinline__ void scores(f32x16 (&s)[2], const uint8_t* sK, const 
     }
 }
 
-// kTok: Q, K and O are token-major [B, h, T*H*W, 128] (the query block is
+// kTok: Q, K and O are token-major [B, h, S, 128] (the query block is
 // gathered, the key blocks are gathered by the LDS loads and the output is
 // scattered directly); otherwise Q, K and O are tile-major
-// [B, h, n_tiles, 128, 128].  V is always dim-major tiles: the P.V product
+// [B, h, n_rows, 128, 128].  V is always dim-major tiles: the P.V product
 // needs 8 consecutive keys of one channel per lane.
-template <bool kTok, bool kRagged>
+// kGen: the instance for ragged grids and joint text (masked partial blocks,
+// text blocks always kept, text query blocks dense); grids the block size
+// divides, without text, run the other instance.
+template <bool kTok, bool kGen>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   // K slots at 0 and 16 KB, V^T slots at 32 and 48 KB.
@@ -236,8 +249,9 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   const int64_t xcd = bid & 7, k8 = bid >> 3;
   const int64_t bh = k8 / slice;
   const int64_t qi = xcd * slice + (k8 - bh * slice);
-  if (qi >= g.n_tiles) return;
-  const int64_t row = bh * g.n_tiles + qi;
+  if (qi >= g.n_rows) return;
+  const int64_t row = bh * g.n_rows + qi;        // LSE and tile-major rows
+  const bool qtext = kGen && qi >= g.n_tiles;    // a text query block
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hl = lane >> 5;
@@ -246,25 +260,30 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   constexpr int64_t kTileElems = kTileTokens * kHeadDim;
 
   // qb: this lane's query row is qb + (kTok ? 0 : qrow * 128).  A query
-  // position an edge block of a ragged grid lacks reads the block's first
-  // token instead (its output is not written).
+  // position its block lacks (ragged edge, past the text) reads the block's
+  // first token instead; its output is not written.
   const int qrow = wave * 32 + l32;
   const bool qvalid =
-      (unit_valid<kRagged>(g, qi, wave >> 1, lane) >> (32 * (wave & 1) + l32)) & 1u;
+      (unit_valid<kGen>(g, qi, wave >> 1, lane) >> (32 * (wave & 1) + l32)) & 1u;
+  // token of the query within its head (clip tokens first, then the text)
+  const int64_t qtok =
+      qtext ? g.N + (qi - g.n_tiles) * kTileTokens + (qvalid ? qrow : 0)
+            : block_origin(g, qi) + (qvalid ? in_block_offset(g, qrow) : 0u);
   const uint16_t* qb = static_cast<const uint16_t*>(a.q_t) + row * kTileElems;
-  if (kTok) {
-    // bh * N tokens precede this head; each lane reads its own query row.
-    const uint16_t* qhead = static_cast<const uint16_t*>(a.q_t) + bh * g.N * kHeadDim;
-    qb = qhead + (block_origin(g, qi) + (qvalid ? in_block_offset(g, qrow) : 0u)) * kHeadDim;
-  }
-  // K: token-major (N rows per head) or tile-major (n_tiles blocks per head)
+  // S tokens of each earlier head precede this one in token-major tensors
+  if (kTok) qb = static_cast<const uint16_t*>(a.q_t) + (bh * g.S + qtok) * kHeadDim;
+  // K: token-major (S rows per head) or tile-major (n_rows blocks per head)
   const uint8_t* kb = reinterpret_cast<const uint8_t*>(
-      static_cast<const uint16_t*>(a.k_t) + bh * (kTok ? g.N * kHeadDim : g.n_tiles * kTileElems));
+      static_cast<const uint16_t*>(a.k_t) + bh * (kTok ? g.S * kHeadDim : g.n_rows * kTileElems));
   const uint8_t* vb = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(a.v_t) +
-                                                       bh * g.n_tiles * kTileElems);
-  const bool dense = a.kv_cnt == nullptr;
-  const int cnt = dense ? (int)g.n_tiles : a.kv_cnt[row];
-  const int32_t* idx = dense ? nullptr : a.kv_idx + row * a.max_kept;
+                                                       bh * g.n_rows * kTileElems);
+  // The row's key blocks: the kept list (clip rows), then every text block;
+  // a text query block, or dense attention, takes every block in order.
+  const bool all_blocks = a.kv_cnt == nullptr || qtext;
+  const int64_t kvrow = bh * g.n_tiles + qi;
+  const int listed = all_blocks ? 0 : a.kv_cnt[kvrow];
+  const int cnt = all_blocks ? (int)g.n_rows : listed + (kGen ? g.n_txt : 0);
+  const int32_t* idx = all_blocks ? nullptr : a.kv_idx + kvrow * a.max_kept;
 
   // B operand of S^T = K Q^T: query (32*wave + l32), channels 16*s + 8*hl .. +8.
   bf16x8 qf[8];
@@ -286,28 +305,29 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   // K and V^T rings; unit u+1 is loaded while unit u is computed.
   const int units = 2 * cnt;
   const DmaOffsets doff = dma_offsets<kTok>(g, wv, lane);
-  // token-major K spans N rows of 256 B; tiles span n_tiles x 32 KB
+  // token-major K spans S rows of 256 B; tiles span n_rows x 32 KB
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kb), (short)0,
-                                        (int)(kTok ? g.N * 256 : g.n_tiles * kTileBytes),
+                                        (int)(kTok ? g.S * 256 : g.n_rows * kTileBytes),
                                         0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(vb, g.n_tiles);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(vb, g.n_rows);
   // Kept-block ids, 64 at a time: lane i holds entry ibase + i.
   int ibase = 0;
-  int ids = (!dense && lane < cnt) ? idx[lane] : 0;
+  int ids = (!all_blocks && lane < listed) ? idx[lane] : 0;
   auto block_at = [&](int pos) -> int64_t {
-    if (dense) return pos;
+    if (all_blocks) return pos;
+    if (kGen && pos >= listed) return g.n_tiles + (pos - listed);   // a text block
     if (pos >= ibase + 64) {   // uniform: next 64 entries
       ibase += 64;
-      ids = (ibase + lane < cnt) ? idx[ibase + lane] : 0;
+      ids = (ibase + lane < listed) ? idx[ibase + lane] : 0;
     }
     return __builtin_amdgcn_readlane(ids, pos - ibase);
   };
   uint64_t valid_next = ~0ull;   // positions of the unit loaded last that exist
   if (units > 0) {
     const int64_t j = block_at(0);
-    valid_next = unit_valid<kRagged>(g, j, 0, lane);
-    dma_k<kTok, kRagged>(smem, krs, g, j, 0, wv, lane, valid_next, doff);
+    valid_next = unit_valid<kGen>(g, j, 0, lane);
+    dma_k<kTok, kGen>(smem, krs, g, j, 0, wv, lane, valid_next, doff);
     dma_v(smem + 2 * kSlotBytes, vrs, j, 0, wv, doff);
   }
 
@@ -318,9 +338,9 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
     const uint64_t valid = valid_next;
     if (u + 1 < units) {
       const int64_t j = block_at((u + 1) >> 1);
-      valid_next = unit_valid<kRagged>(g, j, (u + 1) & 1, lane);
-      dma_k<kTok, kRagged>(smem + (1 - slot) * kSlotBytes, krs, g, j, (u + 1) & 1, wv, lane, valid_next,
-                  doff);
+      valid_next = unit_valid<kGen>(g, j, (u + 1) & 1, lane);
+      dma_k<kTok, kGen>(smem + (1 - slot) * kSlotBytes, krs, g, j, (u + 1) & 1, wv, lane,
+                        valid_next, doff);
       dma_v(smem + (3 - slot) * kSlotBytes, vrs, j, (u + 1) & 1, wv, doff);
     }
     const uint8_t* sK = smem + slot * kSlotBytes;
@@ -352,7 +372,7 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
     // Keys an edge block of a ragged grid lacks get a score far below any
     // real one, so their probabilities vanish (position 0 always exists, so
     // a row's first unit has a real key).
-    if (kRagged && valid != ~0ull) {
+    if (kGen && valid != ~0ull) {
       const uint64_t vl = valid >> (8 * hl);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -440,14 +460,12 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   }
 
   // Epilogue: lane holds query qrow, channels 32*db + 8*g4 + 4*hl + (0..3).
-  // A query position a ragged grid lacks has no output row (token order) or a
+  // A query position its block lacks has no output row (token order) or a
   // zero row (tile order), and LSE -inf.
   const float lt = pair_sum(l);
   const float inv = (lt > 0.0f && qvalid) ? 1.0f / lt : 0.0f;
   uint16_t* ob = static_cast<uint16_t*>(a.o_t) + row * kTileElems + qrow * kHeadDim;
-  if (kTok)
-    ob = static_cast<uint16_t*>(a.o_t) +
-         (bh * g.N + block_origin(g, qi) + in_block_offset(g, qrow)) * kHeadDim;
+  if (kTok) ob = static_cast<uint16_t*>(a.o_t) + (bh * g.S + qtok) * kHeadDim;
   if (!kTok || qvalid) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -456,7 +474,7 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
         bf16x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          w[e] = (!kRagged || qvalid) ? (__bf16)(o[db][4 * g4 + e] * inv) : (__bf16)0.0f;
+          w[e] = (!kGen || qvalid) ? (__bf16)(o[db][4 * g4 + e] * inv) : (__bf16)0.0f;
         *reinterpret_cast<bf16x4*>(ob + 32 * db + 8 * g4 + 4 * hl) = w;
       }
   }
@@ -470,15 +488,17 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
 }  // namespace
 
 hipError_t launch_attention(const Geo& g, const AttnArgs& a, hipStream_t s) {
-  const int64_t slice = (g.n_tiles + 7) / 8;
+  const int64_t slice = (g.n_rows + 7) / 8;
   const int64_t blocks = g.bh * slice * 8;
-  // grids the block size divides take the variant without edge-block masking
+  // grids the block size divides, without text, take the instance without
+  // partial-block masking and text blocks
+  const bool gen = g.ragged || g.L > 0;
   const dim3 grid((unsigned)blocks), block(256);
-  if (a.token_io && g.ragged)
+  if (a.token_io && gen)
     hipLaunchKernelGGL((k_attn_fwd<true, true>), grid, block, 0, s, g, a, slice);
   else if (a.token_io)
     hipLaunchKernelGGL((k_attn_fwd<true, false>), grid, block, 0, s, g, a, slice);
-  else if (g.ragged)
+  else if (gen)
     hipLaunchKernelGGL((k_attn_fwd<false, true>), grid, block, 0, s, g, a, slice);
   else
     hipLaunchKernelGGL((k_attn_fwd<false, false>), grid, block, 0, s, g, a, slice);

@@ -13,6 +13,9 @@
 // HBM traffic per block and tensor: 32 KB read + 32 KB written (+512 B of
 // means); the kernel is bound by HBM bandwidth.  Edge blocks of a ragged grid
 // (a grid the block size does not divide) read only the tokens that exist.
+// On a joint video + text sequence the text follows the clip's tokens; tiled
+// copies append its 128-token blocks after the clip's, and only clip blocks
+// are pooled (the text is kept out of scoring).
 #include "ssta_internal.h"
 
 #pragma clang fp contract(off)
@@ -26,26 +29,31 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
 
+// One workgroup per (batch*head, block) over `rows` blocks per head: the clip's
+// n_tiles, then (when a tiled copy is written) the text blocks of a joint
+// sequence.
 __global__ __launch_bounds__(256) void k_tile_pool(Geo g, const uint16_t* __restrict__ x,
                                                    uint16_t* __restrict__ xt, int layout,
-                                                   float* __restrict__ pooled) {
+                                                   float* __restrict__ pooled, int64_t rows) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[kTileTokens * kHeadDim];  // [r][d]
-  const int64_t blk = blockIdx.x;                 // bh * n_tiles + tile
-  const int64_t bh = blk / g.n_tiles, tile = blk % g.n_tiles;
+  const int64_t blk = blockIdx.x;                 // bh * rows + tile
+  const int64_t bh = blk / rows, tile = blk % rows;
   const int t = threadIdx.x;
   const int ch = t & 15;                          // 16-byte chunk = 8 channels
-  const uint16_t* xb = x + bh * g.N * kHeadDim;
-  // An edge block of a ragged grid lacks some positions: they read as zero
-  // and do not enter the mean.
-  const BlockExtent ext = block_extent(g, tile);
+  const uint16_t* xb = x + bh * g.S * kHeadDim;
+  // An edge block of a ragged grid, or the last text block, lacks some
+  // positions: they read as zero and do not enter the mean.
+  const bool text = tile >= g.n_tiles;
+  const int64_t u0 = (tile - g.n_tiles) * kTileTokens;   // text: first text token
+  const BlockExtent ext = block_extent(g, text ? 0u : (uint32_t)tile);
 
   u32x4 v[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
     const int r = (t >> 4) + 16 * m;
-    const bool ok = ext.full || pos_exists(g, ext, r);
-    const int64_t tok = ok ? tile_token(g, tile, r) : 0;   // a real row either way
-    v[m] = *reinterpret_cast<const u32x4*>(xb + tok * kHeadDim + ch * 8);
+    const bool ok = text ? u0 + r < g.L : (ext.full || pos_exists(g, ext, r));
+    const int64_t tok = !ok ? 0 : text ? g.N + u0 + r : tile_token(g, tile, r);
+    v[m] = *reinterpret_cast<const u32x4*>(xb + tok * kHeadDim + ch * 8);   // a real row
     if (!ok) v[m] = u32x4{0u, 0u, 0u, 0u};
   }
   if (xt != nullptr && layout == 0) {
@@ -56,7 +64,8 @@ __global__ __launch_bounds__(256) void k_tile_pool(Geo g, const uint16_t* __rest
       *reinterpret_cast<u32x4*>(ob + r * kHeadDim + ch * 8) = v[m];
     }
   }
-  const bool need_lds = pooled != nullptr || (xt != nullptr && layout == 1);
+  const bool pool_here = pooled != nullptr && !text;   // text blocks have no mean
+  const bool need_lds = pool_here || (xt != nullptr && layout == 1);
   if (!need_lds) return;
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
@@ -64,13 +73,13 @@ __global__ __launch_bounds__(256) void k_tile_pool(Geo g, const uint16_t* __rest
     *reinterpret_cast<u32x4*>(lds + r * kHeadDim + ch * 8) = v[m];
   }
   __syncthreads();
-  if (pooled != nullptr && t < kHeadDim) {
+  if (pool_here && t < kHeadDim) {
     // missing positions hold +0 in LDS, which leaves the running sum exact
     float s = 0.0f;
 #pragma unroll 16
     for (int r = 0; r < kTileTokens; ++r) s = s + bf16_bits_to_f32(lds[r * kHeadDim + t]);
     const int count = ext.full ? kTileTokens : ext.lt * ext.ly * ext.lx;
-    pooled[blk * kHeadDim + t] = s / (float)count;
+    pooled[(bh * g.n_tiles + tile) * kHeadDim + t] = s / (float)count;
   }
   if (xt != nullptr && layout == 1) {
     // dim-major: thread owns channel d and 64 consecutive tokens
@@ -93,13 +102,15 @@ __global__ __launch_bounds__(256) void k_tile_pool(Geo g, const uint16_t* __rest
 
 __global__ __launch_bounds__(256) void k_tile_unpermute(Geo g, const uint16_t* __restrict__ xt,
                                                         uint16_t* __restrict__ x) {
-  const int64_t blk = blockIdx.x;
-  const int64_t bh = blk / g.n_tiles, tile = blk % g.n_tiles;
+  const int64_t blk = blockIdx.x;                 // bh * n_rows + block
+  const int64_t bh = blk / g.n_rows, tile = blk % g.n_rows;
   const int t = threadIdx.x;
   const int ch = t & 15;
   const uint16_t* ib = xt + blk * (int64_t)(kTileTokens * kHeadDim);
-  uint16_t* ob = x + bh * g.N * kHeadDim;
-  const BlockExtent ext = block_extent(g, tile);
+  uint16_t* ob = x + bh * g.S * kHeadDim;
+  const bool text = tile >= g.n_tiles;
+  const int64_t u0 = (tile - g.n_tiles) * kTileTokens;
+  const BlockExtent ext = block_extent(g, text ? 0u : (uint32_t)tile);
   u32x4 v[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
@@ -109,8 +120,9 @@ __global__ __launch_bounds__(256) void k_tile_unpermute(Geo g, const uint16_t* _
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
     const int r = (t >> 4) + 16 * m;
-    if (ext.full || pos_exists(g, ext, r))
-      *reinterpret_cast<u32x4*>(ob + tile_token(g, tile, r) * kHeadDim + ch * 8) = v[m];
+    if (text ? u0 + r < g.L : (ext.full || pos_exists(g, ext, r)))
+      *reinterpret_cast<u32x4*>(ob + (text ? g.N + u0 + r : tile_token(g, tile, r)) * kHeadDim +
+                                ch * 8) = v[m];
   }
 }
 
@@ -118,15 +130,17 @@ __global__ __launch_bounds__(256) void k_tile_unpermute(Geo g, const uint16_t* _
 
 hipError_t launch_tile_pool(const Geo& g, const void* x, void* x_tiled, int layout,
                             float* pooled, hipStream_t s) {
-  const int64_t blocks = g.bh * g.n_tiles;
+  // text blocks are copied, never pooled
+  const int64_t rows = x_tiled != nullptr ? g.n_rows : g.n_tiles;
+  const int64_t blocks = g.bh * rows;
   hipLaunchKernelGGL(k_tile_pool, dim3((unsigned)blocks), dim3(256), 0, s, g,
                      static_cast<const uint16_t*>(x), static_cast<uint16_t*>(x_tiled), layout,
-                     pooled);
+                     pooled, rows);
   return hipGetLastError();
 }
 
 hipError_t launch_tile_unpermute(const Geo& g, const void* x_tiled, void* x, hipStream_t s) {
-  const int64_t blocks = g.bh * g.n_tiles;
+  const int64_t blocks = g.bh * g.n_rows;
   hipLaunchKernelGGL(k_tile_unpermute, dim3((unsigned)blocks), dim3(256), 0, s, g,
                      static_cast<const uint16_t*>(x_tiled), static_cast<uint16_t*>(x));
   return hipGetLastError();

@@ -35,6 +35,7 @@ int check_geom(const ssta_geom_t* g, Geo* out) {
   if (g->batch < 1 || g->heads < 1 || g->head_dim < 1 || g->T < 1 || g->H < 1 || g->W < 1 ||
       g->tile_t < 1 || g->tile_h < 1 || g->tile_w < 1)
     return SSTA_ERR_ARG;
+  if (g->text_len < 0) return SSTA_ERR_ARG;
   if (g->head_dim != ssta::kHeadDim) return SSTA_ERR_SHAPE;
   if ((int64_t)g->tile_t * g->tile_h * g->tile_w != ssta::kTileTokens) return SSTA_ERR_SHAPE;
   const int64_t N = (int64_t)g->T * g->H * g->W;
@@ -45,10 +46,13 @@ int check_geom(const ssta_geom_t* g, Geo* out) {
   const int64_t ny = (g->H + g->tile_h - 1) / g->tile_h;
   const int64_t nx = (g->W + g->tile_w - 1) / g->tile_w;
   const int64_t n = nt * ny * nx;
+  // A joint sequence appends text_len tokens in blocks of 128 after the clip's.
+  const int64_t n_txt = (g->text_len + ssta::kTileTokens - 1) / ssta::kTileTokens;
+  const int64_t S = N + g->text_len, rows = n + n_txt;
   // Every element offset must fit in int64 and every grid in 31 bits.
-  if (N > (int64_t(1) << 40) / bh) return SSTA_ERR_SHAPE;
-  if (bh * n > 0x7FFFFFFF) return SSTA_ERR_SHAPE;
-  if (n > 0x7FFFFFFF / 8) return SSTA_ERR_SHAPE;
+  if (S > (int64_t(1) << 40) / bh) return SSTA_ERR_SHAPE;
+  if (bh * rows > 0x7FFFFFFF) return SSTA_ERR_SHAPE;
+  if (rows > 0x7FFFFFFF / 8) return SSTA_ERR_SHAPE;
   out->batch = g->batch;
   out->heads = g->heads;
   out->D = g->head_dim;
@@ -65,6 +69,10 @@ int check_geom(const ssta_geom_t* g, Geo* out) {
   out->n_tiles = n;
   out->bh = bh;
   out->ragged = (g->T % g->tile_t || g->H % g->tile_h || g->W % g->tile_w) ? 1 : 0;
+  out->L = g->text_len;
+  out->n_txt = (int32_t)n_txt;
+  out->S = S;
+  out->n_rows = rows;
   return SSTA_OK;
 }
 
@@ -197,6 +205,12 @@ int ssta_tile_unpermute(const ssta_geom_t* g, const void* x_tiled, void* x, void
   return hip_status(ssta::launch_tile_unpermute(geo, x_tiled, x, as_stream(stream)));
 }
 
+int64_t ssta_block_rows(const ssta_geom_t* g) {
+  Geo geo;
+  SSTA_TRY(check_geom(g, &geo));
+  return geo.n_rows;
+}
+
 int32_t ssta_topk_width(const ssta_geom_t* g, const ssta_params_t* p) {
   Geo geo;
   SSTA_TRY(check_geom(g, &geo));
@@ -313,7 +327,7 @@ int attention_common(const ssta_geom_t* g, const ssta_params_t* p, const void* q
   SSTA_TRY(check_ptr(lse, true));
   // One head's K (token-major or tiles) and V_t are addressed with 32-bit
   // buffer offsets.
-  if (geo.n_tiles * int64_t(ssta::kTileTokens) * ssta::kHeadDim * 2 > 0x7FFFFFFF)
+  if (geo.n_rows * int64_t(ssta::kTileTokens) * ssta::kHeadDim * 2 > 0x7FFFFFFF)
     return SSTA_ERR_SHAPE;
   const bool dense = kv_cnt == nullptr;
   if (dense) {
@@ -392,6 +406,7 @@ int ssta_attention_bwd(const ssta_geom_t* g, const ssta_params_t* p, const void*
   for (void* ptr : {dq, dk, dv}) SSTA_TRY(check_ptr(ptr, false));
   if (geo.n_tiles * int64_t(ssta::kTileTokens) * ssta::kHeadDim * 2 > 0x7FFFFFFF)
     return SSTA_ERR_SHAPE;
+  if (geo.L > 0) return SSTA_ERR_SHAPE;   // joint text: forward only for now
   const bool dense = kv_cnt == nullptr;
   if (dense) {
     if (kv_idx != nullptr || max_kept_ != 0) return SSTA_ERR_ARG;

@@ -22,6 +22,10 @@ struct Geo {
   int64_t bh;               // batch * heads
   int32_t ragged;           // some axis is not a multiple of its block size: the blocks on
                             // the far edges of that axis hold fewer tokens
+  int32_t L;                // text tokens after the clip's N (joint sequence)
+  int32_t n_txt;            // text blocks: ceil(L / 128), numbered from n_tiles on
+  int64_t S;                // tokens per (batch, head): N + L
+  int64_t n_rows;           // blocks per (batch, head): n_tiles + n_txt
 };
 
 // Maps a linear workgroup id so that the ids one XCD receives (the hardware

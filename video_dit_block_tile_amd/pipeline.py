@@ -15,6 +15,10 @@ With ``fused_io=False`` the block gathers are materialised instead: step 1
 also writes tile-major Q_t and K_t, step 4 is ssta_attention_fwd, and
 ssta_tile_unpermute brings O_t back to token order.  Both give bit-identical O.
 
+A geometry with text_len > 0 describes a joint sequence (the clip's tokens,
+then the text's): the text is kept out of steps 2-3, and step 4 adds every
+text block to each clip row and runs text rows over every block.
+
 (Steps as numbered in the "HunyuanVideo 1.5 Technical Report" summary page,
 section "SSTA: Selective and Sliding Tile Attention".)
 """
@@ -31,17 +35,17 @@ class SstaPlan:
         self.geom, self.params, self.dense, self.fused_io = geom, params, dense, fused_io
         g = geom
         dev = torch.device(device)
-        n, R, D = g.n_tiles, g.tile_tokens, g.head_dim
+        n, nr, R, D = g.n_tiles, g.n_rows, g.tile_tokens, g.head_dim
         bh = (g.batch, g.heads)
         if fused_io:
             self.q_t = self.k_t = self.o_t = None
         else:
-            self.q_t = torch.empty(bh + (n, R, D), dtype=torch.bfloat16, device=dev)
+            self.q_t = torch.empty(bh + (nr, R, D), dtype=torch.bfloat16, device=dev)
             self.k_t = torch.empty_like(self.q_t)
             self.o_t = torch.empty_like(self.q_t)
-        self.v_t = torch.empty(bh + (n, D, R), dtype=torch.bfloat16, device=dev)
-        self.o = torch.empty(bh + (g.n_tokens, D), dtype=torch.bfloat16, device=dev)
-        self.lse = torch.empty(bh + (n, R), dtype=torch.float32, device=dev)
+        self.v_t = torch.empty(bh + (nr, D, R), dtype=torch.bfloat16, device=dev)
+        self.o = torch.empty(bh + (g.seq_len, D), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(bh + (nr, R), dtype=torch.float32, device=dev)
         self.q_pooled = torch.empty(bh + (n, D), dtype=torch.float32, device=dev)
         self.k_pooled = torch.empty_like(self.q_pooled)
         self.width = L.ssta_topk_width(g, params)
@@ -96,7 +100,7 @@ class SstaPlan:
 
     # whole forward --------------------------------------------------------
     def run(self, q, k, v, stream=None):
-        """Enqueue the whole forward; returns (o [B,h,N,D] bf16, lse [B,h,n,R] fp32)."""
+        """Enqueue the whole forward; returns (o [B,h,S,D] bf16, lse [B,h,n_rows,R] fp32)."""
         self.tile_pool(q, k, v, stream)
         if not self.dense:
             self.select(stream)
@@ -107,7 +111,7 @@ class SstaPlan:
 
 def ssta_forward(q, k, v, geom: L.SstaGeom, params: L.SstaParams, dense: bool = False,
                  fused_io: bool = True):
-    """One-shot SSTA forward on bf16 [B, h, T*H*W, 128] device tensors."""
+    """One-shot SSTA forward on bf16 [B, h, T*H*W + text_len, 128] device tensors."""
     plan = SstaPlan(geom, params, device=q.device, dense=dense, fused_io=fused_io)
     o, lse = plan.run(q, k, v)
     return o, lse, plan
