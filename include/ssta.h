@@ -231,16 +231,18 @@ int64_t ssta_attention_bwd_workspace_bytes(const ssta_geom_t* g);
  * section applies SSTA while the model is trained during distillation, so
  * gradients flow through the sparse attention; the block selection is an
  * integer and carries none).  For a query token a and the tokens b of its
- * kept blocks: p_ab = exp(scale q_a.k_b - lse_a), D_a = dO_a.O_a,
+ * kept blocks (on a joint sequence: as in the forward, text blocks always
+ * kept, text query blocks keeping every block):
+ * p_ab = exp(scale q_a.k_b - lse_a), D_a = dO_a.O_a,
  * dS_ab = p_ab (dO_a.v_b - D_a); dq_a = scale sum_b dS_ab k_b,
  * dk_b = scale sum_a dS_ab q_a, dv_b = sum_a p_ab dO_a.
- *   q, k, v, o, dout in : bf16 [batch, heads, T*H*W, head_dim] (token-major);
+ *   q, k, v, o, dout in : bf16 [batch, heads, S, head_dim] (token-major);
  *                         o and lse are the forward's outputs for these inputs.
- *   lse      in : fp32 [batch, heads, n_tiles, tile_tokens] (tile-major, as the
+ *   lse      in : fp32 [batch, heads, n_rows, tile_tokens] (tile-major, as the
  *                 forward writes it).  A query block that keeps nothing gets
  *                 dq = 0 and contributes to no dk, dv.
  *   kv_idx, kv_cnt, max_kept: the forward's kept lists (NULL, NULL, 0: dense).
- *   dq, dk, dv out : bf16 [batch, heads, T*H*W, head_dim] (token-major).
+ *   dq, dk, dv out : bf16 [batch, heads, S, head_dim] (token-major).
  *   workspace: device scratch of ws_bytes >= ssta_attention_bwd_workspace_bytes()
  *              (dim-major copies of K, Q, dO; per-query (lse, D); the transposed
  *              lists).  Caller-owned; contents on return are unspecified.

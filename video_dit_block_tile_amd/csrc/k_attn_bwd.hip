@@ -33,6 +33,12 @@
 // Algorithmic work per kept (query block, key block) pair: five 128^3
 // products (S, dP, dQ, dK, dV) = 21.0 MFLOP; the split recomputes S twice and
 // dP once more, 33.6 MFLOP executed.
+//
+// Joint video + text sequences: blocks from n_tiles on are text blocks of
+// consecutive tokens after the clip's.  A clip query block keeps its list and
+// every text block, a text query block keeps every block; so a clip key
+// block is kept by the query blocks of its transposed list and every text
+// query block, and a text key block by every query block.
 #include "ssta_internal.h"
 
 namespace ssta {
@@ -102,8 +108,18 @@ __device__ __forceinline__ UnitOffsets unit_offsets(const Geo& g, int wave, int 
   }
   return o;
 }
-// Which of positions 32p .. 32p+31 of block j exist (all, off a ragged grid).
+// Which of positions 32p .. 32p+31 of block j exist: all of them unless the
+// block is an edge block of a ragged grid or the last, partial text block.
+// kGen: the kernels' instance for ragged grids and joint text; the other one
+// (grids the block size divides, no text) compiles every such check away.
+template <bool kGen>
 __device__ __forceinline__ uint32_t rows_valid(const Geo& g, uint32_t j, int p, int lane) {
+  if (!kGen) return ~0u;
+  if (j >= g.n_tiles) {
+    const int64_t u0 = (j - g.n_tiles) * kTileTokens + 32 * p;   // first text token
+    if (u0 + 32 <= g.L) return ~0u;
+    return (uint32_t)__ballot(u0 + (lane & 31) < g.L);
+  }
   if (!g.ragged) return ~0u;
   const BlockExtent e = block_extent(g, j);
   if (e.full) return ~0u;
@@ -114,17 +130,22 @@ __device__ __forceinline__ uint32_t rows_valid(const Geo& g, uint32_t j, int p, 
 // whose position does not exist (bit clear in `valid`) is read from the
 // block's first token instead, so every score it enters stays bounded by
 // the row's log-sum-exp; its dim-major column is zero, so it adds nothing.
+// A text block's rows are consecutive tokens.
+template <bool kGen>
 __device__ __forceinline__ void dma_rows(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, const Geo& g,
                                          uint32_t j, int p, int wave, int lane, uint32_t valid,
                                          const UnitOffsets& off) {
-  const bool part = valid != ~0u;
-  const uint32_t half = in_block_offset(g, 32 * p) * 256u;
-  const uint32_t so = block_origin32(g, j) * 256u + (part ? 0u : half);
+  const bool part = kGen && valid != ~0u;
+  const bool text = kGen && j >= g.n_tiles;
+  const uint32_t origin =
+      text ? (uint32_t)(g.N + (j - g.n_tiles) * kTileTokens) : block_origin32(g, j);
+  const uint32_t half = (text ? 32u * p : in_block_offset(g, 32 * p)) * 256u;
+  const uint32_t so = origin * 256u + (part ? 0u : half);
 #pragma unroll
   for (int mm = 0; mm < 2; ++mm) {
-    uint32_t vo = off.rows[mm];
-    if (part)
-      vo = ((valid >> (4 * (2 * wave + mm) + (lane >> 4))) & 1u) ? vo + half : (vo & 255u);
+    const int r = 4 * (2 * wave + mm) + (lane >> 4);
+    uint32_t vo = text ? r * 256 + (((lane & 15) ^ (r & 15)) << 4) : off.rows[mm];
+    if (part) vo = ((valid >> r) & 1u) ? vo + half : (vo & 255u);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (2 * wave + mm) * 1024), 16, vo,
                                              so, 0, 0);
   }
@@ -137,6 +158,14 @@ __device__ __forceinline__ void dma_cols(uint8_t* dst, __amdgpu_buffer_rsrc_t rs
   for (int mm = 0; mm < 2; ++mm)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (2 * wave + mm) * 1024), 16,
                                              off.cols[mm], so, 0, 0);
+}
+
+// Token (within its head) of position r of block j, or of the block's first
+// position when r does not exist.
+template <bool kGen>
+__device__ __forceinline__ int64_t row_token(const Geo& g, int64_t j, int r, bool exists) {
+  if (kGen && j >= g.n_tiles) return g.N + (j - g.n_tiles) * kTileTokens + (exists ? r : 0);
+  return block_origin(g, j) + (exists ? in_block_offset(g, r) : 0u);
 }
 
 // Kept-block ids of one list, 64 at a time (lane i holds entry base + i);
@@ -183,6 +212,7 @@ __device__ __forceinline__ void store_row(uint16_t* row, const f32x16 (&acc)[4],
 
 // ------------------------------------------------------------------ dQ
 
+template <bool kGen>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void k_attn_bwd_dq(Geo g, BwdArgs a, int64_t slice) {
   // slot s (24 KB): K rows | V rows | K^T columns of one 32-key unit
@@ -191,19 +221,19 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, int64_t slice) {
   const int64_t xcd = bid & 7, k8 = bid >> 3;
   const int64_t bh = k8 / slice;
   const int64_t qi = xcd * slice + (k8 - bh * slice);
-  if (qi >= g.n_tiles) return;
-  const int64_t row = bh * g.n_tiles + qi;
+  if (qi >= g.n_rows) return;
+  const int64_t row = bh * g.n_rows + qi;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
   const int kperm = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
   const int qrow = 32 * wv + l32;
-  const int64_t head = bh * g.N;
-  // a query position an edge block lacks reads the block's first token and
+  const int64_t head = bh * g.S;
+  // a query position its block lacks reads the block's first token and
   // stores nothing
-  const bool qvalid = (rows_valid(g, (uint32_t)qi, wv, lane) >> l32) & 1u;
-  const int64_t qtok = head + block_origin(g, qi) + (qvalid ? in_block_offset(g, qrow) : 0u);
+  const bool qvalid = (rows_valid<kGen>(g, (uint32_t)qi, wv, lane) >> l32) & 1u;
+  const int64_t qtok = head + row_token<kGen>(g, qi, qrow, qvalid);
 
   bf16x8 qf[8], df[8];
   load_row_operand(qf, static_cast<const uint16_t*>(a.q) + qtok * kHeadDim, hl);
@@ -218,27 +248,34 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, int64_t slice) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
 
-  const bool dense = a.kv_cnt == nullptr;
-  const int cnt = dense ? (int)g.n_tiles : a.kv_cnt[row];
+  // key blocks: the kept list, then every text block; a text query block
+  // (or dense attention) takes every block
+  const bool all_blocks = a.kv_cnt == nullptr || (kGen && qi >= g.n_tiles);
+  const int64_t kvrow = bh * g.n_tiles + qi;
+  const int listed = all_blocks ? 0 : a.kv_cnt[kvrow];
+  const int cnt = all_blocks ? (int)g.n_rows : listed + (kGen ? g.n_txt : 0);
   IdStream ids;
-  ids.init(dense ? nullptr : a.kv_idx + row * a.max_kept, cnt, dense, lane);
+  ids.init(all_blocks ? nullptr : a.kv_idx + kvrow * a.max_kept, listed, all_blocks, lane);
   const UnitOffsets off = unit_offsets(g, wv, lane);
-  // token-major: N rows of 256 B per head; dim-major: n_tiles blocks of 32 KB
-  const int64_t tok_bytes = g.N * (int64_t)(kHeadDim * 2);
-  const int64_t head_bytes = g.n_tiles * (int64_t)kBlockBytes;
+  // token-major: S rows of 256 B per head; dim-major: n_rows blocks of 32 KB
+  const int64_t tok_bytes = g.S * (int64_t)(kHeadDim * 2);
+  const int64_t head_bytes = g.n_rows * (int64_t)kBlockBytes;
   const __amdgpu_buffer_rsrc_t krs = rsrc(static_cast<const uint16_t*>(a.k) + head * kHeadDim,
                                           tok_bytes);
   const __amdgpu_buffer_rsrc_t vrs = rsrc(static_cast<const uint16_t*>(a.v) + head * kHeadDim,
                                           tok_bytes);
   const __amdgpu_buffer_rsrc_t ktrs = rsrc(
-      static_cast<const uint16_t*>(a.k_cols) + bh * g.n_tiles * (int64_t)kTileTokens * kHeadDim,
+      static_cast<const uint16_t*>(a.k_cols) + bh * g.n_rows * (int64_t)kTileTokens * kHeadDim,
       head_bytes);
   auto load_unit = [&](int u, uint8_t* dst) {
-    const uint32_t j = ids.at(u >> 2, lane);
+    const int pos = u >> 2;
+    const uint32_t j = kGen && pos >= listed && !all_blocks
+                           ? (uint32_t)(g.n_tiles + pos - listed)
+                           : ids.at(pos, lane);
     const int p = u & 3;
-    const uint32_t valid = rows_valid(g, j, p, lane);
-    dma_rows(dst, krs, g, j, p, wv, lane, valid, off);
-    dma_rows(dst + kUnitBytes, vrs, g, j, p, wv, lane, valid, off);
+    const uint32_t valid = rows_valid<kGen>(g, j, p, lane);
+    dma_rows<kGen>(dst, krs, g, j, p, wv, lane, valid, off);
+    dma_rows<kGen>(dst + kUnitBytes, vrs, g, j, p, wv, lane, valid, off);
     dma_cols(dst + 2 * kUnitBytes, ktrs, j, p, wv, off);
   };
 
@@ -291,7 +328,7 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, int64_t slice) {
 // ------------------------------------------------------------------ dV, dK
 
 // kDK = false: dV^T += dO^T P.  kDK = true: dK^T += Q^T dS with dS = P (dP - D).
-template <bool kDK>
+template <bool kDK, bool kGen>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void k_attn_bwd_kv(Geo g, BwdArgs a, int64_t slice) {
   // slot: Q rows | (dK: dO rows) | columns (dV: dO^T, dK: Q^T) | 32 (lse2, D) pairs
@@ -302,19 +339,18 @@ void k_attn_bwd_kv(Geo g, BwdArgs a, int64_t slice) {
   const int64_t xcd = bid & 7, k8 = bid >> 3;
   const int64_t bh = k8 / slice;
   const int64_t kj = xcd * slice + (k8 - bh * slice);
-  if (kj >= g.n_tiles) return;
-  const int64_t krow = bh * g.n_tiles + kj;
+  if (kj >= g.n_rows) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
   const int kperm = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
   const int kr = 32 * wv + l32;                  // this lane's key within the block
-  const int64_t head = bh * g.N;
-  // a key position an edge block lacks reads the block's first token and
-  // stores nothing
-  const bool kvalid = (rows_valid(g, (uint32_t)kj, wv, lane) >> l32) & 1u;
-  const int64_t ktok = head + block_origin(g, kj) + (kvalid ? in_block_offset(g, kr) : 0u);
+  const int64_t head = bh * g.S;
+  // a key position its block lacks reads the block's first token and stores
+  // nothing
+  const bool kvalid = (rows_valid<kGen>(g, (uint32_t)kj, wv, lane) >> l32) & 1u;
+  const int64_t ktok = head + row_token<kGen>(g, kj, kr, kvalid);
 
   // B operands: the wave's 32 keys (and their values for dP).
   bf16x8 kf[8], vf[8];
@@ -328,28 +364,36 @@ void k_attn_bwd_kv(Geo g, BwdArgs a, int64_t slice) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
 
-  const bool dense = a.q_cnt == nullptr;
-  const int cnt = dense ? (int)g.n_tiles : a.q_cnt[krow];
+  // query blocks that keep this key block: its transposed list, then every
+  // text query block; every query block keeps a text key block (and all
+  // keep all under dense attention)
+  const bool all_blocks = a.q_cnt == nullptr || (kGen && kj >= g.n_tiles);
+  const int64_t klist = bh * g.n_tiles + kj;
+  const int listed = all_blocks ? 0 : a.q_cnt[klist];
+  const int cnt = all_blocks ? (int)g.n_rows : listed + (kGen ? g.n_txt : 0);
   IdStream ids;
-  ids.init(dense ? nullptr : a.q_idx + krow * a.q_width, cnt, dense, lane);
+  ids.init(all_blocks ? nullptr : a.q_idx + klist * a.q_width, listed, all_blocks, lane);
   const UnitOffsets off = unit_offsets(g, wv, lane);
-  const int64_t tok_bytes = g.N * (int64_t)(kHeadDim * 2);
-  const int64_t head_bytes = g.n_tiles * (int64_t)kBlockBytes;
+  const int64_t tok_bytes = g.S * (int64_t)(kHeadDim * 2);
+  const int64_t head_bytes = g.n_rows * (int64_t)kBlockBytes;
   const __amdgpu_buffer_rsrc_t qrs = rsrc(static_cast<const uint16_t*>(a.q) + head * kHeadDim,
                                           tok_bytes);
   const __amdgpu_buffer_rsrc_t drs = rsrc(static_cast<const uint16_t*>(a.dout) + head * kHeadDim,
                                           tok_bytes);
-  const int64_t cols_off = bh * g.n_tiles * (int64_t)kTileTokens * kHeadDim;
+  const int64_t cols_off = bh * g.n_rows * (int64_t)kTileTokens * kHeadDim;
   const __amdgpu_buffer_rsrc_t crs =
       rsrc(static_cast<const uint16_t*>(kDK ? a.q_cols : a.dout_cols) + cols_off, head_bytes);
   const __amdgpu_buffer_rsrc_t lrs =
-      rsrc(a.ld + bh * g.n_tiles * kTileTokens * 2, g.n_tiles * kTileTokens * 8);
+      rsrc(a.ld + bh * g.n_rows * kTileTokens * 2, g.n_rows * kTileTokens * 8);
   auto load_unit = [&](int u, uint8_t* dst) {
-    const uint32_t i = ids.at(u >> 2, lane);
+    const int pos = u >> 2;
+    const uint32_t i = kGen && pos >= listed && !all_blocks
+                           ? (uint32_t)(g.n_tiles + pos - listed)
+                           : ids.at(pos, lane);
     const int p = u & 3;
-    const uint32_t valid = rows_valid(g, i, p, lane);
-    dma_rows(dst, qrs, g, i, p, wv, lane, valid, off);
-    if (kDK) dma_rows(dst + kUnitBytes, drs, g, i, p, wv, lane, valid, off);
+    const uint32_t valid = rows_valid<kGen>(g, i, p, lane);
+    dma_rows<kGen>(dst, qrs, g, i, p, wv, lane, valid, off);
+    if (kDK) dma_rows<kGen>(dst + kUnitBytes, drs, g, i, p, wv, lane, valid, off);
     dma_cols(dst + (kParts - 1) * kUnitBytes, crs, i, p, wv, off);
     if (wv == 0 && lane < 16)   // 32 (lse2, D) pairs = 256 B
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -428,10 +472,13 @@ __global__ __launch_bounds__(256) void k_attn_bwd_prep(Geo g, const uint16_t* __
                                                        const uint16_t* __restrict__ dout,
                                                        const float* __restrict__ lse,
                                                        float* __restrict__ ld) {
-  const int64_t blk = blockIdx.x, bh = blk / g.n_tiles, tile = blk % g.n_tiles;
+  const int64_t blk = blockIdx.x, bh = blk / g.n_rows, tile = blk % g.n_rows;
   const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
-  const BlockExtent ext = block_extent(g, (uint32_t)tile);
-  if (!ext.full && !pos_exists(g, ext, r)) {
+  const bool text = tile >= g.n_tiles;
+  const BlockExtent ext = block_extent(g, text ? 0u : (uint32_t)tile);
+  const bool exists =
+      text ? (tile - g.n_tiles) * kTileTokens + r < g.L : (ext.full || pos_exists(g, ext, r));
+  if (!exists) {
     if (half == 0) {
       const int64_t qi = blk * kTileTokens + r;
       ld[qi * 2] = lse[blk * kTileTokens] * kLog2e;
@@ -439,7 +486,8 @@ __global__ __launch_bounds__(256) void k_attn_bwd_prep(Geo g, const uint16_t* __
     }
     return;
   }
-  const int64_t tok = bh * g.N + tile_token(g, tile, r);
+  const int64_t tok =
+      bh * g.S + (text ? g.N + (tile - g.n_tiles) * kTileTokens + r : tile_token(g, tile, r));
   const uint16_t* orow = o + tok * kHeadDim + 64 * half;
   const uint16_t* drow = dout + tok * kHeadDim + 64 * half;
   float acc = 0.0f;
@@ -502,7 +550,7 @@ __global__ __launch_bounds__(256) void k_gather_lists(Geo g, const uint32_t* __r
 
 hipError_t launch_attention_bwd_prep(const Geo& g, const void* o, const void* dout,
                                      const float* lse, float* ld, hipStream_t s) {
-  hipLaunchKernelGGL(k_attn_bwd_prep, dim3((unsigned)(g.bh * g.n_tiles)), dim3(256), 0, s, g,
+  hipLaunchKernelGGL(k_attn_bwd_prep, dim3((unsigned)(g.bh * g.n_rows)), dim3(256), 0, s, g,
                      static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dout), lse,
                      ld);
   return hipGetLastError();
@@ -527,11 +575,18 @@ hipError_t launch_transpose_lists(const Geo& g, const int32_t* kv_idx, const int
 }
 
 hipError_t launch_attention_bwd(const Geo& g, const BwdArgs& a, hipStream_t s) {
-  const int64_t slice = (g.n_tiles + 7) / 8;
+  const int64_t slice = (g.n_rows + 7) / 8;
   const int64_t blocks = g.bh * slice * 8;
-  hipLaunchKernelGGL(k_attn_bwd_dq, dim3((unsigned)blocks), dim3(256), 0, s, g, a, slice);
-  hipLaunchKernelGGL(k_attn_bwd_kv<false>, dim3((unsigned)blocks), dim3(256), 0, s, g, a, slice);
-  hipLaunchKernelGGL(k_attn_bwd_kv<true>, dim3((unsigned)blocks), dim3(256), 0, s, g, a, slice);
+  const dim3 grid((unsigned)blocks), block(256);
+  if (g.ragged || g.L > 0) {   // partial blocks or text blocks
+    hipLaunchKernelGGL((k_attn_bwd_dq<true>), grid, block, 0, s, g, a, slice);
+    hipLaunchKernelGGL((k_attn_bwd_kv<false, true>), grid, block, 0, s, g, a, slice);
+    hipLaunchKernelGGL((k_attn_bwd_kv<true, true>), grid, block, 0, s, g, a, slice);
+  } else {
+    hipLaunchKernelGGL((k_attn_bwd_dq<false>), grid, block, 0, s, g, a, slice);
+    hipLaunchKernelGGL((k_attn_bwd_kv<false, false>), grid, block, 0, s, g, a, slice);
+    hipLaunchKernelGGL((k_attn_bwd_kv<true, false>), grid, block, 0, s, g, a, slice);
+  }
   return hipGetLastError();
 }
 

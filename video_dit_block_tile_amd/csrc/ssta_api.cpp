@@ -373,13 +373,15 @@ struct BwdLayout {
 };
 BwdLayout bwd_layout(const Geo& g) {
   BwdLayout w;
-  const int64_t tensor = g.bh * g.n_tiles * int64_t(ssta::kTileTokens) * ssta::kHeadDim * 2;
+  // dim-major copies and (lse, D) pairs cover every block (text included);
+  // the transposed lists cover the clip's key blocks
+  const int64_t tensor = g.bh * g.n_rows * int64_t(ssta::kTileTokens) * ssta::kHeadDim * 2;
   const int64_t rows = g.bh * g.n_tiles;
   w.k_cols = 0;
   w.q_cols = w.k_cols + align256(tensor);
   w.d_cols = w.q_cols + align256(tensor);
   w.ld = w.d_cols + align256(tensor);
-  w.mask = w.ld + align256(rows * ssta::kTileTokens * 8);
+  w.mask = w.ld + align256(g.bh * g.n_rows * ssta::kTileTokens * 8);
   w.q_idx = w.mask + align256(rows * ((g.n_tiles + 31) / 32) * 4);
   w.q_cnt = w.q_idx + align256(rows * g.n_tiles * 4);
   w.total = w.q_cnt + align256(rows * 4);
@@ -404,9 +406,8 @@ int ssta_attention_bwd(const ssta_geom_t* g, const ssta_params_t* p, const void*
   for (const void* ptr : {q, k, v, o, dout, static_cast<const void*>(lse)})
     SSTA_TRY(check_ptr(ptr, false));
   for (void* ptr : {dq, dk, dv}) SSTA_TRY(check_ptr(ptr, false));
-  if (geo.n_tiles * int64_t(ssta::kTileTokens) * ssta::kHeadDim * 2 > 0x7FFFFFFF)
+  if (geo.n_rows * int64_t(ssta::kTileTokens) * ssta::kHeadDim * 2 > 0x7FFFFFFF)
     return SSTA_ERR_SHAPE;
-  if (geo.L > 0) return SSTA_ERR_SHAPE;   // joint text: forward only for now
   const bool dense = kv_cnt == nullptr;
   if (dense) {
     if (kv_idx != nullptr || max_kept_ != 0) return SSTA_ERR_ARG;
