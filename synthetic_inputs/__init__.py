@@ -100,8 +100,13 @@ class Workload:
         return self.n_tokens + self.text_len
 
     @property
+    def tile_tokens(self) -> int:
+        """Tokens per block (128 for 2x8x8, 64 for 4x4x4)."""
+        return self.tile[0] * self.tile[1] * self.tile[2]
+
+    @property
     def n_text_blocks(self) -> int:
-        return -(-self.text_len // (self.tile[0] * self.tile[1] * self.tile[2]))
+        return -(-self.text_len // self.tile_tokens)
 
     @property
     def n_rows(self) -> int:
@@ -170,7 +175,19 @@ JOINT = {
                               text_len=256),
 }
 
-ALL = {**CONFIGS, **EXTRA, **LATENT, **JOINT}
+# 64-token blocks (4x4x4, the block the pages use as their example): a small grid, a
+# ragged grid with a text tail, and the 720p 10 s clip (top-k 96 selects as many tokens
+# as top-k 48 of 128-token blocks).
+TILE64 = {
+    "t64-grid": Workload("t64-grid", 1, 2, 8, 16, 16, tile=(4, 4, 4), win=(1, 1, 1), topk=3,
+                         seed=24),
+    "t64-partial": Workload("t64-partial", 2, 1, 6, 10, 18, tile=(4, 4, 4), win=(1, 0, 1),
+                            topk=4, seed=25, text_len=70),
+    "720p-10s-t64": Workload("720p-10s-t64", 1, 16, 60, 48, 80, tile=(4, 4, 4), topk=96,
+                             seed=26),
+}
+
+ALL = {**CONFIGS, **EXTRA, **LATENT, **JOINT, **TILE64}
 
 
 def _copy_tiles(x: np.ndarray, wl: Workload) -> None:

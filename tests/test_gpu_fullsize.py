@@ -1,7 +1,8 @@
 """GPU parity at the five measured shapes (tiny, 480p-short, 480p-5s, 720p-5s,
 720p-10s) in the launch configuration the benchmark times (one SstaPlan.run),
 at the 720p 10 s latent grid (61 x 45 x 80), which the 2 x 8 x 8 block
-does not divide, and at 720p 10 s with 256 text tokens after the clip.
+does not divide, at 720p 10 s with 256 text tokens after the clip, and at
+720p 10 s with 64-token (4x4x4) blocks.
 
 Block means, top-k ids, kept lists and counts are compared in full, bit for
 bit.  The attention output is compared on a deterministic sample of rows that
@@ -21,7 +22,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("name", ["tiny", "480p-short", "480p-5s", "720p-5s", "720p-10s",
-                                  "720p-10s-latent", "720p-10s-text"])
+                                  "720p-10s-latent", "720p-10s-text", "720p-10s-t64"])
 def test_full_shape(name):
     import video_dit_block_tile_amd as m
     wl = si.ALL[name]
@@ -46,7 +47,7 @@ def test_full_shape(name):
     mx, mean = compare_o(o_rows(wl, plan.o, rows), o_ref)
     print("[%s] O max-abs %.3e mean-abs %.3e" % (name, mx, mean), flush=True)
     assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS
-    lse = plan.lse.cpu().numpy().reshape(-1, 128)[rows]
+    lse = plan.lse.cpu().numpy().reshape(-1, wl.tile_tokens)[rows]
     check_lse(wl, q, k, rows, lse, lse_ref)
 
 
@@ -66,5 +67,5 @@ def test_dense_shape(name):
     mx, mean = compare_o(o_rows(wl, plan.o, rows), o_ref)
     print("[%s dense] O max-abs %.3e mean-abs %.3e" % (name, mx, mean), flush=True)
     assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS
-    lse = plan.lse.cpu().numpy().reshape(-1, 128)[rows]
+    lse = plan.lse.cpu().numpy().reshape(-1, wl.tile_tokens)[rows]
     check_lse(wl, q, k, rows, lse, lse_ref)

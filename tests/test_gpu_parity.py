@@ -1,8 +1,9 @@
 """GPU parity of every step of the SSTA forward against the CPU oracle, through
 the C ABI, on small workloads that span several blocks, odd block grids,
 batch > 1, exact score ties, window 0, k = 0, k above the block count, and
-grids the block size does not divide (partial edge blocks), and joint video +
-text sequences (text blocks always kept, text query blocks dense).
+grids the block size does not divide (partial edge blocks), joint video +
+text sequences (text blocks always kept, text query blocks dense), and
+64-token (4x4x4) blocks.
 
 Bit-exact: tile copies (both layouts), block means, Score_r, Score_i, top-k
 ids, kept lists, bitmasks.  Within tolerance (tests/_helpers.py): the bf16
@@ -20,7 +21,8 @@ from _helpers import (O_MAX_ABS, O_MEAN_ABS, bits, check_lse, compare_o, geom_of
 pytestmark = pytest.mark.gpu
 
 SMALL = ["tiny", "grid32-w1-k2", "grid32-w0-k3", "grid32-w0-k0", "dup-ties", "ragged", "wide-k",
-         "partial", "partial-x", "joint-tiny", "joint-grid32", "joint-partial"]
+         "partial", "partial-x", "joint-tiny", "joint-grid32", "joint-partial", "t64-grid",
+         "t64-partial"]
 _cache = {}
 
 
@@ -47,9 +49,10 @@ def test_tile_pool_bit_exact(name):
     g = geom_of(wl)
     for x in (q, v):
         xd = to_dev(x)
-        tok = torch.empty(wl.batch, wl.heads, wl.n_rows, 128, 128, dtype=torch.bfloat16,
+        tok = torch.empty(wl.batch, wl.heads, wl.n_rows, wl.tile_tokens, 128, dtype=torch.bfloat16,
                           device="cuda")
-        dim = torch.empty_like(tok)
+        dim = torch.empty(wl.batch, wl.heads, wl.n_rows, 128, wl.tile_tokens,
+                          dtype=torch.bfloat16, device="cuda")
         pooled = torch.empty(wl.batch, wl.heads, wl.n_tiles, 128, dtype=torch.float32,
                              device="cuda")
         m.ssta_tile_pool(g, xd, tok, m.LAYOUT_TOKEN_MAJOR, pooled)
@@ -63,7 +66,7 @@ def test_tile_pool_bit_exact(name):
 
 
 @pytest.mark.parametrize("name", ["tiny", "ragged", "partial", "partial-x", "joint-tiny",
-                                  "joint-partial"])
+                                  "joint-partial", "t64-grid", "t64-partial"])
 def test_unpermute_inverts(name):
     import video_dit_block_tile_amd as m
     wl, q, k, v, sel = _case(name)
@@ -112,7 +115,7 @@ def _check_attention(wl, q, k, v, sel, plan, rows):
     o_ref, lse_ref = oracle.attention(wl, q, k, v, sel["kv_idx"], sel["kv_cnt"], rows)
     mx, mean = compare_o(o_rows(wl, plan.o, rows), o_ref)
     assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS, (mx, mean)
-    lse = plan.lse.cpu().numpy().reshape(-1, 128)[rows]
+    lse = plan.lse.cpu().numpy().reshape(-1, wl.tile_tokens)[rows]
     check_lse(wl, q, k, rows, lse, lse_ref)
     return mx, mean
 
@@ -129,17 +132,18 @@ def test_attention_vs_oracle(name, fused):
     if not fused:
         # the tile-major output holds the same bits as the token-major one
         o_tok = bits(plan.o).reshape(wl.batch * wl.heads, wl.seq_len, 128)
-        o_til = bits(plan.o_t).reshape(-1, 128, 128)
+        o_til = bits(plan.o_t).reshape(-1, wl.tile_tokens, 128)
         for row in rows[:8]:
             bh, i = divmod(int(row), wl.n_rows)
-            toks = np.array([oracle.tile_to_token(wl, i, r) for r in range(128)])
+            toks = np.array([oracle.tile_to_token(wl, i, r) for r in range(wl.tile_tokens)])
             there = toks >= 0        # an edge block of a ragged grid holds zero rows
             assert np.array_equal(o_tok[bh][toks[there]], o_til[row][there])
             assert not o_til[row][~there].any()
 
 
 @pytest.mark.parametrize("name", ["grid32-w1-k2", "ragged", "dup-ties", "wide-k", "partial",
-                                  "partial-x", "joint-tiny", "joint-grid32", "joint-partial"])
+                                  "partial-x", "joint-tiny", "joint-grid32", "joint-partial",
+                                  "t64-grid", "t64-partial"])
 def test_fused_io_matches_materialised(name):
     """Gathering blocks inside the kernel gives the same bits as permuting first."""
     wl, q, k, v, sel = _case(name)
@@ -225,7 +229,7 @@ def test_flag_variants(flags):
     o_t = o_rows(wl, plan.o, rows)
     mx, mean = compare_o(o_t, o_ref)
     assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS
-    lse = plan.lse.cpu().numpy().reshape(-1, 128)
+    lse = plan.lse.cpu().numpy().reshape(-1, wl.tile_tokens)
     check_lse(wl, q, k, rows, lse, lse_ref)
     if flags == oracle.COMBINE_AND | oracle.TOPK_EXCLUDE_WINDOW:
         # selection outside the window intersected with the window: nothing is kept

@@ -9,6 +9,9 @@ block keeps every text token on top of its kept blocks; a text query attends to
 every token.  The references below are written independently of the oracle: the
 token/block map is computed from its definition with numpy, and attention is a
 dense fp64 softmax under a token-level mask (numpy) or PyTorch fp64 autograd.
+
+The same pins run on 64-token blocks (4x4x4, the block size the technical
+report's summary page gives as its example in Step 1), with and without text.
 """
 import numpy as np
 import pytest
@@ -17,7 +20,7 @@ import torch
 import oracle
 import synthetic_inputs as si
 
-JOINT_SMALL = ["joint-tiny", "joint-grid32", "joint-partial"]
+JOINT_SMALL = ["joint-tiny", "joint-grid32", "joint-partial", "t64-grid", "t64-partial"]
 
 
 def _block_map(wl):
@@ -60,7 +63,8 @@ def _rows_to_tokens(wl, x_rows, b, h):
     """Oracle rows of head (b, h) [n_rows, R, ...] -> token order [S, ...]."""
     blk, pos = _block_map(wl)
     bh = b * wl.heads + h
-    x = x_rows.reshape((wl.batch * wl.heads, wl.n_rows, 128) + x_rows.shape[2:])[bh]
+    R = wl.tile[0] * wl.tile[1] * wl.tile[2]
+    x = x_rows.reshape((wl.batch * wl.heads, wl.n_rows, R) + x_rows.shape[2:])[bh]
     return x[blk, pos]
 
 
@@ -97,6 +101,22 @@ def test_all_kept_is_textbook_dense_attention():
         assert np.max(np.abs(got - ref.numpy())) <= 1e-12
 
 
+@pytest.mark.parametrize("name", ["t64-grid", "t64-partial"])
+def test_pool_of_64_token_blocks(name):
+    """Block means over the (existing) tokens of each 4x4x4 block, against an
+    fp64 mean gathered with the numpy block map."""
+    wl = si.ALL[name]
+    q, _, _ = si.make_qkv(wl)
+    blk, _ = _block_map(wl)
+    pooled = oracle.pool(wl, q).astype(np.float64)
+    xf = si.bf16_bits_to_f32(q).astype(np.float64)
+    for b in range(wl.batch):
+        for h in range(wl.heads):
+            for i in range(wl.n_tiles):
+                mean = xf[b, h, :wl.n_tokens][blk[:wl.n_tokens] == i].mean(axis=0)
+                assert np.max(np.abs(pooled[b, h, i] - mean)) <= 1e-5 * max(1.0, np.abs(mean).max())
+
+
 def test_positions_past_the_text_are_empty():
     wl = si.ALL["joint-tiny"]                          # 77 text tokens: one partial block
     q, k, v = si.make_qkv(wl)
@@ -128,11 +148,14 @@ def test_text_is_not_scored(name):
 def test_permute_appends_text_blocks(name):
     wl = si.ALL[name]
     q, _, _ = si.make_qkv(wl)
+    R = wl.tile[0] * wl.tile[1] * wl.tile[2]
     t = oracle.permute(wl, q)
-    assert t.shape == (wl.batch, wl.heads, wl.n_rows, 128, 128)
+    assert t.shape == (wl.batch, wl.heads, wl.n_rows, R, 128)
     clip = oracle.permute(wl.with_(text_len=0), q[:, :, :wl.n_tokens])
     assert np.array_equal(t[:, :, :wl.n_tiles], clip)
-    txt = np.zeros((wl.batch, wl.heads, wl.n_text_blocks * 128, 128), np.uint16)
+    blk, pos = _block_map(wl.with_(text_len=0))
+    assert np.array_equal(clip[:, :, blk, pos], q[:, :, :wl.n_tokens])
+    txt = np.zeros((wl.batch, wl.heads, wl.n_text_blocks * R, 128), np.uint16)
     txt[:, :, :wl.text_len] = q[:, :, wl.n_tokens:]
     assert np.array_equal(t[:, :, wl.n_tiles:].reshape(txt.shape), txt)
 
@@ -149,7 +172,7 @@ def _torch_grads(wl, q, k, v, do, kv_idx, kv_cnt):
     return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
 
 
-@pytest.mark.parametrize("name", ["joint-tiny", "joint-partial"])
+@pytest.mark.parametrize("name", ["joint-tiny", "joint-partial", "t64-grid", "t64-partial"])
 def test_backward_matches_torch_autograd(name):
     wl = si.ALL[name]
     q, k, v = si.make_qkv(wl)

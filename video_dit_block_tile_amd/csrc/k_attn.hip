@@ -59,8 +59,16 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kTileBytes = kTileTokens * kHeadDim * 2;   // 32 KB
-constexpr int kSlotBytes = kTileBytes / 2;               // one unit of 64 keys: 16 KB of K or V^T
+// Blocks hold kR = 128 or 64 tokens; a workgroup has kR/32 waves (32 queries
+// each) and takes a key block in kR/64 units of 64 keys.
+template <int kR>
+struct Blk {
+  static constexpr int kWaves = kR / 32;
+  static constexpr int kLoads = 16 / kWaves;          // 1 KB loads per wave per 16 KB slot
+  static constexpr int kUnits = kR / 64;              // 64-key units per block
+  static constexpr int kBytes = kR * kHeadDim * 2;    // one block of one tensor
+};
+constexpr int kSlotBytes = 16384;                     // one unit of 64 keys: 16 KB of K or V^T
 constexpr unsigned kWaitVm0 = 0x0F70;                    // s_waitcnt vmcnt(0)
 // Scheduling fence that lets vector, scalar and transcendental ALU
 // instructions move across it but keeps matrix, LDS and global memory
@@ -117,45 +125,48 @@ __device__ __forceinline__ uint32_t block_origin32(const Geo& g, uint32_t j) {
 }
 
 // Token offset (from the block's first token) of in-block position r; block
-// sizes are powers of two because their product is 128.
+// sizes are powers of two because their product is 128 or 64.
 __device__ __forceinline__ uint32_t in_block_offset(const Geo& g, int r) {
   const int ltw = __builtin_ctz(g.tw), lth = __builtin_ctz(g.th);
   const int it = r >> (ltw + lth), iy = (r >> ltw) & (g.th - 1), ix = r & (g.tw - 1);
   return (uint32_t)((it * g.H + iy) * g.W + ix);
 }
 
-// Direct global->LDS loads (global_load_lds_dwordx4).  A slot is 16 KB: each
-// of the 4 waves issues 4 instructions of 1 KB; lane i of an instruction lands
+// Direct global->LDS loads (buffer_load_dwordx4 ... lds).  A slot is 16 KB:
+// each wave issues kLoads instructions of 1 KB; lane i of an instruction lands
 // at byte 16*i of its 1 KB destination block, so the source address of each
 // lane is chosen to put the right (swizzled) chunk there.  The per-lane byte
 // offsets depend only on the lane and wave (computed once); the unit base is
 // uniform, so the loads use a scalar base plus a 32-bit lane offset.
+template <int kR>
 struct DmaOffsets {
-  uint32_t k[4], v[4];
+  uint32_t k[Blk<kR>::kLoads], v[Blk<kR>::kLoads];
 };
 
-// kTokK: K is read from token-major [.., T*H*W, 128] memory, so key row r of
-// a unit comes from token in_block_offset(r) of its block (a 256-byte row).
-template <bool kTokK>
-__device__ __forceinline__ DmaOffsets dma_offsets(const Geo& g, int wave, int lane) {
-  DmaOffsets o;
+// kTokK: K is read from token-major [.., S, 128] memory, so key row r of a
+// unit comes from token in_block_offset(r) of its block (a 256-byte row).
+// V^T comes from dim-major tiles whose channel rows hold 2*kR bytes.
+template <bool kTokK, int kR>
+__device__ __forceinline__ DmaOffsets<kR> dma_offsets(const Geo& g, int wave, int lane) {
+  DmaOffsets<kR> o;
 #pragma unroll
-  for (int mm = 0; mm < 4; ++mm) {
-    const int b = 4 * wave + mm;                 // 1 KB destination block
+  for (int mm = 0; mm < Blk<kR>::kLoads; ++mm) {
+    const int b = Blk<kR>::kLoads * wave + mm;   // 1 KB destination block
     const int row = 4 * b + (lane >> 4);         // K: rows 4b .. 4b+3
     const uint32_t src_row = kTokK ? in_block_offset(g, row) : (uint32_t)row;
     o.k[mm] = src_row * 256 + (((lane & 15) ^ (row & 15)) << 4);
     const int d = 8 * b + (lane >> 3);           // V^T: channel rows 8b .. 8b+7
-    o.v[mm] = d * 256 + (((lane & 7) ^ ((d >> 1) & 7)) << 4);
+    o.v[mm] = d * (2 * kR) + (((lane & 7) ^ ((d >> 1) & 7)) << 4);
   }
   return o;
 }
 
-// Buffer resource over one head's K, K_t or V_t (bytes; n_tiles x 32 KB);
+// Buffer resource over one head's K, K_t or V_t (bytes; n_rows blocks);
 // loads beyond num_records return zero instead of touching other memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint8_t* base, int64_t n_tiles) {
+template <int kR>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint8_t* base, int64_t n_rows) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0,
-                                           (int)(n_tiles * kTileBytes), 0x00020000);
+                                           (int)(n_rows * Blk<kR>::kBytes), 0x00020000);
 }
 
 // Half p (keys 64p .. 64p+63) of K block j.  Tile-major: 64 contiguous rows.
@@ -166,33 +177,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint8_t* base,
 // 64p + r of the block exists; a token-major gather redirects the rows that do
 // not to an existing row (their scores are masked later).  Blocks from n_tiles
 // on are text blocks, whose positions are consecutive tokens after the clip's.
-template <bool kTokK, bool kGen>
+template <bool kTokK, bool kGen, int kR>
 __device__ __forceinline__ void dma_k(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, const Geo& g,
                                       int64_t j, int p, int wave, int lane, uint64_t valid,
-                                      const DmaOffsets& off) {
+                                      const DmaOffsets<kR>& off) {
+  constexpr int kL = Blk<kR>::kLoads;
   const bool text = kGen && kTokK && j >= g.n_tiles;
   uint32_t so =
       kTokK ? (block_origin32(g, (uint32_t)j) + (p ? in_block_offset(g, 64) : 0u)) * 256u
-            : (uint32_t)(j * kTileBytes + p * kSlotBytes);
-  if (text) so = (uint32_t)((g.N + (j - g.n_tiles) * kTileTokens + 64 * p) * 256);
+            : (uint32_t)(j * Blk<kR>::kBytes + p * kSlotBytes);
+  if (text) so = (uint32_t)((g.N + (j - g.n_tiles) * kR + 64 * p) * 256);
 #pragma unroll
-  for (int mm = 0; mm < 4; ++mm) {
+  for (int mm = 0; mm < kL; ++mm) {
     uint32_t vo = off.k[mm];
-    const int r = 16 * wave + 4 * mm + (lane >> 4);
+    const int r = 4 * (kL * wave + mm) + (lane >> 4);
     if (text) vo = r * 256 + (((lane & 15) ^ (r & 15)) << 4);
     if (kGen && kTokK && valid != ~0ull && !((valid >> r) & 1u)) vo &= 255u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (4 * wave + mm) * 1024), 16, vo,
-                                             so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (kL * wave + mm) * 1024), 16,
+                                             vo, so, 0, 0);
   }
 }
 
 // Which of positions 64p .. 64p+63 of block j exist: all of them unless the
 // block is an edge block of a ragged grid or the last, partial text block.
-template <bool kGen>
+template <bool kGen, int kR>
 __device__ __forceinline__ uint64_t unit_valid(const Geo& g, int64_t j, int p, int lane) {
   if (!kGen) return ~0ull;
   if (j >= g.n_tiles) {
-    const int64_t u0 = (j - g.n_tiles) * kTileTokens + 64 * p;   // first text token
+    const int64_t u0 = (j - g.n_tiles) * kR + 64 * p;   // first text token
     if (u0 + 64 <= g.L) return ~0ull;
     return __ballot(u0 + lane < g.L);
   }
@@ -201,14 +213,17 @@ __device__ __forceinline__ uint64_t unit_valid(const Geo& g, int64_t j, int p, i
   if (e.full) return ~0ull;
   return __ballot(pos_exists(g, e, 64 * p + lane));
 }
-// Half p of V^T block j: bytes 128p .. 128p+127 of each 256-byte channel row.
+// Unit p of V^T block j: bytes 128p .. 128p+127 of each channel row (offv:
+// the V^T offsets of a DmaOffsets<kR>).
+template <int kR>
 __device__ __forceinline__ void dma_v(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, int64_t j, int p,
-                                      int wave, const DmaOffsets& off) {
-  const uint32_t so = (uint32_t)(j * kTileBytes + p * 128);
+                                      int wave, const uint32_t* offv) {
+  constexpr int kL = Blk<kR>::kLoads;
+  const uint32_t so = (uint32_t)(j * Blk<kR>::kBytes + p * 128);
 #pragma unroll
-  for (int mm = 0; mm < 4; ++mm)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (4 * wave + mm) * 1024), 16,
-                                             off.v[mm], so, 0, 0);
+  for (int mm = 0; mm < kL; ++mm)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (kL * wave + mm) * 1024), 16,
+                                             offv[mm], so, 0, 0);
 }
 
 // S^T for the 64 keys of a K slot: the A operand row of lane l32 is key
@@ -238,8 +253,11 @@ __device__ __forceinline__ void scores(f32x16 (&s)[2], const uint8_t* sK, const 
 // kGen: the instance for ragged grids and joint text (masked partial blocks,
 // text blocks always kept, text query blocks dense); grids the block size
 // divides, without text, run the other instance.
-template <bool kTok, bool kGen>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+// kR: tokens per block (128: 4 waves; 64: 2 waves, one unit per key block).
+// 64-token blocks: 2-wave workgroups hold 64 KB of LDS each, so a SIMD runs one
+// wave of them.
+template <bool kTok, bool kGen, int kR>
+__global__ __launch_bounds__(kR * 2) __attribute__((amdgpu_waves_per_eu(kR == 128 ? 2 : 1)))
 void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   // K slots at 0 and 16 KB, V^T slots at 32 and 48 KB.
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kSlotBytes];
@@ -257,17 +275,18 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   const int l32 = lane & 31, hl = lane >> 5;
   const int kperm = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  constexpr int64_t kTileElems = kTileTokens * kHeadDim;
+  constexpr int64_t kTileElems = kR * kHeadDim;
+  constexpr int kUnits = Blk<kR>::kUnits;
 
   // qb: this lane's query row is qb + (kTok ? 0 : qrow * 128).  A query
   // position its block lacks (ragged edge, past the text) reads the block's
   // first token instead; its output is not written.
   const int qrow = wave * 32 + l32;
   const bool qvalid =
-      (unit_valid<kGen>(g, qi, wave >> 1, lane) >> (32 * (wave & 1) + l32)) & 1u;
+      (unit_valid<kGen, kR>(g, qi, wave >> 1, lane) >> (32 * (wave & 1) + l32)) & 1u;
   // token of the query within its head (clip tokens first, then the text)
   const int64_t qtok =
-      qtext ? g.N + (qi - g.n_tiles) * kTileTokens + (qvalid ? qrow : 0)
+      qtext ? g.N + (qi - g.n_tiles) * kR + (qvalid ? qrow : 0)
             : block_origin(g, qi) + (qvalid ? in_block_offset(g, qrow) : 0u);
   const uint16_t* qb = static_cast<const uint16_t*>(a.q_t) + row * kTileElems;
   // S tokens of each earlier head precede this one in token-major tensors
@@ -301,16 +320,16 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   const float c = a.scale_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // Unit u = keys 64*(u%2) .. of the (u/2)-th kept block, in slot u%2 of the
-  // K and V^T rings; unit u+1 is loaded while unit u is computed.
-  const int units = 2 * cnt;
-  const DmaOffsets doff = dma_offsets<kTok>(g, wv, lane);
+  // Unit u = keys 64*(u%kUnits) .. of the (u/kUnits)-th kept block, in slot
+  // u%2 of the K and V^T rings; unit u+1 is loaded while unit u is computed.
+  const int units = kUnits * cnt;
+  const DmaOffsets<kR> doff = dma_offsets<kTok, kR>(g, wv, lane);
   // token-major K spans S rows of 256 B; tiles span n_rows x 32 KB
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kb), (short)0,
-                                        (int)(kTok ? g.S * 256 : g.n_rows * kTileBytes),
+                                        (int)(kTok ? g.S * 256 : g.n_rows * Blk<kR>::kBytes),
                                         0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(vb, g.n_rows);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc<kR>(vb, g.n_rows);
   // Kept-block ids, 64 at a time: lane i holds entry ibase + i.
   int ibase = 0;
   int ids = (!all_blocks && lane < listed) ? idx[lane] : 0;
@@ -326,9 +345,9 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   uint64_t valid_next = ~0ull;   // positions of the unit loaded last that exist
   if (units > 0) {
     const int64_t j = block_at(0);
-    valid_next = unit_valid<kGen>(g, j, 0, lane);
-    dma_k<kTok, kGen>(smem, krs, g, j, 0, wv, lane, valid_next, doff);
-    dma_v(smem + 2 * kSlotBytes, vrs, j, 0, wv, doff);
+    valid_next = unit_valid<kGen, kR>(g, j, 0, lane);
+    dma_k<kTok, kGen, kR>(smem, krs, g, j, 0, wv, lane, valid_next, doff);
+    dma_v<kR>(smem + 2 * kSlotBytes, vrs, j, 0, wv, doff.v);
   }
 
   for (int u = 0; u < units; ++u) {
@@ -337,11 +356,12 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
     const int slot = u & 1;
     const uint64_t valid = valid_next;
     if (u + 1 < units) {
-      const int64_t j = block_at((u + 1) >> 1);
-      valid_next = unit_valid<kGen>(g, j, (u + 1) & 1, lane);
-      dma_k<kTok, kGen>(smem + (1 - slot) * kSlotBytes, krs, g, j, (u + 1) & 1, wv, lane,
-                        valid_next, doff);
-      dma_v(smem + (3 - slot) * kSlotBytes, vrs, j, (u + 1) & 1, wv, doff);
+      const int64_t j = block_at((u + 1) / kUnits);
+      const int p = (u + 1) % kUnits;
+      valid_next = unit_valid<kGen, kR>(g, j, p, lane);
+      dma_k<kTok, kGen, kR>(smem + (1 - slot) * kSlotBytes, krs, g, j, p, wv, lane, valid_next,
+                            doff);
+      dma_v<kR>(smem + (3 - slot) * kSlotBytes, vrs, j, p, wv, doff.v);
     }
     const uint8_t* sK = smem + slot * kSlotBytes;
     const uint8_t* sV = smem + (2 + slot) * kSlotBytes;
@@ -481,7 +501,7 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
   if (a.lse != nullptr && hl == 0) {
     const float v =
         (lt > 0.0f && qvalid) ? (m + __log2f(lt)) * 0.69314718055994530942f : -INFINITY;
-    a.lse[row * kTileTokens + qrow] = v;
+    a.lse[row * kR + qrow] = v;
   }
 }
 
@@ -493,15 +513,29 @@ hipError_t launch_attention(const Geo& g, const AttnArgs& a, hipStream_t s) {
   // grids the block size divides, without text, take the instance without
   // partial-block masking and text blocks
   const bool gen = g.ragged || g.L > 0;
-  const dim3 grid((unsigned)blocks), block(256);
-  if (a.token_io && gen)
-    hipLaunchKernelGGL((k_attn_fwd<true, true>), grid, block, 0, s, g, a, slice);
-  else if (a.token_io)
-    hipLaunchKernelGGL((k_attn_fwd<true, false>), grid, block, 0, s, g, a, slice);
-  else if (gen)
-    hipLaunchKernelGGL((k_attn_fwd<false, true>), grid, block, 0, s, g, a, slice);
-  else
-    hipLaunchKernelGGL((k_attn_fwd<false, false>), grid, block, 0, s, g, a, slice);
+  const dim3 grid((unsigned)blocks);
+  if (g.R == kSmallTile) {
+    const dim3 block(2 * kSmallTile);
+    if (a.token_io && gen)
+      hipLaunchKernelGGL((k_attn_fwd<true, true, kSmallTile>), grid, block, 0, s, g, a, slice);
+    else if (a.token_io)
+      hipLaunchKernelGGL((k_attn_fwd<true, false, kSmallTile>), grid, block, 0, s, g, a, slice);
+    else if (gen)
+      hipLaunchKernelGGL((k_attn_fwd<false, true, kSmallTile>), grid, block, 0, s, g, a, slice);
+    else
+      hipLaunchKernelGGL((k_attn_fwd<false, false, kSmallTile>), grid, block, 0, s, g, a, slice);
+  } else {
+    const dim3 block(2 * kTileTokens);
+    if (a.token_io && gen)
+      hipLaunchKernelGGL((k_attn_fwd<true, true, kTileTokens>), grid, block, 0, s, g, a, slice);
+    else if (a.token_io)
+      hipLaunchKernelGGL((k_attn_fwd<true, false, kTileTokens>), grid, block, 0, s, g, a, slice);
+    else if (gen)
+      hipLaunchKernelGGL((k_attn_fwd<false, true, kTileTokens>), grid, block, 0, s, g, a, slice);
+    else
+      hipLaunchKernelGGL((k_attn_fwd<false, false, kTileTokens>), grid, block, 0, s, g, a,
+                         slice);
+  }
   return hipGetLastError();
 }
 

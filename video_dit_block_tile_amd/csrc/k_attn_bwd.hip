@@ -50,8 +50,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-constexpr int kBlockBytes = kTileTokens * kHeadDim * 2;   // 32 KB: one block of one tensor
-constexpr int kUnitBytes = kBlockBytes / 4;               // 32 rows, or 32 columns of a tile
+constexpr int kUnitBytes = 8192;                          // 32 rows, or 32 columns of a tile
+// Blocks hold kR = 128 or 64 tokens: a workgroup has kR/32 waves (32 rows of
+// the block each) and streams the other side in kR/32 units of 32 per block.
+template <int kR>
+struct Blk {
+  static constexpr int kWaves = kR / 32;
+  static constexpr int kLoads = 8 / kWaves;           // 1 KB loads per wave per 8 KB unit
+  static constexpr int kUnits = kR / 32;              // 32-row units per block
+  static constexpr int kBytes = kR * kHeadDim * 2;    // one block of one tensor
+};
 constexpr unsigned kWaitVm0 = 0x0F70;                     // s_waitcnt vmcnt(0)
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -91,20 +99,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
                                            0x00020000);
 }
 
-// Per-lane source offsets of this wave's two 1 KB loads of a row unit and of
-// a column unit.
+// Per-lane source offsets of this wave's 1 KB loads of a row unit and of a
+// column unit (dim-major channel rows hold 2*kR bytes).
+template <int kR>
 struct UnitOffsets {
-  uint32_t rows[2], cols[2];
+  uint32_t rows[Blk<kR>::kLoads], cols[Blk<kR>::kLoads];
 };
-__device__ __forceinline__ UnitOffsets unit_offsets(const Geo& g, int wave, int lane) {
-  UnitOffsets o;
+template <int kR>
+__device__ __forceinline__ UnitOffsets<kR> unit_offsets(const Geo& g, int wave, int lane) {
+  UnitOffsets<kR> o;
 #pragma unroll
-  for (int mm = 0; mm < 2; ++mm) {
-    const int b = 2 * wave + mm;                   // 1 KB destination block 0..7
+  for (int mm = 0; mm < Blk<kR>::kLoads; ++mm) {
+    const int b = Blk<kR>::kLoads * wave + mm;     // 1 KB destination block 0..7
     const int row = 4 * b + (lane >> 4);           // token rows 4b .. 4b+3
     o.rows[mm] = in_block_offset(g, row) * 256 + (((lane & 15) ^ (row & 15)) << 4);
     const int d = 16 * b + (lane >> 2);            // channel rows 16b .. 16b+15
-    o.cols[mm] = d * 256 + (((lane & 3) ^ ((d >> 2) & 3)) << 4);
+    o.cols[mm] = d * (2 * kR) + (((lane & 3) ^ ((d >> 2) & 3)) << 4);
   }
   return o;
 }
@@ -112,11 +122,11 @@ __device__ __forceinline__ UnitOffsets unit_offsets(const Geo& g, int wave, int 
 // block is an edge block of a ragged grid or the last, partial text block.
 // kGen: the kernels' instance for ragged grids and joint text; the other one
 // (grids the block size divides, no text) compiles every such check away.
-template <bool kGen>
+template <bool kGen, int kR>
 __device__ __forceinline__ uint32_t rows_valid(const Geo& g, uint32_t j, int p, int lane) {
   if (!kGen) return ~0u;
   if (j >= g.n_tiles) {
-    const int64_t u0 = (j - g.n_tiles) * kTileTokens + 32 * p;   // first text token
+    const int64_t u0 = (j - g.n_tiles) * kR + 32 * p;   // first text token
     if (u0 + 32 <= g.L) return ~0u;
     return (uint32_t)__ballot(u0 + (lane & 31) < g.L);
   }
@@ -131,40 +141,44 @@ __device__ __forceinline__ uint32_t rows_valid(const Geo& g, uint32_t j, int p, 
 // block's first token instead, so every score it enters stays bounded by
 // the row's log-sum-exp; its dim-major column is zero, so it adds nothing.
 // A text block's rows are consecutive tokens.
-template <bool kGen>
+template <bool kGen, int kR>
 __device__ __forceinline__ void dma_rows(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, const Geo& g,
                                          uint32_t j, int p, int wave, int lane, uint32_t valid,
-                                         const UnitOffsets& off) {
+                                         const UnitOffsets<kR>& off) {
+  constexpr int kL = Blk<kR>::kLoads;
   const bool part = kGen && valid != ~0u;
   const bool text = kGen && j >= g.n_tiles;
   const uint32_t origin =
-      text ? (uint32_t)(g.N + (j - g.n_tiles) * kTileTokens) : block_origin32(g, j);
+      text ? (uint32_t)(g.N + (j - g.n_tiles) * kR) : block_origin32(g, j);
   const uint32_t half = (text ? 32u * p : in_block_offset(g, 32 * p)) * 256u;
   const uint32_t so = origin * 256u + (part ? 0u : half);
 #pragma unroll
-  for (int mm = 0; mm < 2; ++mm) {
-    const int r = 4 * (2 * wave + mm) + (lane >> 4);
+  for (int mm = 0; mm < kL; ++mm) {
+    const int r = 4 * (kL * wave + mm) + (lane >> 4);
     uint32_t vo = text ? r * 256 + (((lane & 15) ^ (r & 15)) << 4) : off.rows[mm];
     if (part) vo = ((valid >> r) & 1u) ? vo + half : (vo & 255u);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (2 * wave + mm) * 1024), 16, vo,
-                                             so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (kL * wave + mm) * 1024), 16,
+                                             vo, so, 0, 0);
   }
 }
-// Columns 32p .. 32p+31 of dim-major block j.
+// Columns 32p .. 32p+31 of dim-major block j (offc: the column offsets of a
+// UnitOffsets<kR>).
+template <int kR>
 __device__ __forceinline__ void dma_cols(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, uint32_t j,
-                                         int p, int wave, const UnitOffsets& off) {
-  const uint32_t so = j * (uint32_t)kBlockBytes + 64u * p;
+                                         int p, int wave, const uint32_t* offc) {
+  constexpr int kL = Blk<kR>::kLoads;
+  const uint32_t so = j * (uint32_t)Blk<kR>::kBytes + 64u * p;
 #pragma unroll
-  for (int mm = 0; mm < 2; ++mm)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (2 * wave + mm) * 1024), 16,
-                                             off.cols[mm], so, 0, 0);
+  for (int mm = 0; mm < kL; ++mm)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (kL * wave + mm) * 1024), 16,
+                                             offc[mm], so, 0, 0);
 }
 
 // Token (within its head) of position r of block j, or of the block's first
 // position when r does not exist.
-template <bool kGen>
+template <bool kGen, int kR>
 __device__ __forceinline__ int64_t row_token(const Geo& g, int64_t j, int r, bool exists) {
-  if (kGen && j >= g.n_tiles) return g.N + (j - g.n_tiles) * kTileTokens + (exists ? r : 0);
+  if (kGen && j >= g.n_tiles) return g.N + (j - g.n_tiles) * kR + (exists ? r : 0);
   return block_origin(g, j) + (exists ? in_block_offset(g, r) : 0u);
 }
 
@@ -212,9 +226,10 @@ __device__ __forceinline__ void store_row(uint16_t* row, const f32x16 (&acc)[4],
 
 // ------------------------------------------------------------------ dQ
 
-template <bool kGen>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+template <bool kGen, int kR>
+__global__ __launch_bounds__(kR * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void k_attn_bwd_dq(Geo g, BwdArgs a, int64_t slice) {
+  constexpr int kUnits = Blk<kR>::kUnits;
   // slot s (24 KB): K rows | V rows | K^T columns of one 32-key unit
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 3 * kUnitBytes];
   const int64_t bid = blockIdx.x;
@@ -232,14 +247,14 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, int64_t slice) {
   const int64_t head = bh * g.S;
   // a query position its block lacks reads the block's first token and
   // stores nothing
-  const bool qvalid = (rows_valid<kGen>(g, (uint32_t)qi, wv, lane) >> l32) & 1u;
-  const int64_t qtok = head + row_token<kGen>(g, qi, qrow, qvalid);
+  const bool qvalid = (rows_valid<kGen, kR>(g, (uint32_t)qi, wv, lane) >> l32) & 1u;
+  const int64_t qtok = head + row_token<kGen, kR>(g, qi, qrow, qvalid);
 
   bf16x8 qf[8], df[8];
   load_row_operand(qf, static_cast<const uint16_t*>(a.q) + qtok * kHeadDim, hl);
   load_row_operand(df, static_cast<const uint16_t*>(a.dout) + qtok * kHeadDim, hl);
-  const float lse2 = a.ld[(row * kTileTokens + qrow) * 2];
-  const float dq_d = a.ld[(row * kTileTokens + qrow) * 2 + 1];
+  const float lse2 = a.ld[(row * kR + qrow) * 2];
+  const float dq_d = a.ld[(row * kR + qrow) * 2 + 1];
   const float c = a.scale_log2;
 
   f32x16 acc[4];
@@ -256,30 +271,30 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, int64_t slice) {
   const int cnt = all_blocks ? (int)g.n_rows : listed + (kGen ? g.n_txt : 0);
   IdStream ids;
   ids.init(all_blocks ? nullptr : a.kv_idx + kvrow * a.max_kept, listed, all_blocks, lane);
-  const UnitOffsets off = unit_offsets(g, wv, lane);
-  // token-major: S rows of 256 B per head; dim-major: n_rows blocks of 32 KB
+  const UnitOffsets<kR> off = unit_offsets<kR>(g, wv, lane);
+  // token-major: S rows of 256 B per head; dim-major: n_rows blocks
   const int64_t tok_bytes = g.S * (int64_t)(kHeadDim * 2);
-  const int64_t head_bytes = g.n_rows * (int64_t)kBlockBytes;
+  const int64_t head_bytes = g.n_rows * (int64_t)Blk<kR>::kBytes;
   const __amdgpu_buffer_rsrc_t krs = rsrc(static_cast<const uint16_t*>(a.k) + head * kHeadDim,
                                           tok_bytes);
   const __amdgpu_buffer_rsrc_t vrs = rsrc(static_cast<const uint16_t*>(a.v) + head * kHeadDim,
                                           tok_bytes);
   const __amdgpu_buffer_rsrc_t ktrs = rsrc(
-      static_cast<const uint16_t*>(a.k_cols) + bh * g.n_rows * (int64_t)kTileTokens * kHeadDim,
+      static_cast<const uint16_t*>(a.k_cols) + bh * g.n_rows * (int64_t)kR * kHeadDim,
       head_bytes);
   auto load_unit = [&](int u, uint8_t* dst) {
-    const int pos = u >> 2;
+    const int pos = u / kUnits;
     const uint32_t j = kGen && pos >= listed && !all_blocks
                            ? (uint32_t)(g.n_tiles + pos - listed)
                            : ids.at(pos, lane);
-    const int p = u & 3;
-    const uint32_t valid = rows_valid<kGen>(g, j, p, lane);
-    dma_rows<kGen>(dst, krs, g, j, p, wv, lane, valid, off);
-    dma_rows<kGen>(dst + kUnitBytes, vrs, g, j, p, wv, lane, valid, off);
-    dma_cols(dst + 2 * kUnitBytes, ktrs, j, p, wv, off);
+    const int p = u % kUnits;
+    const uint32_t valid = rows_valid<kGen, kR>(g, j, p, lane);
+    dma_rows<kGen, kR>(dst, krs, g, j, p, wv, lane, valid, off);
+    dma_rows<kGen, kR>(dst + kUnitBytes, vrs, g, j, p, wv, lane, valid, off);
+    dma_cols<kR>(dst + 2 * kUnitBytes, ktrs, j, p, wv, off.cols);
   };
 
-  const int units = 4 * cnt;
+  const int units = kUnits * cnt;
   if (units > 0) load_unit(0, smem);
   for (int u = 0; u < units; ++u) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -328,9 +343,10 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, int64_t slice) {
 // ------------------------------------------------------------------ dV, dK
 
 // kDK = false: dV^T += dO^T P.  kDK = true: dK^T += Q^T dS with dS = P (dP - D).
-template <bool kDK, bool kGen>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+template <bool kDK, bool kGen, int kR>
+__global__ __launch_bounds__(kR * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void k_attn_bwd_kv(Geo g, BwdArgs a, int64_t slice) {
+  constexpr int kUnits = Blk<kR>::kUnits;
   // slot: Q rows | (dK: dO rows) | columns (dV: dO^T, dK: Q^T) | 32 (lse2, D) pairs
   constexpr int kParts = kDK ? 3 : 2;
   constexpr int kSlot = kParts * kUnitBytes + 256;
@@ -349,8 +365,8 @@ void k_attn_bwd_kv(Geo g, BwdArgs a, int64_t slice) {
   const int64_t head = bh * g.S;
   // a key position its block lacks reads the block's first token and stores
   // nothing
-  const bool kvalid = (rows_valid<kGen>(g, (uint32_t)kj, wv, lane) >> l32) & 1u;
-  const int64_t ktok = head + row_token<kGen>(g, kj, kr, kvalid);
+  const bool kvalid = (rows_valid<kGen, kR>(g, (uint32_t)kj, wv, lane) >> l32) & 1u;
+  const int64_t ktok = head + row_token<kGen, kR>(g, kj, kr, kvalid);
 
   // B operands: the wave's 32 keys (and their values for dP).
   bf16x8 kf[8], vf[8];
@@ -373,35 +389,35 @@ void k_attn_bwd_kv(Geo g, BwdArgs a, int64_t slice) {
   const int cnt = all_blocks ? (int)g.n_rows : listed + (kGen ? g.n_txt : 0);
   IdStream ids;
   ids.init(all_blocks ? nullptr : a.q_idx + klist * a.q_width, listed, all_blocks, lane);
-  const UnitOffsets off = unit_offsets(g, wv, lane);
+  const UnitOffsets<kR> off = unit_offsets<kR>(g, wv, lane);
   const int64_t tok_bytes = g.S * (int64_t)(kHeadDim * 2);
-  const int64_t head_bytes = g.n_rows * (int64_t)kBlockBytes;
+  const int64_t head_bytes = g.n_rows * (int64_t)Blk<kR>::kBytes;
   const __amdgpu_buffer_rsrc_t qrs = rsrc(static_cast<const uint16_t*>(a.q) + head * kHeadDim,
                                           tok_bytes);
   const __amdgpu_buffer_rsrc_t drs = rsrc(static_cast<const uint16_t*>(a.dout) + head * kHeadDim,
                                           tok_bytes);
-  const int64_t cols_off = bh * g.n_rows * (int64_t)kTileTokens * kHeadDim;
+  const int64_t cols_off = bh * g.n_rows * (int64_t)kR * kHeadDim;
   const __amdgpu_buffer_rsrc_t crs =
       rsrc(static_cast<const uint16_t*>(kDK ? a.q_cols : a.dout_cols) + cols_off, head_bytes);
   const __amdgpu_buffer_rsrc_t lrs =
-      rsrc(a.ld + bh * g.n_rows * kTileTokens * 2, g.n_rows * kTileTokens * 8);
+      rsrc(a.ld + bh * g.n_rows * kR * 2, g.n_rows * kR * 8);
   auto load_unit = [&](int u, uint8_t* dst) {
-    const int pos = u >> 2;
+    const int pos = u / kUnits;
     const uint32_t i = kGen && pos >= listed && !all_blocks
                            ? (uint32_t)(g.n_tiles + pos - listed)
                            : ids.at(pos, lane);
-    const int p = u & 3;
-    const uint32_t valid = rows_valid<kGen>(g, i, p, lane);
-    dma_rows<kGen>(dst, qrs, g, i, p, wv, lane, valid, off);
-    if (kDK) dma_rows<kGen>(dst + kUnitBytes, drs, g, i, p, wv, lane, valid, off);
-    dma_cols(dst + (kParts - 1) * kUnitBytes, crs, i, p, wv, off);
+    const int p = u % kUnits;
+    const uint32_t valid = rows_valid<kGen, kR>(g, i, p, lane);
+    dma_rows<kGen, kR>(dst, qrs, g, i, p, wv, lane, valid, off);
+    if (kDK) dma_rows<kGen, kR>(dst + kUnitBytes, drs, g, i, p, wv, lane, valid, off);
+    dma_cols<kR>(dst + (kParts - 1) * kUnitBytes, crs, i, p, wv, off.cols);
     if (wv == 0 && lane < 16)   // 32 (lse2, D) pairs = 256 B
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           lrs, (lds_u8*)(dst + kParts * kUnitBytes), 16, (uint32_t)lane * 16,
-          (i * (uint32_t)kTileTokens + 32u * p) * 8u, 0, 0);
+          (i * (uint32_t)kR + 32u * p) * 8u, 0, 0);
   };
 
-  const int units = 4 * cnt;
+  const int units = kUnits * cnt;
   if (units > 0) load_unit(0, smem);
   for (int u = 0; u < units; ++u) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -465,7 +481,8 @@ void k_attn_bwd_kv(Geo g, BwdArgs a, int64_t slice) {
 // ------------------------------------------------------------------ helpers
 
 // (lse * log2 e, D = dO . O) per query, tile-major like the LSE: one
-// workgroup per (batch*head, block), two threads per token (64 channels each).
+// workgroup per (batch*head, block) of 2*R threads, two threads per token (64
+// channels each).
 // A position an edge block of a ragged grid lacks gets the block's first
 // query's lse and D = 0: the products then read that query in its place.
 __global__ __launch_bounds__(256) void k_attn_bwd_prep(Geo g, const uint16_t* __restrict__ o,
@@ -477,17 +494,17 @@ __global__ __launch_bounds__(256) void k_attn_bwd_prep(Geo g, const uint16_t* __
   const bool text = tile >= g.n_tiles;
   const BlockExtent ext = block_extent(g, text ? 0u : (uint32_t)tile);
   const bool exists =
-      text ? (tile - g.n_tiles) * kTileTokens + r < g.L : (ext.full || pos_exists(g, ext, r));
+      text ? (tile - g.n_tiles) * g.R + r < g.L : (ext.full || pos_exists(g, ext, r));
   if (!exists) {
     if (half == 0) {
-      const int64_t qi = blk * kTileTokens + r;
-      ld[qi * 2] = lse[blk * kTileTokens] * kLog2e;
+      const int64_t qi = blk * g.R + r;
+      ld[qi * 2] = lse[blk * g.R] * kLog2e;
       ld[qi * 2 + 1] = 0.0f;
     }
     return;
   }
   const int64_t tok =
-      bh * g.S + (text ? g.N + (tile - g.n_tiles) * kTileTokens + r : tile_token(g, tile, r));
+      bh * g.S + (text ? g.N + (tile - g.n_tiles) * g.R + r : tile_token(g, tile, r));
   const uint16_t* orow = o + tok * kHeadDim + 64 * half;
   const uint16_t* drow = dout + tok * kHeadDim + 64 * half;
   float acc = 0.0f;
@@ -500,7 +517,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_prep(Geo g, const uint16_t* __
   }
   acc += __shfl_xor(acc, 1);
   if (half == 0) {
-    const int64_t qi = blk * kTileTokens + r;
+    const int64_t qi = blk * g.R + r;
     ld[qi * 2] = lse[qi] * kLog2e;
     ld[qi * 2 + 1] = acc;
   }
@@ -550,7 +567,7 @@ __global__ __launch_bounds__(256) void k_gather_lists(Geo g, const uint32_t* __r
 
 hipError_t launch_attention_bwd_prep(const Geo& g, const void* o, const void* dout,
                                      const float* lse, float* ld, hipStream_t s) {
-  hipLaunchKernelGGL(k_attn_bwd_prep, dim3((unsigned)(g.bh * g.n_rows)), dim3(256), 0, s, g,
+  hipLaunchKernelGGL(k_attn_bwd_prep, dim3((unsigned)(g.bh * g.n_rows)), dim3(2 * g.R), 0, s, g,
                      static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dout), lse,
                      ld);
   return hipGetLastError();
@@ -577,15 +594,38 @@ hipError_t launch_transpose_lists(const Geo& g, const int32_t* kv_idx, const int
 hipError_t launch_attention_bwd(const Geo& g, const BwdArgs& a, hipStream_t s) {
   const int64_t slice = (g.n_rows + 7) / 8;
   const int64_t blocks = g.bh * slice * 8;
-  const dim3 grid((unsigned)blocks), block(256);
-  if (g.ragged || g.L > 0) {   // partial blocks or text blocks
-    hipLaunchKernelGGL((k_attn_bwd_dq<true>), grid, block, 0, s, g, a, slice);
-    hipLaunchKernelGGL((k_attn_bwd_kv<false, true>), grid, block, 0, s, g, a, slice);
-    hipLaunchKernelGGL((k_attn_bwd_kv<true, true>), grid, block, 0, s, g, a, slice);
+  const dim3 grid((unsigned)blocks);
+  const bool gen = g.ragged || g.L > 0;   // partial blocks or text blocks
+  if (g.R == kSmallTile) {
+    const dim3 block(2 * kSmallTile);
+    if (gen) {
+      hipLaunchKernelGGL((k_attn_bwd_dq<true, kSmallTile>), grid, block, 0, s, g, a, slice);
+      hipLaunchKernelGGL((k_attn_bwd_kv<false, true, kSmallTile>), grid, block, 0, s, g, a,
+                         slice);
+      hipLaunchKernelGGL((k_attn_bwd_kv<true, true, kSmallTile>), grid, block, 0, s, g, a,
+                         slice);
+    } else {
+      hipLaunchKernelGGL((k_attn_bwd_dq<false, kSmallTile>), grid, block, 0, s, g, a, slice);
+      hipLaunchKernelGGL((k_attn_bwd_kv<false, false, kSmallTile>), grid, block, 0, s, g, a,
+                         slice);
+      hipLaunchKernelGGL((k_attn_bwd_kv<true, false, kSmallTile>), grid, block, 0, s, g, a,
+                         slice);
+    }
   } else {
-    hipLaunchKernelGGL((k_attn_bwd_dq<false>), grid, block, 0, s, g, a, slice);
-    hipLaunchKernelGGL((k_attn_bwd_kv<false, false>), grid, block, 0, s, g, a, slice);
-    hipLaunchKernelGGL((k_attn_bwd_kv<true, false>), grid, block, 0, s, g, a, slice);
+    const dim3 block(2 * kTileTokens);
+    if (gen) {
+      hipLaunchKernelGGL((k_attn_bwd_dq<true, kTileTokens>), grid, block, 0, s, g, a, slice);
+      hipLaunchKernelGGL((k_attn_bwd_kv<false, true, kTileTokens>), grid, block, 0, s, g, a,
+                         slice);
+      hipLaunchKernelGGL((k_attn_bwd_kv<true, true, kTileTokens>), grid, block, 0, s, g, a,
+                         slice);
+    } else {
+      hipLaunchKernelGGL((k_attn_bwd_dq<false, kTileTokens>), grid, block, 0, s, g, a, slice);
+      hipLaunchKernelGGL((k_attn_bwd_kv<false, false, kTileTokens>), grid, block, 0, s, g, a,
+                         slice);
+      hipLaunchKernelGGL((k_attn_bwd_kv<true, false, kTileTokens>), grid, block, 0, s, g, a,
+                         slice);
+    }
   }
   return hipGetLastError();
 }

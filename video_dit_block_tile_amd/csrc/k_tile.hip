@@ -10,8 +10,9 @@
 // fp32 mean (a sequential sum per channel, ascending token order) and the
 // dim-major copy used for V.
 //
-// HBM traffic per block and tensor: 32 KB read + 32 KB written (+512 B of
-// means); the kernel is bound by HBM bandwidth.  Edge blocks of a ragged grid
+// HBM traffic per 128-token block and tensor: 32 KB read + 32 KB written
+// (+512 B of means); the kernel is bound by HBM bandwidth.  Blocks of 64
+// tokens (e.g. 4x4x4) use the same kernel with half the rows per workgroup.  Edge blocks of a ragged grid
 // (a grid the block size does not divide) read only the tokens that exist.
 // On a joint video + text sequence the text follows the clip's tokens; tiled
 // copies append its 128-token blocks after the clip's, and only clip blocks
@@ -31,11 +32,13 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
 
 // One workgroup per (batch*head, block) over `rows` blocks per head: the clip's
 // n_tiles, then (when a tiled copy is written) the text blocks of a joint
-// sequence.
+// sequence.  kR = tokens per block (128 or 64).
+template <int kR>
 __global__ __launch_bounds__(256) void k_tile_pool(Geo g, const uint16_t* __restrict__ x,
                                                    uint16_t* __restrict__ xt, int layout,
                                                    float* __restrict__ pooled, int64_t rows) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kTileTokens * kHeadDim];  // [r][d]
+  constexpr int kM = kR / 16;                     // 16-byte chunks per thread
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kR * kHeadDim];  // [r][d]
   const int64_t blk = blockIdx.x;                 // bh * rows + tile
   const int64_t bh = blk / rows, tile = blk % rows;
   const int t = threadIdx.x;
@@ -44,12 +47,12 @@ __global__ __launch_bounds__(256) void k_tile_pool(Geo g, const uint16_t* __rest
   // An edge block of a ragged grid, or the last text block, lacks some
   // positions: they read as zero and do not enter the mean.
   const bool text = tile >= g.n_tiles;
-  const int64_t u0 = (tile - g.n_tiles) * kTileTokens;   // text: first text token
+  const int64_t u0 = (tile - g.n_tiles) * kR;   // text: first text token
   const BlockExtent ext = block_extent(g, text ? 0u : (uint32_t)tile);
 
-  u32x4 v[8];
+  u32x4 v[kM];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
+  for (int m = 0; m < kM; ++m) {
     const int r = (t >> 4) + 16 * m;
     const bool ok = text ? u0 + r < g.L : (ext.full || pos_exists(g, ext, r));
     const int64_t tok = !ok ? 0 : text ? g.N + u0 + r : tile_token(g, tile, r);
@@ -57,9 +60,9 @@ __global__ __launch_bounds__(256) void k_tile_pool(Geo g, const uint16_t* __rest
     if (!ok) v[m] = u32x4{0u, 0u, 0u, 0u};
   }
   if (xt != nullptr && layout == 0) {
-    uint16_t* ob = xt + blk * (int64_t)(kTileTokens * kHeadDim);
+    uint16_t* ob = xt + blk * (int64_t)(kR * kHeadDim);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < kM; ++m) {
       const int r = (t >> 4) + 16 * m;
       *reinterpret_cast<u32x4*>(ob + r * kHeadDim + ch * 8) = v[m];
     }
@@ -68,7 +71,7 @@ __global__ __launch_bounds__(256) void k_tile_pool(Geo g, const uint16_t* __rest
   const bool need_lds = pool_here || (xt != nullptr && layout == 1);
   if (!need_lds) return;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
+  for (int m = 0; m < kM; ++m) {
     const int r = (t >> 4) + 16 * m;
     *reinterpret_cast<u32x4*>(lds + r * kHeadDim + ch * 8) = v[m];
   }
@@ -77,17 +80,17 @@ __global__ __launch_bounds__(256) void k_tile_pool(Geo g, const uint16_t* __rest
     // missing positions hold +0 in LDS, which leaves the running sum exact
     float s = 0.0f;
 #pragma unroll 16
-    for (int r = 0; r < kTileTokens; ++r) s = s + bf16_bits_to_f32(lds[r * kHeadDim + t]);
-    const int count = ext.full ? kTileTokens : ext.lt * ext.ly * ext.lx;
+    for (int r = 0; r < kR; ++r) s = s + bf16_bits_to_f32(lds[r * kHeadDim + t]);
+    const int count = ext.full ? kR : ext.lt * ext.ly * ext.lx;
     pooled[(bh * g.n_tiles + tile) * kHeadDim + t] = s / (float)count;
   }
   if (xt != nullptr && layout == 1) {
-    // dim-major: thread owns channel d and 64 consecutive tokens
+    // dim-major: thread owns channel d and kR/2 consecutive tokens
     const int d = t & 127;
-    const int r0 = (t >> 7) * 64;
-    uint16_t* ob = xt + blk * (int64_t)(kTileTokens * kHeadDim) + d * kTileTokens + r0;
+    const int r0 = (t >> 7) * (kR / 2);
+    uint16_t* ob = xt + blk * (int64_t)(kR * kHeadDim) + d * kR + r0;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < kR / 16; ++q) {
       u32x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -100,25 +103,27 @@ __global__ __launch_bounds__(256) void k_tile_pool(Geo g, const uint16_t* __rest
   }
 }
 
+template <int kR>
 __global__ __launch_bounds__(256) void k_tile_unpermute(Geo g, const uint16_t* __restrict__ xt,
                                                         uint16_t* __restrict__ x) {
+  constexpr int kM = kR / 16;
   const int64_t blk = blockIdx.x;                 // bh * n_rows + block
   const int64_t bh = blk / g.n_rows, tile = blk % g.n_rows;
   const int t = threadIdx.x;
   const int ch = t & 15;
-  const uint16_t* ib = xt + blk * (int64_t)(kTileTokens * kHeadDim);
+  const uint16_t* ib = xt + blk * (int64_t)(kR * kHeadDim);
   uint16_t* ob = x + bh * g.S * kHeadDim;
   const bool text = tile >= g.n_tiles;
-  const int64_t u0 = (tile - g.n_tiles) * kTileTokens;
+  const int64_t u0 = (tile - g.n_tiles) * kR;
   const BlockExtent ext = block_extent(g, text ? 0u : (uint32_t)tile);
-  u32x4 v[8];
+  u32x4 v[kM];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
+  for (int m = 0; m < kM; ++m) {
     const int r = (t >> 4) + 16 * m;
     v[m] = *reinterpret_cast<const u32x4*>(ib + r * kHeadDim + ch * 8);
   }
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
+  for (int m = 0; m < kM; ++m) {
     const int r = (t >> 4) + 16 * m;
     if (text ? u0 + r < g.L : (ext.full || pos_exists(g, ext, r)))
       *reinterpret_cast<u32x4*>(ob + (text ? g.N + u0 + r : tile_token(g, tile, r)) * kHeadDim +
@@ -133,16 +138,25 @@ hipError_t launch_tile_pool(const Geo& g, const void* x, void* x_tiled, int layo
   // text blocks are copied, never pooled
   const int64_t rows = x_tiled != nullptr ? g.n_rows : g.n_tiles;
   const int64_t blocks = g.bh * rows;
-  hipLaunchKernelGGL(k_tile_pool, dim3((unsigned)blocks), dim3(256), 0, s, g,
-                     static_cast<const uint16_t*>(x), static_cast<uint16_t*>(x_tiled), layout,
-                     pooled, rows);
+  if (g.R == kSmallTile)
+    hipLaunchKernelGGL(k_tile_pool<kSmallTile>, dim3((unsigned)blocks), dim3(256), 0, s, g,
+                       static_cast<const uint16_t*>(x), static_cast<uint16_t*>(x_tiled), layout,
+                       pooled, rows);
+  else
+    hipLaunchKernelGGL(k_tile_pool<kTileTokens>, dim3((unsigned)blocks), dim3(256), 0, s, g,
+                       static_cast<const uint16_t*>(x), static_cast<uint16_t*>(x_tiled), layout,
+                       pooled, rows);
   return hipGetLastError();
 }
 
 hipError_t launch_tile_unpermute(const Geo& g, const void* x_tiled, void* x, hipStream_t s) {
   const int64_t blocks = g.bh * g.n_rows;
-  hipLaunchKernelGGL(k_tile_unpermute, dim3((unsigned)blocks), dim3(256), 0, s, g,
-                     static_cast<const uint16_t*>(x_tiled), static_cast<uint16_t*>(x));
+  if (g.R == kSmallTile)
+    hipLaunchKernelGGL(k_tile_unpermute<kSmallTile>, dim3((unsigned)blocks), dim3(256), 0, s, g,
+                       static_cast<const uint16_t*>(x_tiled), static_cast<uint16_t*>(x));
+  else
+    hipLaunchKernelGGL(k_tile_unpermute<kTileTokens>, dim3((unsigned)blocks), dim3(256), 0, s, g,
+                       static_cast<const uint16_t*>(x_tiled), static_cast<uint16_t*>(x));
   return hipGetLastError();
 }
 

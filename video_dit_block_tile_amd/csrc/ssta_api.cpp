@@ -37,7 +37,8 @@ int check_geom(const ssta_geom_t* g, Geo* out) {
     return SSTA_ERR_ARG;
   if (g->text_len < 0) return SSTA_ERR_ARG;
   if (g->head_dim != ssta::kHeadDim) return SSTA_ERR_SHAPE;
-  if ((int64_t)g->tile_t * g->tile_h * g->tile_w != ssta::kTileTokens) return SSTA_ERR_SHAPE;
+  const int64_t R = (int64_t)g->tile_t * g->tile_h * g->tile_w;
+  if (R != ssta::kTileTokens && R != ssta::kSmallTile) return SSTA_ERR_SHAPE;
   const int64_t N = (int64_t)g->T * g->H * g->W;
   const int64_t bh = (int64_t)g->batch * g->heads;
   // The block grid rounds up: a grid the block size does not divide has
@@ -46,8 +47,8 @@ int check_geom(const ssta_geom_t* g, Geo* out) {
   const int64_t ny = (g->H + g->tile_h - 1) / g->tile_h;
   const int64_t nx = (g->W + g->tile_w - 1) / g->tile_w;
   const int64_t n = nt * ny * nx;
-  // A joint sequence appends text_len tokens in blocks of 128 after the clip's.
-  const int64_t n_txt = (g->text_len + ssta::kTileTokens - 1) / ssta::kTileTokens;
+  // A joint sequence appends text_len tokens in blocks of R after the clip's.
+  const int64_t n_txt = (g->text_len + R - 1) / R;
   const int64_t S = N + g->text_len, rows = n + n_txt;
   // Every element offset must fit in int64 and every grid in 31 bits.
   if (S > (int64_t(1) << 40) / bh) return SSTA_ERR_SHAPE;
@@ -62,6 +63,7 @@ int check_geom(const ssta_geom_t* g, Geo* out) {
   out->tt = g->tile_t;
   out->th = g->tile_h;
   out->tw = g->tile_w;
+  out->R = (int32_t)R;
   out->nt = (int32_t)nt;
   out->ny = (int32_t)ny;
   out->nx = (int32_t)nx;
@@ -327,7 +329,7 @@ int attention_common(const ssta_geom_t* g, const ssta_params_t* p, const void* q
   SSTA_TRY(check_ptr(lse, true));
   // One head's K (token-major or tiles) and V_t are addressed with 32-bit
   // buffer offsets.
-  if (geo.n_rows * int64_t(ssta::kTileTokens) * ssta::kHeadDim * 2 > 0x7FFFFFFF)
+  if (geo.n_rows * int64_t(geo.R) * ssta::kHeadDim * 2 > 0x7FFFFFFF)
     return SSTA_ERR_SHAPE;
   const bool dense = kv_cnt == nullptr;
   if (dense) {
@@ -375,13 +377,13 @@ BwdLayout bwd_layout(const Geo& g) {
   BwdLayout w;
   // dim-major copies and (lse, D) pairs cover every block (text included);
   // the transposed lists cover the clip's key blocks
-  const int64_t tensor = g.bh * g.n_rows * int64_t(ssta::kTileTokens) * ssta::kHeadDim * 2;
+  const int64_t tensor = g.bh * g.n_rows * int64_t(g.R) * ssta::kHeadDim * 2;
   const int64_t rows = g.bh * g.n_tiles;
   w.k_cols = 0;
   w.q_cols = w.k_cols + align256(tensor);
   w.d_cols = w.q_cols + align256(tensor);
   w.ld = w.d_cols + align256(tensor);
-  w.mask = w.ld + align256(g.bh * g.n_rows * ssta::kTileTokens * 8);
+  w.mask = w.ld + align256(g.bh * g.n_rows * g.R * 8);
   w.q_idx = w.mask + align256(rows * ((g.n_tiles + 31) / 32) * 4);
   w.q_cnt = w.q_idx + align256(rows * g.n_tiles * 4);
   w.total = w.q_cnt + align256(rows * 4);
@@ -406,7 +408,7 @@ int ssta_attention_bwd(const ssta_geom_t* g, const ssta_params_t* p, const void*
   for (const void* ptr : {q, k, v, o, dout, static_cast<const void*>(lse)})
     SSTA_TRY(check_ptr(ptr, false));
   for (void* ptr : {dq, dk, dv}) SSTA_TRY(check_ptr(ptr, false));
-  if (geo.n_rows * int64_t(ssta::kTileTokens) * ssta::kHeadDim * 2 > 0x7FFFFFFF)
+  if (geo.n_rows * int64_t(geo.R) * ssta::kHeadDim * 2 > 0x7FFFFFFF)
     return SSTA_ERR_SHAPE;
   const bool dense = kv_cnt == nullptr;
   if (dense) {

@@ -8,7 +8,8 @@
 namespace ssta {
 
 constexpr int kHeadDim = 128;     // channels per head
-constexpr int kTileTokens = 128;  // tokens per 3D block
+constexpr int kTileTokens = 128;  // tokens per 3D block (the default 2x8x8 block)
+constexpr int kSmallTile = 64;    // tokens per block of the smaller shape (e.g. 4x4x4)
 constexpr int kMaxTopkTiles = 4096;
 
 // Geometry with every derived quantity precomputed on the host.
@@ -16,6 +17,7 @@ struct Geo {
   int32_t batch, heads, D;
   int32_t T, H, W;
   int32_t tt, th, tw;       // block size
+  int32_t R;                // tokens per block: 128 or 64
   int32_t nt, ny, nx;       // block grid
   int64_t N;                // tokens per (batch, head)
   int64_t n_tiles;          // blocks per (batch, head)
@@ -23,7 +25,7 @@ struct Geo {
   int32_t ragged;           // some axis is not a multiple of its block size: the blocks on
                             // the far edges of that axis hold fewer tokens
   int32_t L;                // text tokens after the clip's N (joint sequence)
-  int32_t n_txt;            // text blocks: ceil(L / 128), numbered from n_tiles on
+  int32_t n_txt;            // text blocks: ceil(L / R), numbered from n_tiles on
   int64_t S;                // tokens per (batch, head): N + L
   int64_t n_rows;           // blocks per (batch, head): n_tiles + n_txt
 };
