@@ -46,7 +46,6 @@ METRIC = "SSTA fwd effective TFLOP/s on kept blocks (% bf16 MFMA peak) + speedup
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 PEAK_FP32_VECTOR_TFLOPS = 157.3    # MI355X published fp32 vector peak (packed FMA)
-FLOP_PER_PAIR = 4 * 128 ** 3       # Q.K^T and P.V for one 128x128 block pair
 
 
 def parse():
@@ -61,6 +60,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=3,
                     help="timed runs of the attention backward (dq, dk, dv) after the forward")
+    ap.add_argument("--variant-steps", type=int, default=5,
+                    help="timed forward steps of each variant workload (64-token blocks, "
+                         "joint text, ragged latent grid); 0 to skip")
     ap.add_argument("--no-mfma-ceiling", action="store_true",
                     help="skip the sustained bf16 matrix-core rate measurement")
     ap.add_argument("--materialised", action="store_true",
@@ -115,7 +117,7 @@ def cpu_baseline(wl, q, k, v, rows_wanted):
     t = t_att + t_sel * len(rows) / n            # selection prorated to the sampled rows
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {
-        "value": pairs * FLOP_PER_PAIR / t / 1e12,
+        "value": pairs * 4 * wl.tile_tokens ** 2 * 128 / t / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
@@ -162,6 +164,59 @@ def backward_bench(torch, m, si, wl, plan, g, p, qd, kd, vd, pairs, steps):
             "executed_tflops": round(exe / (mean * 1e-3) / 1e12, 2),
             "pct_bf16_peak_executed": round(100 * exe / (mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
             "dout": "seeded synthetic, same field + noise recipe as Q/K/V"}
+
+
+VARIANTS = ("720p-10s-t64", "720p-10s-text", "720p-10s-latent")
+
+
+def block_pairs(wl, plan):
+    """(query block, key block) pairs the attention computes, text pairs
+    included (text blocks are kept by every clip row; text rows keep all)."""
+    n, nt = wl.n_tiles, wl.n_text_blocks
+    return (int(plan.kv_cnt.sum().item()) + wl.batch * wl.heads * (n * nt + nt * (n + nt)))
+
+
+def variant_runs(torch, m, si, steps):
+    """Forward step and attention time of the variant workloads (each in
+    turn: inputs generated, timed, freed).  TFLOP/s counts whole block pairs,
+    4 * R * R * 128 FLOP each (partial edge and text blocks as full)."""
+    import numpy as np
+    out = {}
+    for name in VARIANTS:
+        wl = si.ALL[name]
+        q, k, v = si.make_qkv(wl)
+        dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        qd, kd, vd = dev(q), dev(k), dev(v)
+        g = m.make_geom(wl.batch, wl.heads, wl.T, wl.H, wl.W, tile=wl.tile,
+                        text_len=wl.text_len)
+        p = m.make_params(win=wl.win, topk=wl.topk)
+        plan = m.SstaPlan(g, p)
+        for _ in range(2):
+            plan.run(qd, kd, vd)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for e in ev:
+            e[0].record()
+            plan.tile_pool(qd, kd, vd)
+            plan.select()
+            e[1].record()
+            plan.attend()
+            e[2].record()
+        torch.cuda.synchronize()
+        step = float(np.mean([e[0].elapsed_time(e[2]) for e in ev]))
+        attn = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+        R = wl.tile_tokens
+        pairs = block_pairs(wl, plan)
+        flop = pairs * 4 * R * R * 128
+        out[name] = {"tile": list(wl.tile), "grid": [wl.T, wl.H, wl.W], "text_len": wl.text_len,
+                     "topk": wl.topk, "block_pairs": pairs, "step_ms": round(step, 4),
+                     "attention_ms": round(attn, 4),
+                     "attention_tflops": round(flop / (attn * 1e-3) / 1e12, 2)}
+        print("[bench] variant %s: step %.3f ms, attention %.3f ms (%.1f TFLOP/s)"
+              % (name, step, attn, out[name]["attention_tflops"]), file=sys.stderr, flush=True)
+        del plan, qd, kd, vd
+        torch.cuda.empty_cache()
+    return out
 
 
 def mfma_ceiling(torch, m, iters=160000, reps=3):
@@ -223,7 +278,7 @@ def main():
         return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
 
     qd, kd, vd = dev(q), dev(k), dev(v)
-    g = m.make_geom(wl.batch, wl.heads, wl.T, wl.H, wl.W, tile=wl.tile)
+    g = m.make_geom(wl.batch, wl.heads, wl.T, wl.H, wl.W, tile=wl.tile, text_len=wl.text_len)
     p = m.make_params(win=wl.win, topk=wl.topk)
     fused = not args.materialised
     plan = m.SstaPlan(g, p, fused_io=fused)
@@ -281,10 +336,13 @@ def main():
                 "attention_ms": stats([e[3].elapsed_time(e[4]) for e in ce])}
         del flush
 
-    pairs = int(plan.kv_cnt.sum().item())
+    # block pairs computed (for a joint sequence the text pairs too); each is
+    # 4 * R * R * 128 FLOP (R = tokens per block: 4 * 128^3 at the default block)
+    pairs = block_pairs(wl, plan)
     n = wl.n_tiles
-    total_pairs = wl.batch * wl.heads * n * n
-    flop = pairs * FLOP_PER_PAIR
+    R = wl.tile_tokens
+    total_pairs = wl.batch * wl.heads * wl.n_rows * wl.n_rows
+    flop = pairs * 4 * R * R * 128
     value = flop / (ms_step * 1e-3) / 1e12
     attn_tflops = flop / (phase_ms["attention"] * 1e-3) / 1e12
     print("[bench] sparse step %.3f ms, attention %.3f ms (%.1f TFLOP/s)"
@@ -319,6 +377,8 @@ def main():
               % (backward["ms"]["mean"], backward["algorithmic_tflops"]), file=sys.stderr,
               flush=True)
 
+    variants = variant_runs(torch, m, si, args.variant_steps) if args.variant_steps > 0 else None
+
     ceiling = None if args.no_mfma_ceiling else mfma_ceiling(torch, m)
     if ceiling is not None:
         print("[bench] sustained bf16 MFMA: %.0f TFLOP/s random operands, %.0f constant"
@@ -346,7 +406,7 @@ def main():
     # Algorithmic bytes and VALU work of each phase (what the step must move or
     # compute at minimum; the design doc lists the per-unit figures).
     bh = wl.batch * wl.heads
-    tensor = bh * wl.n_tokens * 128 * 2                 # one of Q, K, V, O in bf16
+    tensor = bh * wl.seq_len * 128 * 2                  # one of Q, K, V, O in bf16
     pooled = bh * n * 128 * 4
     phase_bytes = {
         # read Q, K, V; write V_t (and Q_t, K_t when materialised); write both pooled arrays
@@ -355,8 +415,9 @@ def main():
         "score_select": 2 * pooled + bh * n * plan.width * 4,
         # read the top-k ids, write the kept lists and counts
         "build_mask": bh * n * (plan.width + plan.max_kept + 1) * 4,
-        # each kept pair reads one 32 KB K block and one 32 KB V^T block; Q read, O written once
-        "attention": pairs * 2 * 128 * 128 * 2 + 2 * tensor,
+        # each kept pair reads one K block and one V^T block (32 KB each at 128 tokens);
+        # Q read, O written once
+        "attention": pairs * 2 * R * 128 * 2 + 2 * tensor,
         "unpermute": 0 if fused else 2 * tensor,
     }
     phase_rates = {}
@@ -413,6 +474,7 @@ def main():
         "roofline": roof,
         "mfma_sustained": ceiling,
         "backward": backward,
+        "variants": variants,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

@@ -25,7 +25,9 @@
 // All XCDs therefore work on the same one or two heads at any time, whose K
 // and V (118 MB per head at the 720p 10 s shape) stay resident in the 256 MB
 // MALL, while within an XCD neighbouring query blocks share most of their
-// window blocks in that XCD's L2.
+// window blocks in that XCD's L2.  On a joint sequence the text query blocks,
+// which run over every block, take the first workgroups of the grid, dealt
+// over all XCDs, so they overlap the clip blocks instead of trailing them.
 // Memory: each kept block is processed as two units of 64 keys.  A unit's K
 // rows and V^T columns (16 KB each) go straight from global memory into LDS
 // with buffer_load_dwordx4 ... lds (no register staging) into a two-slot
@@ -258,16 +260,14 @@ __device__ __forceinline__ void scores(f32x16 (&s)[2], const uint8_t* sK, const 
 // wave of them.
 template <bool kTok, bool kGen, int kR>
 __global__ __launch_bounds__(kR * 2) __attribute__((amdgpu_waves_per_eu(kR == 128 ? 2 : 1)))
-void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
+void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
   // K slots at 0 and 16 KB, V^T slots at 32 and 48 KB.
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kSlotBytes];
 
-  // Head-synchronous XCD slices (see the file comment).
-  const int64_t bid = blockIdx.x;
-  const int64_t xcd = bid & 7, k8 = bid >> 3;
-  const int64_t bh = k8 / slice;
-  const int64_t qi = xcd * slice + (k8 - bh * slice);
-  if (qi >= g.n_rows) return;
+  // Text query blocks first, then head-synchronous XCD slices of the clip
+  // blocks (see the file comment and attn_grid).
+  int64_t bh, qi;
+  if (!attn_block<kGen>(g, grid, blockIdx.x, bh, qi)) return;
   const int64_t row = bh * g.n_rows + qi;        // LSE and tile-major rows
   const bool qtext = kGen && qi >= g.n_tiles;    // a text query block
 
@@ -508,8 +508,8 @@ void k_attn_fwd(Geo g, AttnArgs a, int64_t slice) {
 }  // namespace
 
 hipError_t launch_attention(const Geo& g, const AttnArgs& a, hipStream_t s) {
-  const int64_t slice = (g.n_rows + 7) / 8;
-  const int64_t blocks = g.bh * slice * 8;
+  const AttnGrid ag = attn_grid(g);
+  const int64_t blocks = ag.blocks;
   // grids the block size divides, without text, take the instance without
   // partial-block masking and text blocks
   const bool gen = g.ragged || g.L > 0;
@@ -517,24 +517,23 @@ hipError_t launch_attention(const Geo& g, const AttnArgs& a, hipStream_t s) {
   if (g.R == kSmallTile) {
     const dim3 block(2 * kSmallTile);
     if (a.token_io && gen)
-      hipLaunchKernelGGL((k_attn_fwd<true, true, kSmallTile>), grid, block, 0, s, g, a, slice);
+      hipLaunchKernelGGL((k_attn_fwd<true, true, kSmallTile>), grid, block, 0, s, g, a, ag);
     else if (a.token_io)
-      hipLaunchKernelGGL((k_attn_fwd<true, false, kSmallTile>), grid, block, 0, s, g, a, slice);
+      hipLaunchKernelGGL((k_attn_fwd<true, false, kSmallTile>), grid, block, 0, s, g, a, ag);
     else if (gen)
-      hipLaunchKernelGGL((k_attn_fwd<false, true, kSmallTile>), grid, block, 0, s, g, a, slice);
+      hipLaunchKernelGGL((k_attn_fwd<false, true, kSmallTile>), grid, block, 0, s, g, a, ag);
     else
-      hipLaunchKernelGGL((k_attn_fwd<false, false, kSmallTile>), grid, block, 0, s, g, a, slice);
+      hipLaunchKernelGGL((k_attn_fwd<false, false, kSmallTile>), grid, block, 0, s, g, a, ag);
   } else {
     const dim3 block(2 * kTileTokens);
     if (a.token_io && gen)
-      hipLaunchKernelGGL((k_attn_fwd<true, true, kTileTokens>), grid, block, 0, s, g, a, slice);
+      hipLaunchKernelGGL((k_attn_fwd<true, true, kTileTokens>), grid, block, 0, s, g, a, ag);
     else if (a.token_io)
-      hipLaunchKernelGGL((k_attn_fwd<true, false, kTileTokens>), grid, block, 0, s, g, a, slice);
+      hipLaunchKernelGGL((k_attn_fwd<true, false, kTileTokens>), grid, block, 0, s, g, a, ag);
     else if (gen)
-      hipLaunchKernelGGL((k_attn_fwd<false, true, kTileTokens>), grid, block, 0, s, g, a, slice);
+      hipLaunchKernelGGL((k_attn_fwd<false, true, kTileTokens>), grid, block, 0, s, g, a, ag);
     else
-      hipLaunchKernelGGL((k_attn_fwd<false, false, kTileTokens>), grid, block, 0, s, g, a,
-                         slice);
+      hipLaunchKernelGGL((k_attn_fwd<false, false, kTileTokens>), grid, block, 0, s, g, a, ag);
   }
   return hipGetLastError();
 }

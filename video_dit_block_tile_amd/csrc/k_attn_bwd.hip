@@ -228,15 +228,12 @@ __device__ __forceinline__ void store_row(uint16_t* row, const f32x16 (&acc)[4],
 
 template <bool kGen, int kR>
 __global__ __launch_bounds__(kR * 2) __attribute__((amdgpu_waves_per_eu(2)))
-void k_attn_bwd_dq(Geo g, BwdArgs a, int64_t slice) {
+void k_attn_bwd_dq(Geo g, BwdArgs a, AttnGrid grid) {
   constexpr int kUnits = Blk<kR>::kUnits;
   // slot s (24 KB): K rows | V rows | K^T columns of one 32-key unit
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 3 * kUnitBytes];
-  const int64_t bid = blockIdx.x;
-  const int64_t xcd = bid & 7, k8 = bid >> 3;
-  const int64_t bh = k8 / slice;
-  const int64_t qi = xcd * slice + (k8 - bh * slice);
-  if (qi >= g.n_rows) return;
+  int64_t bh, qi;
+  if (!attn_block<kGen>(g, grid, blockIdx.x, bh, qi)) return;
   const int64_t row = bh * g.n_rows + qi;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -345,17 +342,15 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, int64_t slice) {
 // kDK = false: dV^T += dO^T P.  kDK = true: dK^T += Q^T dS with dS = P (dP - D).
 template <bool kDK, bool kGen, int kR>
 __global__ __launch_bounds__(kR * 2) __attribute__((amdgpu_waves_per_eu(2)))
-void k_attn_bwd_kv(Geo g, BwdArgs a, int64_t slice) {
+void k_attn_bwd_kv(Geo g, BwdArgs a, AttnGrid grid) {
   constexpr int kUnits = Blk<kR>::kUnits;
   // slot: Q rows | (dK: dO rows) | columns (dV: dO^T, dK: Q^T) | 32 (lse2, D) pairs
   constexpr int kParts = kDK ? 3 : 2;
   constexpr int kSlot = kParts * kUnitBytes + 256;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kSlot];
-  const int64_t bid = blockIdx.x;
-  const int64_t xcd = bid & 7, k8 = bid >> 3;
-  const int64_t bh = k8 / slice;
-  const int64_t kj = xcd * slice + (k8 - bh * slice);
-  if (kj >= g.n_rows) return;
+  // text key blocks (kept by every query block) first, then XCD slices
+  int64_t bh, kj;
+  if (!attn_block<kGen>(g, grid, blockIdx.x, bh, kj)) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -592,39 +587,31 @@ hipError_t launch_transpose_lists(const Geo& g, const int32_t* kv_idx, const int
 }
 
 hipError_t launch_attention_bwd(const Geo& g, const BwdArgs& a, hipStream_t s) {
-  const int64_t slice = (g.n_rows + 7) / 8;
-  const int64_t blocks = g.bh * slice * 8;
+  const AttnGrid ag = attn_grid(g);
+  const int64_t blocks = ag.blocks;
   const dim3 grid((unsigned)blocks);
   const bool gen = g.ragged || g.L > 0;   // partial blocks or text blocks
   if (g.R == kSmallTile) {
     const dim3 block(2 * kSmallTile);
     if (gen) {
-      hipLaunchKernelGGL((k_attn_bwd_dq<true, kSmallTile>), grid, block, 0, s, g, a, slice);
-      hipLaunchKernelGGL((k_attn_bwd_kv<false, true, kSmallTile>), grid, block, 0, s, g, a,
-                         slice);
-      hipLaunchKernelGGL((k_attn_bwd_kv<true, true, kSmallTile>), grid, block, 0, s, g, a,
-                         slice);
+      hipLaunchKernelGGL((k_attn_bwd_dq<true, kSmallTile>), grid, block, 0, s, g, a, ag);
+      hipLaunchKernelGGL((k_attn_bwd_kv<false, true, kSmallTile>), grid, block, 0, s, g, a, ag);
+      hipLaunchKernelGGL((k_attn_bwd_kv<true, true, kSmallTile>), grid, block, 0, s, g, a, ag);
     } else {
-      hipLaunchKernelGGL((k_attn_bwd_dq<false, kSmallTile>), grid, block, 0, s, g, a, slice);
-      hipLaunchKernelGGL((k_attn_bwd_kv<false, false, kSmallTile>), grid, block, 0, s, g, a,
-                         slice);
-      hipLaunchKernelGGL((k_attn_bwd_kv<true, false, kSmallTile>), grid, block, 0, s, g, a,
-                         slice);
+      hipLaunchKernelGGL((k_attn_bwd_dq<false, kSmallTile>), grid, block, 0, s, g, a, ag);
+      hipLaunchKernelGGL((k_attn_bwd_kv<false, false, kSmallTile>), grid, block, 0, s, g, a, ag);
+      hipLaunchKernelGGL((k_attn_bwd_kv<true, false, kSmallTile>), grid, block, 0, s, g, a, ag);
     }
   } else {
     const dim3 block(2 * kTileTokens);
     if (gen) {
-      hipLaunchKernelGGL((k_attn_bwd_dq<true, kTileTokens>), grid, block, 0, s, g, a, slice);
-      hipLaunchKernelGGL((k_attn_bwd_kv<false, true, kTileTokens>), grid, block, 0, s, g, a,
-                         slice);
-      hipLaunchKernelGGL((k_attn_bwd_kv<true, true, kTileTokens>), grid, block, 0, s, g, a,
-                         slice);
+      hipLaunchKernelGGL((k_attn_bwd_dq<true, kTileTokens>), grid, block, 0, s, g, a, ag);
+      hipLaunchKernelGGL((k_attn_bwd_kv<false, true, kTileTokens>), grid, block, 0, s, g, a, ag);
+      hipLaunchKernelGGL((k_attn_bwd_kv<true, true, kTileTokens>), grid, block, 0, s, g, a, ag);
     } else {
-      hipLaunchKernelGGL((k_attn_bwd_dq<false, kTileTokens>), grid, block, 0, s, g, a, slice);
-      hipLaunchKernelGGL((k_attn_bwd_kv<false, false, kTileTokens>), grid, block, 0, s, g, a,
-                         slice);
-      hipLaunchKernelGGL((k_attn_bwd_kv<true, false, kTileTokens>), grid, block, 0, s, g, a,
-                         slice);
+      hipLaunchKernelGGL((k_attn_bwd_dq<false, kTileTokens>), grid, block, 0, s, g, a, ag);
+      hipLaunchKernelGGL((k_attn_bwd_kv<false, false, kTileTokens>), grid, block, 0, s, g, a, ag);
+      hipLaunchKernelGGL((k_attn_bwd_kv<true, false, kTileTokens>), grid, block, 0, s, g, a, ag);
     }
   }
   return hipGetLastError();

@@ -30,6 +30,41 @@ struct Geo {
   int64_t n_rows;           // blocks per (batch, head): n_tiles + n_txt
 };
 
+// Grid of the attention kernels (forward and backward): first one workgroup
+// per (batch*head, text block) of a joint sequence -- each runs over every
+// block, many times a clip block's work -- dealt round-robin over the XCDs so
+// they overlap everything else; then the clip blocks in head-synchronous XCD
+// slices: XCD x takes, head after head, blocks [x*slice, (x+1)*slice).  The
+// text part is padded to a multiple of 8 workgroups so every slice keeps its
+// XCD (the hardware deals workgroup ids round-robin over the 8 XCDs).
+struct AttnGrid {
+  int64_t text_wgs;   // workgroups of the text blocks (multiple of 8)
+  int64_t slice;      // clip blocks per XCD per head
+  int64_t blocks;     // total workgroups
+};
+inline AttnGrid attn_grid(const Geo& g) {
+  AttnGrid a;
+  a.text_wgs = (g.bh * g.n_txt + 7) / 8 * 8;
+  a.slice = (g.n_tiles + 7) / 8;
+  a.blocks = a.text_wgs + g.bh * a.slice * 8;
+  return a;
+}
+// (batch*head, block) of workgroup bid; false for the padding workgroups.
+// kText = false: the instance for sequences without text (text_wgs == 0).
+template <bool kText>
+__device__ __forceinline__ bool attn_block(const Geo& g, const AttnGrid& a, int64_t bid,
+                                           int64_t& bh, int64_t& blk) {
+  if (kText && bid < a.text_wgs) {
+    bh = bid / g.n_txt;
+    blk = g.n_tiles + bid % g.n_txt;
+    return bh < g.bh;
+  }
+  const int64_t b = bid - a.text_wgs, xcd = b & 7, k8 = b >> 3;
+  bh = k8 / a.slice;
+  blk = xcd * a.slice + (k8 - bh * a.slice);
+  return blk < g.n_tiles;
+}
+
 // Maps a linear workgroup id so that the ids one XCD receives (the hardware
 // deals ids round-robin over the 8 XCDs) form one contiguous range.  A
 // bijection on [0, nblocks) for any nblocks.
