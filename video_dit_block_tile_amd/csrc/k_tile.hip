@@ -49,14 +49,16 @@ __global__ __launch_bounds__(256) void k_tile_pool(Geo g, const uint16_t* __rest
   const bool text = tile >= g.n_tiles;
   const int64_t u0 = (tile - g.n_tiles) * kR;   // text: first text token
   const BlockExtent ext = block_extent(g, text ? 0u : (uint32_t)tile);
+  const int64_t first = text ? g.N + u0 : block_first_token(g, (uint32_t)tile);
 
   u32x4 v[kM];
 #pragma unroll
   for (int m = 0; m < kM; ++m) {
     const int r = (t >> 4) + 16 * m;
     const bool ok = text ? u0 + r < g.L : (ext.full || pos_exists(g, ext, r));
-    const int64_t tok = !ok ? 0 : text ? g.N + u0 + r : tile_token(g, tile, r);
-    v[m] = *reinterpret_cast<const u32x4*>(xb + tok * kHeadDim + ch * 8);   // a real row
+    // a missing position reads the block's first token (which exists), then zero
+    const int64_t tok = first + (!ok ? 0 : text ? r : pos_token_offset(g, r));
+    v[m] = *reinterpret_cast<const u32x4*>(xb + tok * kHeadDim + ch * 8);
     if (!ok) v[m] = u32x4{0u, 0u, 0u, 0u};
   }
   if (xt != nullptr && layout == 0) {
@@ -116,6 +118,7 @@ __global__ __launch_bounds__(256) void k_tile_unpermute(Geo g, const uint16_t* _
   const bool text = tile >= g.n_tiles;
   const int64_t u0 = (tile - g.n_tiles) * kR;
   const BlockExtent ext = block_extent(g, text ? 0u : (uint32_t)tile);
+  const int64_t first = text ? g.N + u0 : block_first_token(g, (uint32_t)tile);
   u32x4 v[kM];
 #pragma unroll
   for (int m = 0; m < kM; ++m) {
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(256) void k_tile_unpermute(Geo g, const uint16_t* _
   for (int m = 0; m < kM; ++m) {
     const int r = (t >> 4) + 16 * m;
     if (text ? u0 + r < g.L : (ext.full || pos_exists(g, ext, r)))
-      *reinterpret_cast<u32x4*>(ob + (text ? g.N + u0 + r : tile_token(g, tile, r)) * kHeadDim +
+      *reinterpret_cast<u32x4*>(ob + (first + (text ? r : pos_token_offset(g, r))) * kHeadDim +
                                 ch * 8) = v[m];
   }
 }

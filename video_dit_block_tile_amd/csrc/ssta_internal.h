@@ -98,6 +98,21 @@ __device__ __forceinline__ bool pos_exists(const Geo& g, const BlockExtent& e, i
   return (r >> (ltw + lth)) < e.lt && ((r >> ltw) & (g.th - 1)) < e.ly && (r & (g.tw - 1)) < e.lx;
 }
 
+// First token (within one batch/head) of clip block `tile`: the token of its
+// position 0, which always exists.
+__device__ __forceinline__ int64_t block_first_token(const Geo& g, uint32_t tile) {
+  const uint32_t nyx = (uint32_t)g.ny * (uint32_t)g.nx;
+  const uint32_t bt = tile / nyx, rem = tile - bt * nyx;
+  const uint32_t by = rem / (uint32_t)g.nx, bx = rem - by * (uint32_t)g.nx;
+  return ((int64_t)bt * g.tt * g.H + (int64_t)by * g.th) * g.W + (int64_t)bx * g.tw;
+}
+// Token offset of in-block position r from the block's first token (block
+// sizes are powers of two, so the position is a bit-field code of (t, y, x)).
+__device__ __forceinline__ int64_t pos_token_offset(const Geo& g, int r) {
+  const int ltw = __builtin_ctz(g.tw), lth = __builtin_ctz(g.th);
+  return ((int64_t)(r >> (ltw + lth)) * g.H + ((r >> ltw) & (g.th - 1))) * g.W + (r & (g.tw - 1));
+}
+
 // Token index (within one batch/head) of in-block position r of block `tile`
 // (beyond the grid for a position that does not exist: check pos_exists).
 __device__ __forceinline__ int64_t tile_token(const Geo& g, int64_t tile, int r) {
