@@ -11,7 +11,8 @@
 //   * dot products are fmaf chains over the channel index 0..127 ascending,
 //     starting at 0.0f (an LDS-tiled fp32 VALU GEMM whose inner loop runs
 //     over channels in order: no split-K, no matrix cores, whose internal
-//     accumulation order is not sequential);
+//     accumulation order is not sequential; channels are staged in two LDS
+//     chunks, and each chain simply continues into the second);
 //   * sqrt and division are IEEE correctly rounded;
 //   * the redundancy sum runs over key blocks in ascending order;
 //   * nothing is contracted (this file is built with -ffp-contract=off).
@@ -24,7 +25,12 @@
 namespace ssta {
 namespace {
 
-constexpr int kBlk = 64;   // GEMM tile: 64 rows x 64 columns per workgroup
+// GEMM tiles: 128 rows x 64 columns per workgroup of 256 threads, each
+// thread an 8 x 4 block of dot products; channels staged through LDS in two
+// chunks of 64 (each dot product stays one fmaf chain over channels 0..127).
+constexpr int kTI = 128;   // rows (query blocks, or key blocks i for Score_r)
+constexpr int kTJ = 64;    // columns (key blocks j)
+constexpr int kDC = 64;    // channels per LDS chunk
 
 // One thread per vector: x / |x| with a sequential fmaf sum of squares.
 __global__ __launch_bounds__(256) void k_normalize(const float* __restrict__ p,
@@ -59,99 +65,112 @@ __global__ __launch_bounds__(256) void k_normalize(const float* __restrict__ p,
   }
 }
 
-// Loads rows [row0, row0+64) of a [n][128] fp32 matrix into LDS transposed,
-// dst[d][row] (rows past n are zero).
-__device__ __forceinline__ void load_block_t(float (*dst)[kBlk], const float* __restrict__ src,
-                                             int64_t row0, int64_t n) {
-  const int t = threadIdx.x;
-  const int r = t & 63;
-  const int64_t gr = row0 + r;
+// Loads rows [row0, row0+ROWS) x channels [d0, d0+kDC) of a [n][128] fp32
+// matrix into LDS transposed, dst[d - d0][row - row0] (rows past n are zero).
+template <int ROWS>
+__device__ __forceinline__ void load_chunk_t(float (*dst)[ROWS], const float* __restrict__ src,
+                                             int64_t row0, int64_t n, int d0) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int d = ((t >> 6) + 4 * q) * 4;
+  for (int it = 0; it < ROWS / 16; ++it) {
+    const int q = threadIdx.x + 256 * it;
+    const int r = q % ROWS, c4 = q / ROWS;          // 16 chunks of 4 channels
+    const int64_t gr = row0 + r;
     float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (gr < n) a = *reinterpret_cast<const float4*>(src + gr * kHeadDim + d);
-    dst[d + 0][r] = a.x;
-    dst[d + 1][r] = a.y;
-    dst[d + 2][r] = a.z;
-    dst[d + 3][r] = a.w;
+    if (gr < n) a = *reinterpret_cast<const float4*>(src + gr * kHeadDim + d0 + 4 * c4);
+    dst[4 * c4 + 0][r] = a.x;
+    dst[4 * c4 + 1][r] = a.y;
+    dst[4 * c4 + 2][r] = a.z;
+    dst[4 * c4 + 3][r] = a.w;
   }
 }
 
-// acc[a][b] = fmaf chain over d ascending of A[d][4*ti+a] * B[d][4*tj+b].
-__device__ __forceinline__ void block_dots(const float (*A)[kBlk], const float (*B)[kBlk],
-                                           int ti, int tj, float acc[4][4]) {
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
+// acc[a][b] = fmaf(A[d][8*ti+a], B[d][4*tj+b], acc[a][b]) for d = 0 .. kDC-1
+// in order: continues each chain over one channel chunk.
+__device__ __forceinline__ void dots_8x4(const float (*A)[kTI], const float (*B)[kTJ], int ti,
+                                         int tj, float acc[8][4]) {
 #pragma unroll 4
-  for (int d = 0; d < kHeadDim; ++d) {
-    const float4 x = *reinterpret_cast<const float4*>(&A[d][4 * ti]);
+  for (int d = 0; d < kDC; ++d) {
+    const float4 x0 = *reinterpret_cast<const float4*>(&A[d][8 * ti]);
+    const float4 x1 = *reinterpret_cast<const float4*>(&A[d][8 * ti + 4]);
     const float4 y = *reinterpret_cast<const float4*>(&B[d][4 * tj]);
-    const float xa[4] = {x.x, x.y, x.z, x.w};
+    const float xa[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
     const float yb[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
       for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_fmaf(xa[a], yb[b], acc[a][b]);
   }
 }
 
 // Score_r: one workgroup owns 64 key columns j and walks the key blocks i in
-// ascending order, 64 at a time, adding u(i, j) = (khat_i.khat_j + 1) * 0.5
+// ascending order, 128 at a time, adding u(i, j) = (khat_i.khat_j + 1) * 0.5
 // for i != j into one running fp32 sum per column.
 __global__ __launch_bounds__(256) void k_redundancy(const float* __restrict__ khat,
                                                     float* __restrict__ red, int64_t n) {
-  __shared__ __attribute__((aligned(16))) float kj[kHeadDim][kBlk];
-  __shared__ __attribute__((aligned(16))) float ki[kHeadDim][kBlk];   // reused for u
+  __shared__ __attribute__((aligned(16))) float kj[kHeadDim][kTJ];   // the 64 columns
+  __shared__ __attribute__((aligned(16))) float ki[kDC][kTI];        // rows; reused for u
   const int64_t bh = blockIdx.y;
-  const int64_t j0 = (int64_t)blockIdx.x * kBlk;
+  const int64_t j0 = (int64_t)blockIdx.x * kTJ;
   const float* kb = khat + bh * n * kHeadDim;
   const int t = threadIdx.x;
   const int ti = t >> 4, tj = t & 15;
-  load_block_t(kj, kb, j0, n);
+  load_chunk_t<kTJ>(kj, kb, j0, n, 0);
+  load_chunk_t<kTJ>(kj + kDC, kb, j0, n, kDC);
   float s = 0.0f;                                   // running sum of column j0 + t (t < 64)
-  float (*u)[kBlk + 1] = reinterpret_cast<float (*)[kBlk + 1]>(&ki[0][0]);
-  for (int64_t i0 = 0; i0 < n; i0 += kBlk) {
-    __syncthreads();                                // ki/u free
-    load_block_t(ki, kb, i0, n);
-    __syncthreads();
-    float acc[4][4];
-    block_dots(ki, kj, ti, tj, acc);
+  float (*u)[kTJ] = reinterpret_cast<float (*)[kTJ]>(&ki[0][0]);   // [kTI][kTJ]
+  for (int64_t i0 = 0; i0 < n; i0 += kTI) {
+    float acc[8][4];
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
+    for (int dc = 0; dc < kHeadDim; dc += kDC) {
+      __syncthreads();                              // ki (or u) free
+      load_chunk_t<kTI>(ki, kb, i0, n, dc);
+      __syncthreads();
+      dots_8x4(ki, kj + dc, ti, tj, acc);
+    }
     __syncthreads();                                // everyone done reading ki
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) u[4 * ti + a][4 * tj + b] = (acc[a][b] + 1.0f) * 0.5f;
+      for (int b = 0; b < 4; ++b) u[8 * ti + a][4 * tj + b] = (acc[a][b] + 1.0f) * 0.5f;
     __syncthreads();
-    if (t < kBlk) {
+    if (t < kTJ) {
       const int64_t j = j0 + t;
-      const int lim = (int)((n - i0) < kBlk ? (n - i0) : kBlk);
+      const int lim = (int)((n - i0) < kTI ? (n - i0) : kTI);
       for (int r = 0; r < lim; ++r)
         if (i0 + r != j) s = s + u[r][t];
     }
   }
-  if (t < kBlk && j0 + t < n) red[bh * n + j0 + t] = (n > 1) ? s / (float)(n - 1) : 0.0f;
+  if (t < kTJ && j0 + t < n) red[bh * n + j0 + t] = (n > 1) ? s / (float)(n - 1) : 0.0f;
 }
 
-// Score_i = (lambda * (qhat_i.khat_j + 1) * 0.5) - (beta * red_j), one 64x64 tile per workgroup.
+// Score_i = (lambda * (qhat_i.khat_j + 1) * 0.5) - (beta * red_j), one
+// 128 x 64 tile per workgroup.
 __global__ __launch_bounds__(256) void k_score_matrix(const float* __restrict__ qhat,
                                                       const float* __restrict__ khat,
                                                       const float* __restrict__ red,
                                                       float* __restrict__ scores, int64_t n,
                                                       float lambda_, float beta) {
-  __shared__ __attribute__((aligned(16))) float qi[kHeadDim][kBlk];
-  __shared__ __attribute__((aligned(16))) float kj[kHeadDim][kBlk];
+  __shared__ __attribute__((aligned(16))) float qi[kDC][kTI];
+  __shared__ __attribute__((aligned(16))) float kj[kDC][kTJ];
   const int64_t bh = blockIdx.z;
-  const int64_t i0 = (int64_t)blockIdx.y * kBlk, j0 = (int64_t)blockIdx.x * kBlk;
+  const int64_t i0 = (int64_t)blockIdx.y * kTI, j0 = (int64_t)blockIdx.x * kTJ;
   const int t = threadIdx.x;
   const int ti = t >> 4, tj = t & 15;
-  load_block_t(qi, qhat + bh * n * kHeadDim, i0, n);
-  load_block_t(kj, khat + bh * n * kHeadDim, j0, n);
-  __syncthreads();
-  float acc[4][4];
-  block_dots(qi, kj, ti, tj, acc);
+  float acc[8][4];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
+  for (int dc = 0; dc < kHeadDim; dc += kDC) {
+    __syncthreads();
+    load_chunk_t<kTI>(qi, qhat + bh * n * kHeadDim, i0, n, dc);
+    load_chunk_t<kTJ>(kj, khat + bh * n * kHeadDim, j0, n, dc);
+    __syncthreads();
+    dots_8x4(qi, kj, ti, tj, acc);
+  }
   float* sb = scores + bh * n * n;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -159,8 +178,8 @@ __global__ __launch_bounds__(256) void k_score_matrix(const float* __restrict__ 
     if (j >= n) continue;
     const float rb = beta * red[bh * n + j];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int64_t i = i0 + 4 * ti + a;
+    for (int a = 0; a < 8; ++a) {
+      const int64_t i = i0 + 8 * ti + a;
       if (i >= n) continue;
       const float gs = (acc[a][b] + 1.0f) * 0.5f;
       const float la = lambda_ * gs;
@@ -263,10 +282,10 @@ hipError_t launch_scores(const Geo& g, const ScoreArgs& a, hipStream_t s) {
   const unsigned nb = (unsigned)((vecs + 255) / 256);
   hipLaunchKernelGGL(k_normalize, dim3(nb), dim3(256), 0, s, a.q_pooled, a.qhat, vecs);
   hipLaunchKernelGGL(k_normalize, dim3(nb), dim3(256), 0, s, a.k_pooled, a.khat, vecs);
-  const unsigned tiles = (unsigned)((n + kBlk - 1) / kBlk);
-  hipLaunchKernelGGL(k_redundancy, dim3(tiles, (unsigned)g.bh), dim3(256), 0, s, a.khat, a.red,
+  const unsigned cols = (unsigned)((n + kTJ - 1) / kTJ), rows = (unsigned)((n + kTI - 1) / kTI);
+  hipLaunchKernelGGL(k_redundancy, dim3(cols, (unsigned)g.bh), dim3(256), 0, s, a.khat, a.red,
                      n);
-  hipLaunchKernelGGL(k_score_matrix, dim3(tiles, tiles, (unsigned)g.bh), dim3(256), 0, s, a.qhat,
+  hipLaunchKernelGGL(k_score_matrix, dim3(cols, rows, (unsigned)g.bh), dim3(256), 0, s, a.qhat,
                      a.khat, a.red, a.scores, n, a.lambda_, a.beta);
   return hipGetLastError();
 }
