@@ -136,11 +136,24 @@ __global__ __launch_bounds__(256) void k_redundancy(const float* __restrict__ kh
 #pragma unroll
       for (int b = 0; b < 4; ++b) u[8 * ti + a][4 * tj + b] = (acc[a][b] + 1.0f) * 0.5f;
     __syncthreads();
+    // Every u is >= +0 and s starts at +0, so adding +0 in place of the
+    // skipped diagonal term leaves s bit-identical; the branch-free form lets
+    // the LDS reads run ahead of the dependent adds.
     if (t < kTJ) {
       const int64_t j = j0 + t;
-      const int lim = (int)((n - i0) < kTI ? (n - i0) : kTI);
-      for (int r = 0; r < lim; ++r)
-        if (i0 + r != j) s = s + u[r][t];
+      if (n - i0 >= kTI) {
+#pragma unroll 16
+        for (int r = 0; r < kTI; ++r) {
+          const float v = u[r][t];
+          s = s + (i0 + r != j ? v : 0.0f);
+        }
+      } else {
+        const int lim = (int)(n - i0);
+        for (int r = 0; r < lim; ++r) {
+          const float v = u[r][t];
+          s = s + (i0 + r != j ? v : 0.0f);
+        }
+      }
     }
   }
   if (t < kTJ && j0 + t < n) red[bh * n + j0 + t] = (n > 1) ? s / (float)(n - 1) : 0.0f;
