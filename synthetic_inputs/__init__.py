@@ -187,7 +187,12 @@ TILE64 = {
                              seed=26),
 }
 
-ALL = {**CONFIGS, **EXTRA, **LATENT, **JOINT, **TILE64}
+# The largest block grid the selection takes (4096 blocks in one head: 16 x 16 x 16).
+LIMITS = {
+    "max-tiles": Workload("max-tiles", 1, 1, 32, 128, 128, topk=64, seed=27),
+}
+
+ALL = {**CONFIGS, **EXTRA, **LATENT, **JOINT, **TILE64, **LIMITS}
 
 
 def _copy_tiles(x: np.ndarray, wl: Workload) -> None:

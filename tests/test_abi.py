@@ -131,6 +131,32 @@ def test_workspace_and_score_validation():
                                  None) == SHAPE
 
 
+def test_size_limits_at_the_boundary():
+    """ssta_score_select takes up to 4096 blocks; the attention entry points up
+    to 65535 blocks per head (one head's K/V addressed with 32-bit offsets)."""
+    lib = m.load()
+    p = m.make_params(topk=2)
+    at_limit = m.make_geom(1, 1, 32, 128, 128)           # 16 x 16 x 16 = 4096 blocks
+    over = m.make_geom(1, 1, 34, 8, 1928)                # 17 x 1 x 241 = 4097 blocks
+    assert at_limit.n_tiles == 4096 and over.n_tiles == 4097
+    # accepted shape: the call gets as far as the (too small) workspace
+    assert lib.ssta_score_select(ctypes.byref(at_limit), ctypes.byref(p), 16, 16, 16, 16, 1,
+                                 None) == WS
+    assert lib.ssta_score_select(ctypes.byref(over), ctypes.byref(p), 16, 16, 16, 16, 1 << 40,
+                                 None) == SHAPE
+    rows_max = m.make_geom(1, 1, 510, 2056, 8)            # 255 x 257 x 1 = 65535 blocks
+    rows_over = m.make_geom(1, 1, 512, 2048, 8)           # 256 x 256 x 1 = 65536 blocks
+    assert rows_max.n_tiles == 65535 and rows_over.n_tiles == 65536
+    # a negative list width is rejected after the size check, so ARG means
+    # the shape was accepted (and nothing is ever launched)
+    args = (16, 16, 16, 16, 16, -1, 16, None, None)
+    assert lib.ssta_attention_fwd(ctypes.byref(rows_max), ctypes.byref(p), *args) == ARG
+    assert lib.ssta_attention_fwd(ctypes.byref(rows_over), ctypes.byref(p), *args) == SHAPE
+    # text blocks count towards the attention limit
+    rows_text = m.make_geom(1, 1, 510, 2056, 8, text_len=1)
+    assert lib.ssta_attention_fwd(ctypes.byref(rows_text), ctypes.byref(p), *args) == SHAPE
+
+
 def test_attention_argument_rules():
     lib = m.load()
     g = _g()

@@ -2,7 +2,8 @@
 720p-10s) in the launch configuration the benchmark times (one SstaPlan.run),
 at the 720p 10 s latent grid (61 x 45 x 80), which the 2 x 8 x 8 block
 does not divide, at 720p 10 s with 256 text tokens after the clip, and at
-720p 10 s with 64-token (4x4x4) blocks.
+720p 10 s with 64-token (4x4x4) blocks, and at the largest block grid the
+selection takes (4096 blocks in one head).
 
 Block means, top-k ids, kept lists and counts are compared in full, bit for
 bit.  The attention output is compared on a deterministic sample of rows that
@@ -22,7 +23,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("name", ["tiny", "480p-short", "480p-5s", "720p-5s", "720p-10s",
-                                  "720p-10s-latent", "720p-10s-text", "720p-10s-t64"])
+                                  "720p-10s-latent", "720p-10s-text", "720p-10s-t64",
+                                  "max-tiles"])
 def test_full_shape(name):
     import video_dit_block_tile_amd as m
     wl = si.ALL[name]
