@@ -111,29 +111,6 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Token index of the first token of block j within one (batch, head).
-__device__ __forceinline__ int64_t block_origin(const Geo& g, int64_t j) {
-  const int64_t bt = j / ((int64_t)g.ny * g.nx), by = (j / g.nx) % g.ny, bx = j % g.nx;
-  return ((bt * g.tt) * g.H + by * g.th) * (int64_t)g.W + bx * g.tw;
-}
-
-// The same in 32-bit arithmetic (block ids and a head's token count fit).
-__device__ __forceinline__ uint32_t block_origin32(const Geo& g, uint32_t j) {
-  const uint32_t nyx = (uint32_t)g.ny * (uint32_t)g.nx;
-  const uint32_t bt = j / nyx, rem = j - bt * nyx;
-  const uint32_t by = rem / (uint32_t)g.nx, bx = rem - by * (uint32_t)g.nx;
-  return ((bt * (uint32_t)g.tt) * (uint32_t)g.H + by * (uint32_t)g.th) * (uint32_t)g.W +
-         bx * (uint32_t)g.tw;
-}
-
-// Token offset (from the block's first token) of in-block position r; block
-// sizes are powers of two because their product is 128 or 64.
-__device__ __forceinline__ uint32_t in_block_offset(const Geo& g, int r) {
-  const int ltw = __builtin_ctz(g.tw), lth = __builtin_ctz(g.th);
-  const int it = r >> (ltw + lth), iy = (r >> ltw) & (g.th - 1), ix = r & (g.tw - 1);
-  return (uint32_t)((it * g.H + iy) * g.W + ix);
-}
-
 // Direct global->LDS loads (buffer_load_dwordx4 ... lds).  A slot is 16 KB:
 // each wave issues kLoads instructions of 1 KB; lane i of an instruction lands
 // at byte 16*i of its 1 KB destination block, so the source address of each
@@ -287,7 +264,7 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
   // token of the query within its head (clip tokens first, then the text)
   const int64_t qtok =
       qtext ? g.N + (qi - g.n_tiles) * kR + (qvalid ? qrow : 0)
-            : block_origin(g, qi) + (qvalid ? in_block_offset(g, qrow) : 0u);
+            : block_first_token(g, (uint32_t)qi) + (qvalid ? in_block_offset(g, qrow) : 0u);
   const uint16_t* qb = static_cast<const uint16_t*>(a.q_t) + row * kTileElems;
   // S tokens of each earlier head precede this one in token-major tensors
   if (kTok) qb = static_cast<const uint16_t*>(a.q_t) + (bh * g.S + qtok) * kHeadDim;

@@ -74,26 +74,6 @@ __device__ __forceinline__ int swz_col(int d, int chunk) {
   return d * 64 + ((chunk ^ ((d >> 2) & 3)) << 4);
 }
 
-__device__ __forceinline__ int64_t block_origin(const Geo& g, int64_t j) {
-  const int64_t bt = j / ((int64_t)g.ny * g.nx), by = (j / g.nx) % g.ny, bx = j % g.nx;
-  return ((bt * g.tt) * g.H + by * g.th) * (int64_t)g.W + bx * g.tw;
-}
-__device__ __forceinline__ uint32_t block_origin32(const Geo& g, uint32_t j) {
-  const uint32_t nyx = (uint32_t)g.ny * (uint32_t)g.nx;
-  const uint32_t bt = j / nyx, rem = j - bt * nyx;
-  const uint32_t by = rem / (uint32_t)g.nx, bx = rem - by * (uint32_t)g.nx;
-  return ((bt * (uint32_t)g.tt) * (uint32_t)g.H + by * (uint32_t)g.th) * (uint32_t)g.W +
-         bx * (uint32_t)g.tw;
-}
-// Token offset (from the block's first token) of in-block position r.  The
-// position is a bit-field code of (t, y, x) offsets (block sizes are powers of
-// two), so positions with disjoint bits add: off(32p + r) = off(32p) + off(r).
-__device__ __forceinline__ uint32_t in_block_offset(const Geo& g, int r) {
-  const int ltw = __builtin_ctz(g.tw), lth = __builtin_ctz(g.th);
-  const int it = r >> (ltw + lth), iy = (r >> ltw) & (g.th - 1), ix = r & (g.tw - 1);
-  return (uint32_t)((it * g.H + iy) * g.W + ix);
-}
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
@@ -179,7 +159,7 @@ __device__ __forceinline__ void dma_cols(uint8_t* dst, __amdgpu_buffer_rsrc_t rs
 template <bool kGen, int kR>
 __device__ __forceinline__ int64_t row_token(const Geo& g, int64_t j, int r, bool exists) {
   if (kGen && j >= g.n_tiles) return g.N + (j - g.n_tiles) * kR + (exists ? r : 0);
-  return block_origin(g, j) + (exists ? in_block_offset(g, r) : 0u);
+  return block_first_token(g, (uint32_t)j) + (exists ? in_block_offset(g, r) : 0u);
 }
 
 // Kept-block ids of one list, 64 at a time (lane i holds entry base + i);
@@ -499,7 +479,8 @@ __global__ __launch_bounds__(256) void k_attn_bwd_prep(Geo g, const uint16_t* __
     return;
   }
   const int64_t tok =
-      bh * g.S + (text ? g.N + (tile - g.n_tiles) * g.R + r : tile_token(g, tile, r));
+      bh * g.S + (text ? g.N + (tile - g.n_tiles) * g.R + r
+                       : block_first_token(g, (uint32_t)tile) + pos_token_offset(g, r));
   const uint16_t* orow = o + tok * kHeadDim + 64 * half;
   const uint16_t* drow = dout + tok * kHeadDim + 64 * half;
   float acc = 0.0f;

@@ -65,15 +65,6 @@ __device__ __forceinline__ bool attn_block(const Geo& g, const AttnGrid& a, int6
   return blk < g.n_tiles;
 }
 
-// Maps a linear workgroup id so that the ids one XCD receives (the hardware
-// deals ids round-robin over the 8 XCDs) form one contiguous range.  A
-// bijection on [0, nblocks) for any nblocks.
-__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblocks) {
-  const int64_t q = nblocks / 8, r = nblocks % 8;
-  const int64_t xcd = bid % 8, k = bid / 8;
-  return xcd < r ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
-}
-
 // Extent of block `tile` along each axis: the block size, except at the far
 // edges of a ragged grid.
 struct BlockExtent {
@@ -113,16 +104,21 @@ __device__ __forceinline__ int64_t pos_token_offset(const Geo& g, int r) {
   return ((int64_t)(r >> (ltw + lth)) * g.H + ((r >> ltw) & (g.th - 1))) * g.W + (r & (g.tw - 1));
 }
 
-// Token index (within one batch/head) of in-block position r of block `tile`
-// (beyond the grid for a position that does not exist: check pos_exists).
-__device__ __forceinline__ int64_t tile_token(const Geo& g, int64_t tile, int r) {
-  const int64_t bt = tile / ((int64_t)g.ny * g.nx);
-  const int64_t by = (tile / g.nx) % g.ny;
-  const int64_t bx = tile % g.nx;
-  const int it = r / (g.th * g.tw);
-  const int iy = (r / g.tw) % g.th;
-  const int ix = r % g.tw;
-  return ((bt * g.tt + it) * g.H + (by * g.th + iy)) * (int64_t)g.W + (bx * g.tw + ix);
+// 32-bit forms for the attention kernels, whose per-head offsets fit 32 bits
+// (one head's tensor is below 2^31 bytes).  Because the position is a
+// bit-field code, positions with disjoint bits add:
+// in_block_offset(a + b) = in_block_offset(a) + in_block_offset(b).
+__device__ __forceinline__ uint32_t block_origin32(const Geo& g, uint32_t tile) {
+  const uint32_t nyx = (uint32_t)g.ny * (uint32_t)g.nx;
+  const uint32_t bt = tile / nyx, rem = tile - bt * nyx;
+  const uint32_t by = rem / (uint32_t)g.nx, bx = rem - by * (uint32_t)g.nx;
+  return ((bt * (uint32_t)g.tt) * (uint32_t)g.H + by * (uint32_t)g.th) * (uint32_t)g.W +
+         bx * (uint32_t)g.tw;
+}
+__device__ __forceinline__ uint32_t in_block_offset(const Geo& g, int r) {
+  const int ltw = __builtin_ctz(g.tw), lth = __builtin_ctz(g.th);
+  const int it = r >> (ltw + lth), iy = (r >> ltw) & (g.th - 1), ix = r & (g.tw - 1);
+  return (uint32_t)((it * g.H + iy) * g.W + ix);
 }
 
 hipError_t launch_tile_pool(const Geo& g, const void* x, void* x_tiled, int layout,
