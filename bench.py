@@ -51,7 +51,7 @@ PEAK_FP32_VECTOR_TFLOPS = 157.3    # MI355X published fp32 vector peak (packed F
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="720p-10s")
     ap.add_argument("--dense-steps", type=int, default=2)
@@ -97,9 +97,54 @@ def kernel_hash():
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def cpu_baseline(wl, q, k, v, rows_wanted):
+_SINGLE_CORE = r"""
+import json, sys, time
+sys.path.insert(0, sys.argv[1])
+import numpy as np
+import oracle
+import synthetic_inputs as si
+wl = si.ALL[sys.argv[2]].with_(heads=1, batch=1)
+q, k, v = (np.load(sys.argv[3] + "/%s.npy" % n) for n in "qkv")
+rows = np.linspace(0, wl.n_tiles - 1, num=int(sys.argv[4])).astype(np.int64)
+t0 = time.perf_counter()
+sel = oracle.select(wl, q, k)
+t_sel = time.perf_counter() - t0
+t0 = time.perf_counter()
+oracle.attention(wl, q, k, v, sel["kv_idx"], sel["kv_cnt"], rows)
+t_att = time.perf_counter() - t0
+print(json.dumps({"t_sel": t_sel, "t_att": t_att,
+                  "pairs": int(sel["kv_cnt"].reshape(-1)[rows].sum()), "rows": int(rows.size)}))
+"""
+
+
+def cpu_single_core(wl, q1, k1, v1, rows):
+    """The same oracle with one thread (OMP_NUM_THREADS=1 in a child process),
+    on head 0's selection and `rows` query blocks."""
+    import tempfile
+    import subprocess
+    import numpy as np
+    with tempfile.TemporaryDirectory() as d:
+        for name, x in zip("qkv", (q1, k1, v1)):
+            np.save(os.path.join(d, name + ".npy"), x)
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        r = subprocess.run([sys.executable, "-c", _SINGLE_CORE, ROOT, wl.name, d, str(rows)],
+                           env=env, capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        return {"error": r.stderr[-400:]}
+    res = json.loads(r.stdout.strip().splitlines()[-1])
+    n = wl.n_tiles
+    t = res["t_att"] + res["t_sel"] * res["rows"] / n
+    return {"value": res["pairs"] * 4 * wl.tile_tokens ** 2 * 128 / t / 1e12, "unit": "TFLOP/s",
+            "cores": 1, "selection_head0_s": round(res["t_sel"], 3),
+            "attention_s_per_query_block": round(res["t_att"] / res["rows"], 4),
+            "sample": "head 0: full selection (prorated) + fp64 attention of %d query blocks"
+                      % res["rows"]}
+
+
+def cpu_baseline(wl, q, k, v, rows_wanted, single_rows=24):
     """Oracle (as is) on a bounded sample: the selection for head 0 and the
-    attention of `rows_wanted` query blocks of head 0."""
+    attention of `rows_wanted` query blocks of head 0, on every host thread,
+    then a smaller sample of the same on one thread."""
     import numpy as np
     import oracle
 
@@ -124,6 +169,9 @@ def cpu_baseline(wl, q, k, v, rows_wanted):
         "sample": ("%s head 0: full selection (%.1f s, prorated to the sampled rows) + fp64 "
                    "attention of %d of %d query blocks (%d kept pairs, %.1f s)"
                    % (wl.name, t_sel, len(rows), n, pairs, t_att)),
+        "selection_head0_s": round(t_sel, 3),
+        "attention_s_per_query_block": round(t_att / len(rows), 4),
+        "single_core": cpu_single_core(wl, q1, k1, v1, single_rows),
     }
 
 
