@@ -31,6 +31,40 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(L.SIGNATURES)
 
 
+def test_header_is_plain_c(tmp_path):
+    """include/ssta.h compiles as C11 and a C program links against the
+    library and calls its host-side entry points (no device needed)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "use_ssta.c"
+    src.write_text(r"""
+#include <stdio.h>
+#include "ssta.h"
+int main(void) {
+  ssta_geom_t g = {1, 2, 128, 4, 16, 16, 2, 8, 8, 77};
+  ssta_params_t p = {1, 1, 1, 2, 0.9f, 0.1f, 0.08838834764831845f, 0u};
+  printf("%lld %d %d %s\n", (long long)ssta_block_rows(&g), ssta_topk_width(&g, &p),
+         ssta_max_kept(&g, &p), ssta_status_string(SSTA_ERR_SHAPE));
+  return 0;
+}
+""")
+    lib = m.library_path()
+    exe = tmp_path / "use_ssta"
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), lib, "-o", str(exe)], check=True)
+    env = dict(os.environ, LD_LIBRARY_PATH=os.path.dirname(lib))
+    out = subprocess.run([str(exe)], capture_output=True, text=True, env=env, check=True).stdout
+    rows, width, kept, text = out.split(maxsplit=3)
+    assert (int(rows), int(width), int(kept)) == (9, 2, 8)
+    assert text.strip() == lib_status_text(SHAPE)
+
+
+def lib_status_text(code):
+    return m.load().ssta_status_string(code).decode()
+
+
 def test_status_strings():
     lib = m.load()
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
