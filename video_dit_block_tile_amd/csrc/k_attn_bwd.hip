@@ -328,9 +328,18 @@ void k_attn_bwd_kv(Geo g, BwdArgs a, AttnGrid grid) {
   constexpr int kParts = kDK ? 3 : 2;
   constexpr int kSlot = kParts * kUnitBytes + 256;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kSlot];
-  // text key blocks (kept by every query block) first, then XCD slices
+  // text key blocks (kept by every query block) first; then, with the kept
+  // lists, each head's key blocks longest first (k_order_blocks), dealt
+  // round-robin over the XCDs; under dense attention, XCD slices
   int64_t bh, kj;
-  if (!attn_block<kGen>(g, grid, blockIdx.x, bh, kj)) return;
+  if (a.order != nullptr && !(kGen && (int64_t)blockIdx.x < grid.text_wgs)) {
+    const int64_t b = (int64_t)blockIdx.x - grid.text_wgs;
+    bh = b / g.n_tiles;
+    if (bh >= g.bh) return;
+    kj = a.order[b];
+  } else if (!attn_block<kGen>(g, grid, blockIdx.x, bh, kj)) {
+    return;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -539,6 +548,73 @@ __global__ __launch_bounds__(256) void k_gather_lists(Geo g, const uint32_t* __r
   q_cnt[krow] = m;
 }
 
+// Key blocks of every head in decreasing order of the number of query
+// blocks that keep them (ties: ascending block id), for the dK/dV grids: a
+// key block's workgroup runs over that many query blocks, and top-k
+// selection makes a few key blocks many times more popular than the median.
+// Taking the longest first, dealt round-robin over the XCDs, balances the
+// XCDs and leaves only short workgroups for the end of the launch.  A
+// counting sort per head (one workgroup): bucket b holds the count
+// kOrderBuckets-1-b (counts beyond share the first bucket), and a block's
+// place within its bucket is the number of earlier blocks with the same
+// bucket, found chunk by chunk.
+constexpr int kOrderBuckets = 4096;
+constexpr int kOrderThreads = 1024;
+__global__ __launch_bounds__(kOrderThreads) void k_order_blocks(Geo g,
+                                                                const int32_t* __restrict__ q_cnt,
+                                                                int32_t* __restrict__ order) {
+  __shared__ uint32_t start[kOrderBuckets];
+  __shared__ uint32_t part[kOrderThreads];
+  __shared__ uint16_t chunk[kOrderThreads];
+  const int t = threadIdx.x;
+  const int64_t n = g.n_tiles;
+  const int32_t* cnt = q_cnt + (int64_t)blockIdx.x * n;
+  int32_t* out = order + (int64_t)blockIdx.x * n;
+  auto bucket = [&](int64_t j) -> int {
+    return kOrderBuckets - 1 - min(cnt[j], kOrderBuckets - 1);
+  };
+  for (int b = t; b < kOrderBuckets; b += kOrderThreads) start[b] = 0u;
+  __syncthreads();
+  for (int64_t j = t; j < n; j += kOrderThreads) atomicAdd(&start[bucket(j)], 1u);
+  __syncthreads();
+  // exclusive scan of the bucket sizes: 4 buckets per thread, then the
+  // threads' totals
+  constexpr int kPer = kOrderBuckets / kOrderThreads;
+  uint32_t own = 0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) own += start[kPer * t + e];
+  part[t] = own;
+  __syncthreads();
+  for (int d = 1; d < kOrderThreads; d *= 2) {
+    const uint32_t add = t >= d ? part[t - d] : 0u;
+    __syncthreads();
+    part[t] += add;
+    __syncthreads();
+  }
+  uint32_t run = part[t] - own;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const uint32_t c = start[kPer * t + e];
+    start[kPer * t + e] = run;
+    run += c;
+  }
+  __syncthreads();
+  for (int64_t c0 = 0; c0 < n; c0 += kOrderThreads) {
+    const int64_t j = c0 + t;
+    const int b = j < n ? bucket(j) : -1;
+    chunk[t] = (uint16_t)(b < 0 ? 0xFFFF : b);
+    __syncthreads();
+    if (b >= 0) {
+      uint32_t before = 0;
+      for (int i = 0; i < t; ++i) before += chunk[i] == (uint16_t)b;
+      out[start[b] + before] = (int32_t)j;
+    }
+    __syncthreads();
+    if (b >= 0) atomicAdd(&start[b], 1u);
+    __syncthreads();
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attention_bwd_prep(const Geo& g, const void* o, const void* dout,
@@ -551,7 +627,7 @@ hipError_t launch_attention_bwd_prep(const Geo& g, const void* o, const void* do
 
 hipError_t launch_transpose_lists(const Geo& g, const int32_t* kv_idx, const int32_t* kv_cnt,
                                   int32_t max_kept, uint32_t* mask_t, int32_t* q_idx,
-                                  int32_t* q_cnt, hipStream_t s) {
+                                  int32_t* q_cnt, int32_t* order, hipStream_t s) {
   const int64_t rows = g.bh * g.n_tiles;
   const int64_t words = (g.n_tiles + 31) / 32;
   const int64_t total = rows * words;
@@ -564,6 +640,8 @@ hipError_t launch_transpose_lists(const Geo& g, const int32_t* kv_idx, const int
   }
   hipLaunchKernelGGL(k_gather_lists, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, g,
                      mask_t, words, q_idx, q_cnt);
+  hipLaunchKernelGGL(k_order_blocks, dim3((unsigned)g.bh), dim3(kOrderThreads), 0, s, g, q_cnt,
+                     order);
   return hipGetLastError();
 }
 

@@ -371,7 +371,7 @@ int ssta_attention_fwd_tokens(const ssta_geom_t* g, const ssta_params_t* p, cons
 
 namespace {
 struct BwdLayout {
-  int64_t k_cols, q_cols, d_cols, ld, mask, q_idx, q_cnt, total;
+  int64_t k_cols, q_cols, d_cols, ld, mask, q_idx, q_cnt, order, total;
 };
 BwdLayout bwd_layout(const Geo& g) {
   BwdLayout w;
@@ -386,7 +386,8 @@ BwdLayout bwd_layout(const Geo& g) {
   w.mask = w.ld + align256(g.bh * g.n_rows * g.R * 8);
   w.q_idx = w.mask + align256(rows * ((g.n_tiles + 31) / 32) * 4);
   w.q_cnt = w.q_idx + align256(rows * g.n_tiles * 4);
-  w.total = w.q_cnt + align256(rows * 4);
+  w.order = w.q_cnt + align256(rows * 4);
+  w.total = w.order + align256(rows * 4);
   return w;
 }
 }  // namespace
@@ -434,10 +435,11 @@ int ssta_attention_bwd(const ssta_geom_t* g, const ssta_params_t* p, const void*
   SSTA_TRY(hip_status(ssta::launch_attention_bwd_prep(geo, o, dout, lse, ld, st)));
   int32_t* q_idx = reinterpret_cast<int32_t*>(ws + lay.q_idx);
   int32_t* q_cnt = reinterpret_cast<int32_t*>(ws + lay.q_cnt);
+  int32_t* order = reinterpret_cast<int32_t*>(ws + lay.order);
   if (!dense)
     SSTA_TRY(hip_status(ssta::launch_transpose_lists(
         geo, kv_idx, kv_cnt, max_kept_, reinterpret_cast<uint32_t*>(ws + lay.mask), q_idx,
-        q_cnt, st)));
+        q_cnt, order, st)));
   ssta::BwdArgs a;
   a.q = q;
   a.k = k;
@@ -453,6 +455,7 @@ int ssta_attention_bwd(const ssta_geom_t* g, const ssta_params_t* p, const void*
   a.q_idx = dense ? nullptr : q_idx;
   a.q_cnt = dense ? nullptr : q_cnt;
   a.q_width = (int32_t)geo.n_tiles;
+  a.order = dense ? nullptr : order;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;

@@ -188,6 +188,7 @@ struct BwdArgs {
   const int32_t* q_idx;   // key block -> query blocks that keep it, ascending (NULL: dense)
   const int32_t* q_cnt;
   int32_t q_width;
+  const int32_t* order;   // per head, key blocks by decreasing q_cnt (NULL: grid order)
   void* dq;               // token-major bf16 outputs
   void* dk;
   void* dv;
@@ -197,7 +198,7 @@ hipError_t launch_attention_bwd_prep(const Geo& g, const void* o, const void* do
                                      const float* lse, float* ld, hipStream_t s);
 hipError_t launch_transpose_lists(const Geo& g, const int32_t* kv_idx, const int32_t* kv_cnt,
                                   int32_t max_kept, uint32_t* mask_t, int32_t* q_idx,
-                                  int32_t* q_cnt, hipStream_t s);
+                                  int32_t* q_cnt, int32_t* order, hipStream_t s);
 hipError_t launch_attention_bwd(const Geo& g, const BwdArgs& a, hipStream_t s);
 
 // Sustained matrix-core rate (measurement aid; see k_calib.hip).
