@@ -452,18 +452,19 @@ def main():
         cpu = cpu_baseline(wl, q, k, v, args.cpu_rows)
 
     # Algorithmic bytes and VALU work of each phase (what the step must move or
-    # compute at minimum; the design doc lists the per-unit figures).
+    # compute at minimum).
     bh = wl.batch * wl.heads
     tensor = bh * wl.seq_len * 128 * 2                  # one of Q, K, V, O in bf16
     pooled = bh * n * 128 * 4
     phase_bytes = {
-        # read Q, K, V; write V_t (and Q_t, K_t when materialised); write both pooled arrays
-        "tile_pool": (4 if fused else 6) * tensor + 2 * pooled,
+        # read Q and K, write both pooled arrays (materialised blocks: also read V and
+        # write Q_t, K_t and V_t)
+        "tile_pool": (2 if fused else 6) * tensor + 2 * pooled,
         # read both pooled arrays, write the top-k ids
         "score_select": 2 * pooled + bh * n * plan.width * 4,
         # read the top-k ids, write the kept lists and counts
         "build_mask": bh * n * (plan.width + plan.max_kept + 1) * 4,
-        # each kept pair reads one K block and one V^T block (32 KB each at 128 tokens);
+        # each kept pair reads one K block and one V block (32 KB each at 128 tokens);
         # Q read, O written once
         "attention": pairs * 2 * R * 128 * 2 + 2 * tensor,
         "unpermute": 0 if fused else 2 * tensor,

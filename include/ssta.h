@@ -203,21 +203,22 @@ int ssta_attention_fwd(const ssta_geom_t* g, const ssta_params_t* p, const void*
 
 /*
  * Step 4 with the block gathers and the output scatter folded into the
- * attention kernel: the same computation as ssta_attention_fwd, but Q, K and
- * the output O stay in the caller's token order, so neither Q nor K needs a
- * tile-major copy and O no unpermute (each kept key block is gathered token
- * row by token row straight into LDS).  V keeps its dim-major block layout:
- * the P.V product needs 8 consecutive keys of one channel per lane.
+ * attention kernel: the same computation as ssta_attention_fwd, but Q, K, V
+ * and the output O stay in the caller's token order, so no input needs a
+ * block copy and O no unpermute (each kept key block's K and V rows are
+ * gathered token row by token row straight into LDS; the P.V product reads
+ * its V^T operand from the token rows with transposing LDS loads).
  *   q        in : bf16 [batch, heads, S, head_dim] (token-major).
  *   k        in : bf16 [batch, heads, S, head_dim] (token-major).
- *   v_t      in : bf16 [batch, heads, n_rows, head_dim, tile_tokens] (dim-major tiles).
+ *   v        in : bf16 [batch, heads, S, head_dim] (token-major).
  *   kv_idx, kv_cnt, max_kept, lse: as for ssta_attention_fwd (LSE stays tile-major).
  *   o       out : bf16 [batch, heads, S, head_dim] (token-major).
- * Results are bit-identical to permuting Q and K with ssta_tile_pool,
- * ssta_attention_fwd and ssta_tile_unpermute.
+ * Results are bit-identical to permuting Q, K (token-major tiles) and V
+ * (dim-major tiles) with ssta_tile_pool, ssta_attention_fwd and
+ * ssta_tile_unpermute.
  */
 int ssta_attention_fwd_tokens(const ssta_geom_t* g, const ssta_params_t* p, const void* q,
-                              const void* k, const void* v_t, const int32_t* kv_idx,
+                              const void* k, const void* v, const int32_t* kv_idx,
                               const int32_t* kv_cnt, int32_t max_kept, void* o, float* lse,
                               void* stream);
 

@@ -290,15 +290,14 @@ def ssta_attention_fwd(g: SstaGeom, p: SstaParams, q_t, k_t, v_t, kv_idx, kv_cnt
           _ptr(kv_idx), _ptr(kv_cnt), mk, _ptr(o_t), _ptr(lse), _stream(stream))
 
 
-def ssta_attention_fwd_tokens(g: SstaGeom, p: SstaParams, q, k, v_t, kv_idx, kv_cnt, o,
+def ssta_attention_fwd_tokens(g: SstaGeom, p: SstaParams, q, k, v, kv_idx, kv_cnt, o,
                               lse=None, stream=None):
-    """Attention with token-major q, k and o (block gathers and output scatter
-    inside the kernel); v_t dim-major tiles."""
+    """Attention with token-major q, k, v and o (block gathers and output
+    scatter inside the kernel)."""
     tok = (g.batch, g.heads, g.seq_len, g.head_dim)
     _expect("q", q, tok, torch.bfloat16)
     _expect("k", k, tok, torch.bfloat16)
-    _expect("v_t", v_t, (g.batch, g.heads, g.n_rows, g.head_dim, g.tile_tokens),
-            torch.bfloat16)
+    _expect("v", v, tok, torch.bfloat16)
     _expect("o", o, tok, torch.bfloat16)
     _expect("lse", lse, (g.batch, g.heads, g.n_rows, g.tile_tokens), torch.float32,
             allow_none=True)
@@ -311,7 +310,7 @@ def ssta_attention_fwd_tokens(g: SstaGeom, p: SstaParams, q, k, v_t, kv_idx, kv_
         mk = kv_idx.shape[-1]
         _expect("kv_idx", kv_idx, (g.batch, g.heads, g.n_tiles, mk), torch.int32)
     _call("ssta_attention_fwd_tokens", ctypes.byref(g), ctypes.byref(p), _ptr(q), _ptr(k),
-          _ptr(v_t), _ptr(kv_idx), _ptr(kv_cnt), mk, _ptr(o), _ptr(lse), _stream(stream))
+          _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), mk, _ptr(o), _ptr(lse), _stream(stream))
 
 
 def ssta_calibrate_mfma(operands, sink, grid: int, iters: int, stream=None):

@@ -14,11 +14,13 @@
 // MFMA output layout of S^T is reused directly as the B operand of
 // O^T += V^T P^T.  Each lane feeds key row kperm(lane) (bits 2 and 3 of the
 // lane index swapped) into the S^T product, which makes every 8 output
-// registers of a lane 8 consecutive keys; V arrives dim-major, so the matching
-// A operand of the P.V product is one 16-byte LDS read of a V^T row.
-// K rows and V^T rows are staged in LDS with a 16-byte-chunk XOR swizzle
-// (K: chunk ^ row%16; V^T: chunk ^ (row/2)%8) so the MFMA operand reads are
-// conflict-free.
+// registers of a lane 8 consecutive keys, the A operand of the P.V product:
+// channel d of 8 consecutive keys.  With token-major inputs V is gathered in
+// token rows like K, and that operand comes from two transposing LDS reads
+// (ds_read_b64_tr_b16) of 4 keys each; with dim-major V tiles it is one
+// 16-byte read of a V^T row.  LDS rows carry a 16-byte-chunk XOR swizzle
+// (K rows: chunk ^ row%16; V rows: chunk ^ 4*(row%4); V^T rows:
+// chunk ^ (row/2)%8) so the MFMA operand reads are conflict-free.
 // Schedule: the hardware deals workgroup ids round-robin over the 8 XCDs.
 // The grid is laid out so that XCD x receives, head after head, the
 // contiguous slice [x*c, (x+1)*c) of that head's query blocks (c = ceil(n/8)).
@@ -29,7 +31,7 @@
 // which run over every block, take the first workgroups of the grid, dealt
 // over all XCDs, so they overlap the clip blocks instead of trailing them.
 // Memory: each kept block is processed as two units of 64 keys.  A unit's K
-// rows and V^T columns (16 KB each) go straight from global memory into LDS
+// and V (16 KB each) go straight from global memory into LDS
 // with buffer_load_dwordx4 ... lds (no register staging) into a two-slot
 // ring; the next unit's loads are issued right after the barrier that frees
 // its slot and overlap the whole current unit.  The buffer form (a per-head
@@ -82,15 +84,50 @@ constexpr float kMaxUnitSum = 4294967296.0f;   // 2^32
 constexpr int kFenceKeepDs = 0x0002 | 0x0004 | 0x0400;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-// K slot (64 rows of 256 B): chunk c of row r sits at chunk c ^ (r % 16).
+// Token-row slots (64 rows of 256 B): 16-byte chunk c of row r sits at chunk
+// c ^ row_swz(r).  K (read a whole 16-byte chunk per lane, 16 rows at a time):
+// r % 16.  V (read 8 bytes per lane by the transposing loads, 4 rows at a
+// time): 4 * (r % 4).  Both make the operand reads conflict-free.
+template <bool kV>
+__device__ __forceinline__ int row_swz(int row) {
+  return kV ? 4 * (row & 3) : (row & 15);
+}
 __device__ __forceinline__ int swz_k(int row, int chunk) {
-  return row * 256 + ((chunk ^ (row & 15)) << 4);
+  return row * 256 + ((chunk ^ row_swz<false>(row)) << 4);
 }
 // V^T slot (128 channel rows of 128 B): chunk c of row d sits at chunk
 // c ^ ((d / 2) % 8), so 16 consecutive rows read one chunk from 16 distinct
 // bank groups.
 __device__ __forceinline__ int swz_v(int d, int chunk) {
   return d * 128 + ((chunk ^ ((d >> 1) & 7)) << 4);
+}
+
+// A operand of O^T += V^T P^T for k-step (t, ks) and channel block db: lane
+// (l32, hl) needs channel 32*db + l32 of the 8 keys 32t + 16ks + 8hl + (0..7).
+// From a token-major V slot (rows of 256 B, swizzle row_swz<true>) this is two
+// transposing reads (ds_read_b64_tr_b16): within each group of 16 lanes, lane
+// j reads 4 channels of key j/4 of a 4-key row group, and lane i of the group
+// receives channel i of those 4 keys.  v_lane_offset gives this lane's byte
+// offset for the first 4 keys of the hl half (the second 4 keys lie 1 KB
+// further); with row & 3 = j/4 the swizzle only flips the 64-byte group.
+__device__ __forceinline__ int v_lane_offset(int lane, int db) {
+  const int j = lane & 15, grp = (lane >> 4) & 1, hl = lane >> 5;
+  const int kq = j >> 2;                                   // key within the 4-row group
+  const int chunk = 4 * (db ^ kq) + 2 * grp + ((j & 3) >> 1);   // swizzled 16-byte chunk
+  return (8 * hl + kq) * 256 + chunk * 16 + 8 * (j & 1);
+}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+template <bool kTok>
+__device__ __forceinline__ bf16x8 v_operand(const uint8_t* sV, int t, int ks, int db, int l32,
+                                            int hl, int vofs) {
+  if (!kTok)
+    return *reinterpret_cast<const bf16x8*>(sV + swz_v(32 * db + l32, 4 * t + 2 * ks + hl));
+  const uint8_t* p = sV + vofs + (32 * t + 16 * ks) * 256;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 1024));
+  const auto w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, w);
 }
 
 __device__ __forceinline__ float max3f(float a, float b, float c) {
@@ -122,20 +159,26 @@ struct DmaOffsets {
   uint32_t k[Blk<kR>::kLoads], v[Blk<kR>::kLoads];
 };
 
-// kTokK: K is read from token-major [.., S, 128] memory, so key row r of a
-// unit comes from token in_block_offset(r) of its block (a 256-byte row).
-// V^T comes from dim-major tiles whose channel rows hold 2*kR bytes.
-template <bool kTokK, int kR>
+// kTok: K and V are read from token-major [.., S, 128] memory, so key row r
+// of a unit comes from token in_block_offset(r) of its block (a 256-byte
+// row); V rows land like K rows, with their own swizzle.  Otherwise K comes
+// from tile-major blocks and V^T from dim-major tiles whose channel rows hold
+// 2*kR bytes.
+template <bool kTok, int kR>
 __device__ __forceinline__ DmaOffsets<kR> dma_offsets(const Geo& g, int wave, int lane) {
   DmaOffsets<kR> o;
 #pragma unroll
   for (int mm = 0; mm < Blk<kR>::kLoads; ++mm) {
     const int b = Blk<kR>::kLoads * wave + mm;   // 1 KB destination block
-    const int row = 4 * b + (lane >> 4);         // K: rows 4b .. 4b+3
-    const uint32_t src_row = kTokK ? in_block_offset(g, row) : (uint32_t)row;
-    o.k[mm] = src_row * 256 + (((lane & 15) ^ (row & 15)) << 4);
-    const int d = 8 * b + (lane >> 3);           // V^T: channel rows 8b .. 8b+7
-    o.v[mm] = d * (2 * kR) + (((lane & 7) ^ ((d >> 1) & 7)) << 4);
+    const int row = 4 * b + (lane >> 4);         // token rows 4b .. 4b+3
+    const uint32_t src_row = kTok ? in_block_offset(g, row) : (uint32_t)row;
+    o.k[mm] = src_row * 256 + (((lane & 15) ^ row_swz<false>(row)) << 4);
+    if (kTok) {
+      o.v[mm] = src_row * 256 + (((lane & 15) ^ row_swz<true>(row)) << 4);
+    } else {
+      const int d = 8 * b + (lane >> 3);         // V^T: channel rows 8b .. 8b+7
+      o.v[mm] = d * (2 * kR) + (((lane & 7) ^ ((d >> 1) & 7)) << 4);
+    }
   }
   return o;
 }
@@ -148,18 +191,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint8_t* base,
                                            (int)(n_rows * Blk<kR>::kBytes), 0x00020000);
 }
 
-// Half p (keys 64p .. 64p+63) of K block j.  Tile-major: 64 contiguous rows.
-// Token-major: the rows of the block's tokens; in-block positions are a
-// bit-field code of (t, y, x) offsets, so position 64p + r lies at token
-// offset in_block_offset(64p) + in_block_offset(r) from the block's origin.
-// kGen (ragged grids, joint text): bit r of `valid` says whether position
-// 64p + r of the block exists; a token-major gather redirects the rows that do
-// not to an existing row (their scores are masked later).  Blocks from n_tiles
-// on are text blocks, whose positions are consecutive tokens after the clip's.
-template <bool kTokK, bool kGen, int kR>
-__device__ __forceinline__ void dma_k(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, const Geo& g,
-                                      int64_t j, int p, int wave, int lane, uint64_t valid,
-                                      const DmaOffsets<kR>& off) {
+// Half p (keys 64p .. 64p+63) of the K (kV: V) block j, as 64 token rows.
+// Tile-major: 64 contiguous rows.  Token-major: the rows of the block's
+// tokens; in-block positions are a bit-field code of (t, y, x) offsets, so
+// position 64p + r lies at token offset in_block_offset(64p) +
+// in_block_offset(r) from the block's origin.  kGen (ragged grids, joint
+// text): bit r of `valid` says whether position 64p + r of the block exists;
+// a token-major gather redirects the rows that do not to an existing row
+// (their probabilities are zero).  Blocks from n_tiles on are text blocks,
+// whose positions are consecutive tokens after the clip's.  `offs`: the K or
+// V offsets of a DmaOffsets<kR>.
+template <bool kTokK, bool kGen, int kR, bool kV>
+__device__ __forceinline__ void dma_rows(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, const Geo& g,
+                                         int64_t j, int p, int wave, int lane, uint64_t valid,
+                                         const uint32_t* offs) {
   constexpr int kL = Blk<kR>::kLoads;
   const bool text = kGen && kTokK && j >= g.n_tiles;
   uint32_t so =
@@ -168,9 +213,9 @@ __device__ __forceinline__ void dma_k(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, c
   if (text) so = (uint32_t)((g.N + (j - g.n_tiles) * kR + 64 * p) * 256);
 #pragma unroll
   for (int mm = 0; mm < kL; ++mm) {
-    uint32_t vo = off.k[mm];
+    uint32_t vo = offs[mm];
     const int r = 4 * (kL * wave + mm) + (lane >> 4);
-    if (text) vo = r * 256 + (((lane & 15) ^ (r & 15)) << 4);
+    if (text) vo = r * 256 + (((lane & 15) ^ row_swz<kV>(r)) << 4);
     if (kGen && kTokK && valid != ~0ull && !((valid >> r) & 1u)) vo &= 255u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (kL * wave + mm) * 1024), 16,
                                              vo, so, 0, 0);
@@ -224,11 +269,10 @@ __device__ __forceinline__ void scores(f32x16 (&s)[2], const uint8_t* sK, const 
     }
 }
 
-// kTok: Q, K and O are token-major [B, h, S, 128] (the query block is
+// kTok: Q, K, V and O are token-major [B, h, S, 128] (the query block is
 // gathered, the key blocks are gathered by the LDS loads and the output is
 // scattered directly); otherwise Q, K and O are tile-major
-// [B, h, n_rows, 128, 128].  V is always dim-major tiles: the P.V product
-// needs 8 consecutive keys of one channel per lane.
+// [B, h, n_rows, R, 128] and V is dim-major tiles [B, h, n_rows, 128, R].
 // kGen: the instance for ragged grids and joint text (masked partial blocks,
 // text blocks always kept, text query blocks dense); grids the block size
 // divides, without text, run the other instance.
@@ -271,8 +315,9 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
   // K: token-major (S rows per head) or tile-major (n_rows blocks per head)
   const uint8_t* kb = reinterpret_cast<const uint8_t*>(
       static_cast<const uint16_t*>(a.k_t) + bh * (kTok ? g.S * kHeadDim : g.n_rows * kTileElems));
-  const uint8_t* vb = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(a.v_t) +
-                                                       bh * g.n_rows * kTileElems);
+  // V: token-major like K, or dim-major tiles
+  const uint8_t* vb = reinterpret_cast<const uint8_t*>(
+      static_cast<const uint16_t*>(a.v_t) + bh * (kTok ? g.S * kHeadDim : g.n_rows * kTileElems));
   // The row's key blocks: the kept list (clip rows), then every text block;
   // a text query block, or dense attention, takes every block in order.
   const bool all_blocks = a.kv_cnt == nullptr || qtext;
@@ -306,7 +351,15 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kb), (short)0,
                                         (int)(kTok ? g.S * 256 : g.n_rows * Blk<kR>::kBytes),
                                         0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = head_rsrc<kR>(vb, g.n_rows);
+  const __amdgpu_buffer_rsrc_t vrs =
+      kTok ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vb), (short)0, (int)(g.S * 256),
+                                               0x00020000)
+           : head_rsrc<kR>(vb, g.n_rows);
+  // V operand reads: per-lane byte offsets within a V slot for channel block
+  // db (token-major V; see v_operand)
+  int vofs[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) vofs[db] = kTok ? v_lane_offset(lane, db) : 0;
   // Kept-block ids, 64 at a time: lane i holds entry ibase + i.
   int ibase = 0;
   int ids = (!all_blocks && lane < listed) ? idx[lane] : 0;
@@ -323,8 +376,12 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
   if (units > 0) {
     const int64_t j = block_at(0);
     valid_next = unit_valid<kGen, kR>(g, j, 0, lane);
-    dma_k<kTok, kGen, kR>(smem, krs, g, j, 0, wv, lane, valid_next, doff);
-    dma_v<kR>(smem + 2 * kSlotBytes, vrs, j, 0, wv, doff.v);
+    dma_rows<kTok, kGen, kR, false>(smem, krs, g, j, 0, wv, lane, valid_next, doff.k);
+    if (kTok)
+      dma_rows<kTok, kGen, kR, true>(smem + 2 * kSlotBytes, vrs, g, j, 0, wv, lane, valid_next,
+                                     doff.v);
+    else
+      dma_v<kR>(smem + 2 * kSlotBytes, vrs, j, 0, wv, doff.v);
   }
 
   for (int u = 0; u < units; ++u) {
@@ -336,9 +393,13 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
       const int64_t j = block_at((u + 1) / kUnits);
       const int p = (u + 1) % kUnits;
       valid_next = unit_valid<kGen, kR>(g, j, p, lane);
-      dma_k<kTok, kGen, kR>(smem + (1 - slot) * kSlotBytes, krs, g, j, p, wv, lane, valid_next,
-                            doff);
-      dma_v<kR>(smem + (3 - slot) * kSlotBytes, vrs, j, p, wv, doff.v);
+      dma_rows<kTok, kGen, kR, false>(smem + (1 - slot) * kSlotBytes, krs, g, j, p, wv, lane,
+                                      valid_next, doff.k);
+      if (kTok)
+        dma_rows<kTok, kGen, kR, true>(smem + (3 - slot) * kSlotBytes, vrs, g, j, p, wv, lane,
+                                       valid_next, doff.v);
+      else
+        dma_v<kR>(smem + (3 - slot) * kSlotBytes, vrs, j, p, wv, doff.v);
     }
     const uint8_t* sK = smem + slot * kSlotBytes;
     const uint8_t* sV = smem + (2 + slot) * kSlotBytes;
@@ -384,8 +445,7 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
     bf16x8 vr[kVAhead];
 #pragma unroll
     for (int i = 0; i < kVAhead; ++i)
-      vr[i] = *reinterpret_cast<const bf16x8*>(
-          sV + swz_v(32 * (i & 3) + l32, 4 * (i >> 3) + 2 * ((i >> 2) & 1) + hl));
+      vr[i] = v_operand<kTok>(sV, i >> 3, (i >> 2) & 1, i & 3, l32, hl, vofs[i & 3]);
 
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(kFenceKeepDs);
@@ -449,8 +509,7 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[i % kVAhead], pf[t][ks], o[db], 0, 0, 0);
       const int n = i + kVAhead;
       if (n < 16)
-        vr[i % kVAhead] = *reinterpret_cast<const bf16x8*>(
-            sV + swz_v(32 * (n & 3) + l32, 4 * (n >> 3) + 2 * ((n >> 2) & 1) + hl));
+        vr[i % kVAhead] = v_operand<kTok>(sV, n >> 3, (n >> 2) & 1, n & 3, l32, hl, vofs[n & 3]);
       __builtin_amdgcn_sched_barrier(kFenceKeepDs);
     }
     __builtin_amdgcn_s_setprio(0);

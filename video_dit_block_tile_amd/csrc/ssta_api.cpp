@@ -327,7 +327,7 @@ int attention_common(const ssta_geom_t* g, const ssta_params_t* p, const void* q
   SSTA_TRY(check_ptr(v_t, false));
   SSTA_TRY(check_ptr(o, false));
   SSTA_TRY(check_ptr(lse, true));
-  // One head's K (token-major or tiles) and V_t are addressed with 32-bit
+  // One head's K and V (token-major or tiles) are addressed with 32-bit
   // buffer offsets.
   if (geo.n_rows * int64_t(geo.R) * ssta::kHeadDim * 2 > 0x7FFFFFFF)
     return SSTA_ERR_SHAPE;
@@ -363,10 +363,10 @@ int ssta_attention_fwd(const ssta_geom_t* g, const ssta_params_t* p, const void*
 }
 
 int ssta_attention_fwd_tokens(const ssta_geom_t* g, const ssta_params_t* p, const void* q,
-                              const void* k, const void* v_t, const int32_t* kv_idx,
+                              const void* k, const void* v, const int32_t* kv_idx,
                               const int32_t* kv_cnt, int32_t max_kept_, void* o, float* lse,
                               void* stream) {
-  return attention_common(g, p, q, k, v_t, kv_idx, kv_cnt, max_kept_, o, lse, stream, 1);
+  return attention_common(g, p, q, k, v, kv_idx, kv_cnt, max_kept_, o, lse, stream, 1);
 }
 
 namespace {

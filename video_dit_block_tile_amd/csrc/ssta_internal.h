@@ -161,14 +161,14 @@ hipError_t launch_build_mask(const Geo& g, const MaskArgs& a, hipStream_t s);
 struct AttnArgs {
   const void* q_t;
   const void* k_t;
-  const void* v_t;
+  const void* v_t;          // token_io: token-major V; else dim-major tiles
   const int32_t* kv_idx;   // nullptr: dense
   const int32_t* kv_cnt;
   int32_t max_kept;
   void* o_t;
   float* lse;
   float scale_log2;        // softmax scale * log2(e)
-  int32_t token_io;        // 1: q_t, k_t, o_t are token-major [B, h, N, 128]
+  int32_t token_io;        // 1: q_t, k_t, v_t, o_t are token-major [B, h, S, 128]
 };
 hipError_t launch_attention(const Geo& g, const AttnArgs& a, hipStream_t s);
 

@@ -3,17 +3,18 @@
 ``SstaPlan`` allocates every buffer once for a geometry (PyTorch is only the
 allocator here) and ``run`` enqueues the steps.  Default (``fused_io=True``):
 
-  1. ssta_tile_pool            Q -> block means; K -> block means; V -> dim-major
-                               tiles V_t  (Step 1 + Step 2 pooling)
+  1. ssta_tile_pool            Q -> block means; K -> block means
+                               (Step 1 + Step 2 pooling)
   2. ssta_score_select         block means -> top-k key blocks per query block  (Step 2)
   3. ssta_build_mask           top-k + sliding-tile window -> kept lists  (Steps 3-4)
   4. ssta_attention_fwd_tokens block-sparse attention, gathering each query block
-                               and each kept key block from token order and
-                               writing O in token order  (Step 4)
+                               and each kept key block (K and V) from token
+                               order and writing O in token order  (Step 4)
 
 With ``fused_io=False`` the block gathers are materialised instead: step 1
-also writes tile-major Q_t and K_t, step 4 is ssta_attention_fwd, and
-ssta_tile_unpermute brings O_t back to token order.  Both give bit-identical O.
+also writes tile-major Q_t and K_t and dim-major V_t, step 4 is
+ssta_attention_fwd, and ssta_tile_unpermute brings O_t back to token order.
+Both give bit-identical O.
 
 A geometry with text_len > 0 describes a joint sequence (the clip's tokens,
 then the text's): the text is kept out of steps 2-3, and step 4 adds every
@@ -38,12 +39,12 @@ class SstaPlan:
         n, nr, R, D = g.n_tiles, g.n_rows, g.tile_tokens, g.head_dim
         bh = (g.batch, g.heads)
         if fused_io:
-            self.q_t = self.k_t = self.o_t = None
+            self.q_t = self.k_t = self.v_t = self.o_t = None
         else:
             self.q_t = torch.empty(bh + (nr, R, D), dtype=torch.bfloat16, device=dev)
             self.k_t = torch.empty_like(self.q_t)
             self.o_t = torch.empty_like(self.q_t)
-        self.v_t = torch.empty(bh + (nr, D, R), dtype=torch.bfloat16, device=dev)
+            self.v_t = torch.empty(bh + (nr, D, R), dtype=torch.bfloat16, device=dev)
         self.o = torch.empty(bh + (g.seq_len, D), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty(bh + (nr, R), dtype=torch.float32, device=dev)
         self.q_pooled = torch.empty(bh + (n, D), dtype=torch.float32, device=dev)
@@ -61,10 +62,11 @@ class SstaPlan:
     # individual steps -----------------------------------------------------
     def tile_pool(self, q, k, v, stream=None):
         g = self.geom
-        self._q, self._k = q, k
+        self._q, self._k, self._v = q, k, v
         L.ssta_tile_pool(g, q, self.q_t, L.LAYOUT_TOKEN_MAJOR, self.q_pooled, stream)
         L.ssta_tile_pool(g, k, self.k_t, L.LAYOUT_TOKEN_MAJOR, self.k_pooled, stream)
-        L.ssta_tile_pool(g, v, self.v_t, L.LAYOUT_DIM_MAJOR, None, stream)
+        if not self.fused_io:
+            L.ssta_tile_pool(g, v, self.v_t, L.LAYOUT_DIM_MAJOR, None, stream)
 
     def score_select(self, stream=None):
         """Block scores and per-query-block top-k (Step 2)."""
@@ -87,7 +89,7 @@ class SstaPlan:
         g, p = self.geom, self.params
         idx, cnt = (None, None) if dense else (self.kv_idx, self.kv_cnt)
         if self.fused_io:
-            L.ssta_attention_fwd_tokens(g, p, self._q, self._k, self.v_t, idx, cnt, self.o,
+            L.ssta_attention_fwd_tokens(g, p, self._q, self._k, self._v, idx, cnt, self.o,
                                         self.lse, stream)
         else:
             L.ssta_attention_fwd(g, p, self.q_t, self.k_t, self.v_t, idx, cnt, self.o_t,
