@@ -108,12 +108,14 @@ __device__ __forceinline__ int swz_v(int d, int chunk) {
 // transposing reads (ds_read_b64_tr_b16): within each group of 16 lanes, lane
 // j reads 4 channels of key j/4 of a 4-key row group, and lane i of the group
 // receives channel i of those 4 keys.  v_lane_offset gives this lane's byte
-// offset for the first 4 keys of the hl half (the second 4 keys lie 1 KB
-// further); with row & 3 = j/4 the swizzle only flips the 64-byte group.
-__device__ __forceinline__ int v_lane_offset(int lane, int db) {
+// offset for channel block 0 and the first 4 keys of the hl half (the second
+// 4 keys lie 1 KB further).  With row & 3 = j/4 the swizzle only flips the
+// 64-byte group, bits 6-7 of the offset, which hold db ^ j/4: channel block db
+// is at offset ^ (db << 6).
+__device__ __forceinline__ int v_lane_offset(int lane) {
   const int j = lane & 15, grp = (lane >> 4) & 1, hl = lane >> 5;
   const int kq = j >> 2;                                   // key within the 4-row group
-  const int chunk = 4 * (db ^ kq) + 2 * grp + ((j & 3) >> 1);   // swizzled 16-byte chunk
+  const int chunk = 4 * kq + 2 * grp + ((j & 3) >> 1);     // swizzled 16-byte chunk, db = 0
   return (8 * hl + kq) * 256 + chunk * 16 + 8 * (j & 1);
 }
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -123,7 +125,7 @@ __device__ __forceinline__ bf16x8 v_operand(const uint8_t* sV, int t, int ks, in
                                             int hl, int vofs) {
   if (!kTok)
     return *reinterpret_cast<const bf16x8*>(sV + swz_v(32 * db + l32, 4 * t + 2 * ks + hl));
-  const uint8_t* p = sV + vofs + (32 * t + 16 * ks) * 256;
+  const uint8_t* p = sV + (vofs ^ (db << 6)) + (32 * t + 16 * ks) * 256;
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 1024));
   const auto w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -216,7 +218,10 @@ __device__ __forceinline__ void dma_rows(uint8_t* dst, __amdgpu_buffer_rsrc_t rs
     uint32_t vo = offs[mm];
     const int r = 4 * (kL * wave + mm) + (lane >> 4);
     if (text) vo = r * 256 + (((lane & 15) ^ row_swz<kV>(r)) << 4);
-    if (kGen && kTokK && valid != ~0ull && !((valid >> r) & 1u)) vo &= 255u;
+    // (V rows need no redirect: a missing key's probability is exactly zero,
+    // and its row holds another token of the head or, past the head, the
+    // zeros of the range check)
+    if (!kV && kGen && kTokK && valid != ~0ull && !((valid >> r) & 1u)) vo &= 255u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (kL * wave + mm) * 1024), 16,
                                              vo, so, 0, 0);
   }
@@ -355,11 +360,9 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
       kTok ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vb), (short)0, (int)(g.S * 256),
                                                0x00020000)
            : head_rsrc<kR>(vb, g.n_rows);
-  // V operand reads: per-lane byte offsets within a V slot for channel block
-  // db (token-major V; see v_operand)
-  int vofs[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) vofs[db] = kTok ? v_lane_offset(lane, db) : 0;
+  // V operand reads: this lane's byte offset within a token-major V slot
+  // (see v_operand)
+  const int vofs = kTok ? v_lane_offset(lane) : 0;
   // Kept-block ids, 64 at a time: lane i holds entry ibase + i.
   int ibase = 0;
   int ids = (!all_blocks && lane < listed) ? idx[lane] : 0;
@@ -445,7 +448,7 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
     bf16x8 vr[kVAhead];
 #pragma unroll
     for (int i = 0; i < kVAhead; ++i)
-      vr[i] = v_operand<kTok>(sV, i >> 3, (i >> 2) & 1, i & 3, l32, hl, vofs[i & 3]);
+      vr[i] = v_operand<kTok>(sV, i >> 3, (i >> 2) & 1, i & 3, l32, hl, vofs);
 
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(kFenceKeepDs);
@@ -509,7 +512,7 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[i % kVAhead], pf[t][ks], o[db], 0, 0, 0);
       const int n = i + kVAhead;
       if (n < 16)
-        vr[i % kVAhead] = v_operand<kTok>(sV, n >> 3, (n >> 2) & 1, n & 3, l32, hl, vofs[n & 3]);
+        vr[i % kVAhead] = v_operand<kTok>(sV, n >> 3, (n >> 2) & 1, n & 3, l32, hl, vofs);
       __builtin_amdgcn_sched_barrier(kFenceKeepDs);
     }
     __builtin_amdgcn_s_setprio(0);
