@@ -245,9 +245,9 @@ int64_t ssta_attention_bwd_workspace_bytes(const ssta_geom_t* g);
  *   kv_idx, kv_cnt, max_kept: the forward's kept lists (NULL, NULL, 0: dense).
  *   dq, dk, dv out : bf16 [batch, heads, S, head_dim] (token-major).
  *   workspace: device scratch of ws_bytes >= ssta_attention_bwd_workspace_bytes()
- *              (dim-major copies of K, Q, dO; per-query (lse, D); the transposed
- *              lists and each head's key blocks ordered by how many query
- *              blocks keep them, which only schedules the dk/dv work).
+ *              (per-query (lse, D); the transposed lists and each head's key
+ *              blocks ordered by how many query blocks keep them, which only
+ *              schedules the dk/dv work).
  *              Caller-owned; contents on return are unspecified.
  * Probabilities and dS enter the matrix products as bf16, accumulation is fp32.
  * Errors: as ssta_attention_fwd, plus SSTA_ERR_WORKSPACE.

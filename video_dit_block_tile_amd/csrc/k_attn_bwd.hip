@@ -18,16 +18,19 @@
 //   k_attn_bwd_dq  per query block, over its kept key blocks in units of 32
 //                  keys: S^T = K Q^T and dP^T = V dO^T (Q, dO of the wave's 32
 //                  queries held in registers), dS^T in registers, then
-//                  dQ^T += K^T dS^T with K^T from dim-major tiles;
+//                  dQ^T += K^T dS^T with K^T read transposed from the K rows;
 //   k_attn_bwd_dv  per key block, over the query blocks that keep it, in
 //                  units of 32 queries: S = Q K^T (the wave's 32 keys held in
 //                  registers), P in registers, dV^T += dO^T P;
 //   k_attn_bwd_dk  per key block likewise: S = Q K^T, dP = dO V^T, dS in
 //                  registers, dK^T += Q^T dS.
+// The transposed operands (K^T, dO^T, Q^T: channel d of 8 consecutive rows)
+// come from the same token rows in LDS through the transposing reads
+// (ds_read_b64_tr_b16), so nothing is copied to a dim-major layout first.
 // dV and dK are separate kernels so that each keeps two waves per SIMD (their
 // fused accumulators would not fit 256 VGPRs).  Every streamed unit (token
-// rows gathered from token-major memory, 32-column slices of dim-major tiles,
-// and the per-query (lse*log2 e, D) pairs) goes straight into LDS with
+// rows gathered from token-major memory and the per-query (lse*log2 e, D)
+// pairs) goes straight into LDS with
 // buffer_load_dwordx4 ... lds into a two-slot ring, as in the forward kernel.
 //
 // Algorithmic work per kept (query block, key block) pair: five 128^3
@@ -50,7 +53,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-constexpr int kUnitBytes = 8192;                          // 32 rows, or 32 columns of a tile
+constexpr int kUnitBytes = 8192;                          // 32 token rows
 // Blocks hold kR = 128 or 64 tokens: a workgroup has kR/32 waves (32 rows of
 // the block each) and streams the other side in kR/32 units of 32 per block.
 template <int kR>
@@ -63,15 +66,42 @@ struct Blk {
 constexpr unsigned kWaitVm0 = 0x0F70;                     // s_waitcnt vmcnt(0)
 constexpr float kLog2e = 1.44269504088896340736f;
 
-// Unit of 32 token rows (256 B each): chunk c of row r sits at chunk c ^ (r % 16).
-__device__ __forceinline__ int swz_row(int row, int chunk) {
-  return row * 256 + ((chunk ^ (row & 15)) << 4);
+// Unit of 32 token rows (256 B each): 16-byte chunk c of row r sits at chunk
+// c ^ row_swz(r), row_swz(r) = 4*(r % 4) + (r / 4) % 4 (the two 2-bit fields of
+// r's low nibble swapped).  A unit is read two ways, both conflict-free: a
+// whole chunk per lane from 16 consecutive rows (a bijection on the low
+// nibble), and 8 bytes per lane from 4 consecutive rows by the transposing
+// reads (row_swz's upper bits differ across any 4 aligned rows).
+__device__ __forceinline__ int row_swz(int row) {
+  return ((row & 3) << 2) | ((row >> 2) & 3);
 }
-// Unit of 32 columns of a dim-major tile (128 channel rows of 64 B): chunk c
-// of row d sits at chunk c ^ ((d / 4) % 4), so 16 consecutive rows read one
-// chunk from 16 distinct bank groups.
-__device__ __forceinline__ int swz_col(int d, int chunk) {
-  return d * 64 + ((chunk ^ ((d >> 2) & 3)) << 4);
+__device__ __forceinline__ int swz_row(int row, int chunk) {
+  return row * 256 + ((chunk ^ row_swz(row)) << 4);
+}
+
+// The transposed operand from a row unit: for k-step ks and channel block db
+// lane (l32, hl) needs channel 32*db + l32 of the 8 rows 16ks + 8hl + (0..7),
+// which two transposing reads (ds_read_b64_tr_b16) give: within each group of
+// 16 lanes, lane j reads 4 channels (8 B) of row j/4 of a 4-row group, and
+// lane i receives channel i of those 4 rows.  row_t_base is this lane's byte
+// offset for ks = 0, db = 0 and the first 4 rows; channel block db flips bits
+// 6-7 (db << 6), the second 4 rows lie at (offset + 1 KB) ^ 16, and k-step ks
+// adds 16 rows (4 KB).
+__device__ __forceinline__ int row_t_base(int lane) {
+  const int j = lane & 15, grp = (lane >> 4) & 1, hl = lane >> 5;
+  const int kq = j >> 2;                         // row within the 4-row group
+  const int row = 8 * hl + kq;
+  const int chunk = (2 * grp + ((j & 3) >> 1)) ^ row_swz(row);   // channel chunk 2grp + ..
+  return row * 256 + chunk * 16 + 8 * (j & 1);
+}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ bf16x8 row_t_operand(const uint8_t* unit, int tb, int ks, int db) {
+  const int o0 = (tb ^ (db << 6)) + 4096 * ks;
+  const int o1 = ((tb + 1024) ^ 16 ^ (db << 6)) + 4096 * ks;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(unit + o0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(unit + o1));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
@@ -79,11 +109,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
                                            0x00020000);
 }
 
-// Per-lane source offsets of this wave's 1 KB loads of a row unit and of a
-// column unit (dim-major channel rows hold 2*kR bytes).
+// Per-lane source offsets of this wave's 1 KB loads of a row unit.
 template <int kR>
 struct UnitOffsets {
-  uint32_t rows[Blk<kR>::kLoads], cols[Blk<kR>::kLoads];
+  uint32_t rows[Blk<kR>::kLoads];
 };
 template <int kR>
 __device__ __forceinline__ UnitOffsets<kR> unit_offsets(const Geo& g, int wave, int lane) {
@@ -92,9 +121,7 @@ __device__ __forceinline__ UnitOffsets<kR> unit_offsets(const Geo& g, int wave, 
   for (int mm = 0; mm < Blk<kR>::kLoads; ++mm) {
     const int b = Blk<kR>::kLoads * wave + mm;     // 1 KB destination block 0..7
     const int row = 4 * b + (lane >> 4);           // token rows 4b .. 4b+3
-    o.rows[mm] = in_block_offset(g, row) * 256 + (((lane & 15) ^ (row & 15)) << 4);
-    const int d = 16 * b + (lane >> 2);            // channel rows 16b .. 16b+15
-    o.cols[mm] = d * (2 * kR) + (((lane & 3) ^ ((d >> 2) & 3)) << 4);
+    o.rows[mm] = in_block_offset(g, row) * 256 + (((lane & 15) ^ row_swz(row)) << 4);
   }
   return o;
 }
@@ -119,7 +146,7 @@ __device__ __forceinline__ uint32_t rows_valid(const Geo& g, uint32_t j, int p, 
 // Rows 32p .. 32p+31 of block j, gathered from token-major memory.  A row
 // whose position does not exist (bit clear in `valid`) is read from the
 // block's first token instead, so every score it enters stays bounded by
-// the row's log-sum-exp; its dim-major column is zero, so it adds nothing.
+// the row's log-sum-exp; the kernels zero its dS or P, so it adds nothing.
 // A text block's rows are consecutive tokens.
 template <bool kGen, int kR>
 __device__ __forceinline__ void dma_rows(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, const Geo& g,
@@ -135,23 +162,11 @@ __device__ __forceinline__ void dma_rows(uint8_t* dst, __amdgpu_buffer_rsrc_t rs
 #pragma unroll
   for (int mm = 0; mm < kL; ++mm) {
     const int r = 4 * (kL * wave + mm) + (lane >> 4);
-    uint32_t vo = text ? r * 256 + (((lane & 15) ^ (r & 15)) << 4) : off.rows[mm];
+    uint32_t vo = text ? r * 256 + (((lane & 15) ^ row_swz(r)) << 4) : off.rows[mm];
     if (part) vo = ((valid >> r) & 1u) ? vo + half : (vo & 255u);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (kL * wave + mm) * 1024), 16,
                                              vo, so, 0, 0);
   }
-}
-// Columns 32p .. 32p+31 of dim-major block j (offc: the column offsets of a
-// UnitOffsets<kR>).
-template <int kR>
-__device__ __forceinline__ void dma_cols(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, uint32_t j,
-                                         int p, int wave, const uint32_t* offc) {
-  constexpr int kL = Blk<kR>::kLoads;
-  const uint32_t so = j * (uint32_t)Blk<kR>::kBytes + 64u * p;
-#pragma unroll
-  for (int mm = 0; mm < kL; ++mm)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (kL * wave + mm) * 1024), 16,
-                                             offc[mm], so, 0, 0);
 }
 
 // Token (within its head) of position r of block j, or of the block's first
@@ -210,8 +225,8 @@ template <bool kGen, int kR>
 __global__ __launch_bounds__(kR * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void k_attn_bwd_dq(Geo g, BwdArgs a, AttnGrid grid) {
   constexpr int kUnits = Blk<kR>::kUnits;
-  // slot s (24 KB): K rows | V rows | K^T columns of one 32-key unit
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 3 * kUnitBytes];
+  // slot s (16 KB): K rows | V rows of one 32-key unit
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * kUnitBytes];
   int64_t bh, qi;
   if (!attn_block<kGen>(g, grid, blockIdx.x, bh, qi)) return;
   const int64_t row = bh * g.n_rows + qi;
@@ -249,17 +264,15 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, AttnGrid grid) {
   IdStream ids;
   ids.init(all_blocks ? nullptr : a.kv_idx + kvrow * a.max_kept, listed, all_blocks, lane);
   const UnitOffsets<kR> off = unit_offsets<kR>(g, wv, lane);
-  // token-major: S rows of 256 B per head; dim-major: n_rows blocks
+  const int tb = row_t_base(lane);
+  // token-major: S rows of 256 B per head
   const int64_t tok_bytes = g.S * (int64_t)(kHeadDim * 2);
-  const int64_t head_bytes = g.n_rows * (int64_t)Blk<kR>::kBytes;
   const __amdgpu_buffer_rsrc_t krs = rsrc(static_cast<const uint16_t*>(a.k) + head * kHeadDim,
                                           tok_bytes);
   const __amdgpu_buffer_rsrc_t vrs = rsrc(static_cast<const uint16_t*>(a.v) + head * kHeadDim,
                                           tok_bytes);
-  const __amdgpu_buffer_rsrc_t ktrs = rsrc(
-      static_cast<const uint16_t*>(a.k_cols) + bh * g.n_rows * (int64_t)kR * kHeadDim,
-      head_bytes);
-  auto load_unit = [&](int u, uint8_t* dst) {
+  // returns which of the unit's 32 keys exist
+  auto load_unit = [&](int u, uint8_t* dst) -> uint32_t {
     const int pos = u / kUnits;
     const uint32_t j = kGen && pos >= listed && !all_blocks
                            ? (uint32_t)(g.n_tiles + pos - listed)
@@ -268,19 +281,20 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, AttnGrid grid) {
     const uint32_t valid = rows_valid<kGen, kR>(g, j, p, lane);
     dma_rows<kGen, kR>(dst, krs, g, j, p, wv, lane, valid, off);
     dma_rows<kGen, kR>(dst + kUnitBytes, vrs, g, j, p, wv, lane, valid, off);
-    dma_cols<kR>(dst + 2 * kUnitBytes, ktrs, j, p, wv, off.cols);
+    return valid;
   };
 
   const int units = kUnits * cnt;
-  if (units > 0) load_unit(0, smem);
+  uint32_t valid_next = ~0u;
+  if (units > 0) valid_next = load_unit(0, smem);
   for (int u = 0; u < units; ++u) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
-    uint8_t* cur = smem + (u & 1) * 3 * kUnitBytes;
-    if (u + 1 < units) load_unit(u + 1, smem + ((u + 1) & 1) * 3 * kUnitBytes);
+    uint8_t* cur = smem + (u & 1) * 2 * kUnitBytes;
+    const uint32_t valid = valid_next;
+    if (u + 1 < units) valid_next = load_unit(u + 1, smem + ((u + 1) & 1) * 2 * kUnitBytes);
     const uint8_t* sK = cur;
     const uint8_t* sV = cur + kUnitBytes;
-    const uint8_t* sKT = cur + 2 * kUnitBytes;
 
     // S^T and dP^T for the unit's 32 keys: register r of lane (l32, hl) is
     // query l32 and key 16*(r/8) + 8*hl + r%8.
@@ -294,7 +308,8 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, AttnGrid grid) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[st], dp, 0, 0, 0);
     }
-    // dS^T = P^T (dP^T - D), as the B operand of k-step ks (keys 16*ks + 8*hl + e).
+    // dS^T = P^T (dP^T - D), as the B operand of k-step ks (keys 16*ks + 8*hl + e);
+    // zero for a key its block lacks (its row holds the block's first token).
     bf16x8 dsf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -302,15 +317,17 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, AttnGrid grid) {
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * ks + e;
         const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
-        dsf[ks][e] = (__bf16)(pr * (dp[r] - dq_d));
+        float ds = pr * (dp[r] - dq_d);
+        if (kGen && !((valid >> (16 * ks + 8 * hl + e)) & 1u)) ds = 0.0f;
+        dsf[ks][e] = (__bf16)ds;
       }
-    // dQ^T += K^T dS^T: A operand row d of K^T, the same 8 keys.
+    // dQ^T += K^T dS^T: A operand row d of K^T, the same 8 keys, read
+    // transposed from the K rows.
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const bf16x8 kt =
-            *reinterpret_cast<const bf16x8*>(sKT + swz_col(32 * db + l32, 2 * ks + hl));
+        const bf16x8 kt = row_t_operand(sK, tb, ks, db);
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsf[ks], acc[db], 0, 0, 0);
       }
   }
@@ -324,9 +341,9 @@ template <bool kDK, bool kGen, int kR>
 __global__ __launch_bounds__(kR * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void k_attn_bwd_kv(Geo g, BwdArgs a, AttnGrid grid) {
   constexpr int kUnits = Blk<kR>::kUnits;
-  // slot: Q rows | (dK: dO rows) | columns (dV: dO^T, dK: Q^T) | 32 (lse2, D) pairs
-  constexpr int kParts = kDK ? 3 : 2;
-  constexpr int kSlot = kParts * kUnitBytes + 256;
+  // slot: Q rows | dO rows | 32 (lse2, D) pairs; dO^T (dV) and Q^T (dK) are
+  // read transposed from the rows
+  constexpr int kSlot = 2 * kUnitBytes + 256;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kSlot];
   // text key blocks (kept by every query block) first; then, with the kept
   // lists, each head's key blocks longest first (k_order_blocks), dealt
@@ -374,18 +391,16 @@ void k_attn_bwd_kv(Geo g, BwdArgs a, AttnGrid grid) {
   IdStream ids;
   ids.init(all_blocks ? nullptr : a.q_idx + klist * a.q_width, listed, all_blocks, lane);
   const UnitOffsets<kR> off = unit_offsets<kR>(g, wv, lane);
+  const int tb = row_t_base(lane);
   const int64_t tok_bytes = g.S * (int64_t)(kHeadDim * 2);
-  const int64_t head_bytes = g.n_rows * (int64_t)Blk<kR>::kBytes;
   const __amdgpu_buffer_rsrc_t qrs = rsrc(static_cast<const uint16_t*>(a.q) + head * kHeadDim,
                                           tok_bytes);
   const __amdgpu_buffer_rsrc_t drs = rsrc(static_cast<const uint16_t*>(a.dout) + head * kHeadDim,
                                           tok_bytes);
-  const int64_t cols_off = bh * g.n_rows * (int64_t)kR * kHeadDim;
-  const __amdgpu_buffer_rsrc_t crs =
-      rsrc(static_cast<const uint16_t*>(kDK ? a.q_cols : a.dout_cols) + cols_off, head_bytes);
   const __amdgpu_buffer_rsrc_t lrs =
       rsrc(a.ld + bh * g.n_rows * kR * 2, g.n_rows * kR * 8);
-  auto load_unit = [&](int u, uint8_t* dst) {
+  // returns which of the unit's 32 queries exist
+  auto load_unit = [&](int u, uint8_t* dst) -> uint32_t {
     const int pos = u / kUnits;
     const uint32_t i = kGen && pos >= listed && !all_blocks
                            ? (uint32_t)(g.n_tiles + pos - listed)
@@ -393,25 +408,26 @@ void k_attn_bwd_kv(Geo g, BwdArgs a, AttnGrid grid) {
     const int p = u % kUnits;
     const uint32_t valid = rows_valid<kGen, kR>(g, i, p, lane);
     dma_rows<kGen, kR>(dst, qrs, g, i, p, wv, lane, valid, off);
-    if (kDK) dma_rows<kGen, kR>(dst + kUnitBytes, drs, g, i, p, wv, lane, valid, off);
-    dma_cols<kR>(dst + (kParts - 1) * kUnitBytes, crs, i, p, wv, off.cols);
+    dma_rows<kGen, kR>(dst + kUnitBytes, drs, g, i, p, wv, lane, valid, off);
     if (wv == 0 && lane < 16)   // 32 (lse2, D) pairs = 256 B
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          lrs, (lds_u8*)(dst + kParts * kUnitBytes), 16, (uint32_t)lane * 16,
+          lrs, (lds_u8*)(dst + 2 * kUnitBytes), 16, (uint32_t)lane * 16,
           (i * (uint32_t)kR + 32u * p) * 8u, 0, 0);
+    return valid;
   };
 
   const int units = kUnits * cnt;
-  if (units > 0) load_unit(0, smem);
+  uint32_t valid_next = ~0u;
+  if (units > 0) valid_next = load_unit(0, smem);
   for (int u = 0; u < units; ++u) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     uint8_t* cur = smem + (u & 1) * kSlot;
-    if (u + 1 < units) load_unit(u + 1, smem + ((u + 1) & 1) * kSlot);
+    const uint32_t valid = valid_next;
+    if (u + 1 < units) valid_next = load_unit(u + 1, smem + ((u + 1) & 1) * kSlot);
     const uint8_t* sQ = cur;
     const uint8_t* sD = cur + kUnitBytes;
-    const uint8_t* sC = cur + (kParts - 1) * kUnitBytes;
-    const float* sL = reinterpret_cast<const float*>(cur + kParts * kUnitBytes);
+    const float* sL = reinterpret_cast<const float*>(cur + 2 * kUnitBytes);
 
     // S (queries x keys, lane = key l32): register r is query 16*(r/8) + 8*hl + r%8.
     f32x16 s, dp;
@@ -426,7 +442,8 @@ void k_attn_bwd_kv(Geo g, BwdArgs a, AttnGrid grid) {
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[st], dp, 0, 0, 0);
       }
     }
-    // P (dV) or dS (dK) as the B operand of k-step ks (queries 16*ks + 8*hl + e).
+    // P (dV) or dS (dK) as the B operand of k-step ks (queries 16*ks + 8*hl + e);
+    // zero for a query its block lacks (its rows hold the block's first token).
     bf16x8 bf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -439,21 +456,22 @@ void k_attn_bwd_kv(Geo g, BwdArgs a, AttnGrid grid) {
         const int r = 8 * ks + e;
         const float lse2 = lv[e >> 1][(e & 1) * 2];
         const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
+        float w = pr;
         if (kDK) {
           const float dd = lv[e >> 1][(e & 1) * 2 + 1];
-          bf[ks][e] = (__bf16)(pr * (dp[r] - dd));
-        } else {
-          bf[ks][e] = (__bf16)pr;
+          w = pr * (dp[r] - dd);
         }
+        if (kGen && !((valid >> (16 * ks + 8 * hl + e)) & 1u)) w = 0.0f;
+        bf[ks][e] = (__bf16)w;
       }
     }
-    // dV^T += dO^T P  or  dK^T += Q^T dS: A operand row d, the same 8 queries.
+    // dV^T += dO^T P  or  dK^T += Q^T dS: A operand row d, the same 8 queries,
+    // read transposed from the dO or Q rows.
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const bf16x8 ca =
-            *reinterpret_cast<const bf16x8*>(sC + swz_col(32 * db + l32, 2 * ks + hl));
+        const bf16x8 ca = row_t_operand(kDK ? sQ : sD, tb, ks, db);
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca, bf[ks], acc[db], 0, 0, 0);
       }
   }

@@ -371,18 +371,14 @@ int ssta_attention_fwd_tokens(const ssta_geom_t* g, const ssta_params_t* p, cons
 
 namespace {
 struct BwdLayout {
-  int64_t k_cols, q_cols, d_cols, ld, mask, q_idx, q_cnt, order, total;
+  int64_t ld, mask, q_idx, q_cnt, order, total;
 };
 BwdLayout bwd_layout(const Geo& g) {
   BwdLayout w;
-  // dim-major copies and (lse, D) pairs cover every block (text included);
-  // the transposed lists cover the clip's key blocks
-  const int64_t tensor = g.bh * g.n_rows * int64_t(g.R) * ssta::kHeadDim * 2;
+  // (lse, D) pairs cover every block (text included); the transposed lists
+  // cover the clip's key blocks
   const int64_t rows = g.bh * g.n_tiles;
-  w.k_cols = 0;
-  w.q_cols = w.k_cols + align256(tensor);
-  w.d_cols = w.q_cols + align256(tensor);
-  w.ld = w.d_cols + align256(tensor);
+  w.ld = 0;
   w.mask = w.ld + align256(g.bh * g.n_rows * g.R * 8);
   w.q_idx = w.mask + align256(rows * ((g.n_tiles + 31) / 32) * 4);
   w.q_cnt = w.q_idx + align256(rows * g.n_tiles * 4);
@@ -425,12 +421,6 @@ int ssta_attention_bwd(const ssta_geom_t* g, const ssta_params_t* p, const void*
   SSTA_TRY(check_device());
   hipStream_t st = as_stream(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  SSTA_TRY(hip_status(ssta::launch_tile_pool(geo, k, ws + lay.k_cols, SSTA_LAYOUT_DIM_MAJOR,
-                                             nullptr, st)));
-  SSTA_TRY(hip_status(ssta::launch_tile_pool(geo, q, ws + lay.q_cols, SSTA_LAYOUT_DIM_MAJOR,
-                                             nullptr, st)));
-  SSTA_TRY(hip_status(ssta::launch_tile_pool(geo, dout, ws + lay.d_cols, SSTA_LAYOUT_DIM_MAJOR,
-                                             nullptr, st)));
   float* ld = reinterpret_cast<float*>(ws + lay.ld);
   SSTA_TRY(hip_status(ssta::launch_attention_bwd_prep(geo, o, dout, lse, ld, st)));
   int32_t* q_idx = reinterpret_cast<int32_t*>(ws + lay.q_idx);
@@ -445,9 +435,6 @@ int ssta_attention_bwd(const ssta_geom_t* g, const ssta_params_t* p, const void*
   a.k = k;
   a.v = v;
   a.dout = dout;
-  a.k_cols = ws + lay.k_cols;
-  a.q_cols = ws + lay.q_cols;
-  a.dout_cols = ws + lay.d_cols;
   a.ld = ld;
   a.kv_idx = kv_idx;
   a.kv_cnt = kv_cnt;

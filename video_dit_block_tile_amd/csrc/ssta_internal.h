@@ -178,9 +178,6 @@ struct BwdArgs {
   const void* k;
   const void* v;
   const void* dout;
-  const void* k_cols;     // dim-major tiles bf16 [bh][n][128 ch][128 tok]
-  const void* q_cols;
-  const void* dout_cols;
   const float* ld;        // [bh][n][128][2]: (lse * log2(e), D = dO . O) per query
   const int32_t* kv_idx;  // query block -> kept key blocks (NULL: dense)
   const int32_t* kv_cnt;
