@@ -42,7 +42,7 @@
 // and taken out with v_readlane, so no per-unit global load sits on the
 // critical path.
 // LDS operand reads are issued ahead of their products (up to 8 for K, the
-// first 8 V^T operands before the softmax), held in place by scheduling
+// first 8 V operands before the softmax), held in place by scheduling
 // fences; waves raise their issue priority around the matrix-core sections.
 // Softmax: the running max m is raised only when the probabilities formed
 // with the current m would exceed 2^32 on some lane (always on a row's first
@@ -51,7 +51,7 @@
 // same weights the P.V product uses).
 //
 // Work per kept pair: 4*128^3 = 8.39 MFLOP on the matrix cores, 64 KB of
-// K/V^T reads.  Bound: bf16 MFMA throughput (and the fp32 softmax that must
+// K and V reads.  Bound: bf16 MFMA throughput (and the fp32 softmax that must
 // overlap it).
 #include "ssta_internal.h"
 
@@ -72,7 +72,7 @@ struct Blk {
   static constexpr int kUnits = kR / 64;              // 64-key units per block
   static constexpr int kBytes = kR * kHeadDim * 2;    // one block of one tensor
 };
-constexpr int kSlotBytes = 16384;                     // one unit of 64 keys: 16 KB of K or V^T
+constexpr int kSlotBytes = 16384;                     // one unit of 64 keys: 16 KB of K or V
 constexpr unsigned kWaitVm0 = 0x0F70;                    // s_waitcnt vmcnt(0)
 // Scheduling fence that lets vector, scalar and transcendental ALU
 // instructions move across it but keeps matrix, LDS and global memory
@@ -255,25 +255,6 @@ __device__ __forceinline__ void dma_v(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, i
                                              offv[mm], so, 0, 0);
 }
 
-// S^T for the 64 keys of a K slot: the A operand row of lane l32 is key
-// kperm(l32) (bits 2 and 3 of l32 swapped), so output register r of lane
-// (l32, hl) of s[t] holds query l32 and key 32*t + 16*(r/8) + 8*hl + r%8: each
-// group of 8 registers is 8 consecutive keys.
-__device__ __forceinline__ void scores(f32x16 (&s)[2], const uint8_t* sK, const bf16x8 (&qf)[8],
-                                       int kperm, int hl) {
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
-#pragma unroll
-  for (int st = 0; st < 8; ++st)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(sK + swz_k(32 * t + kperm, 2 * st + hl));
-      s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s[t], 0, 0, 0);
-    }
-}
-
 // kTok: Q, K, V and O are token-major [B, h, S, 128] (the query block is
 // gathered, the key blocks are gathered by the LDS loads and the output is
 // scattered directly); otherwise Q, K and O are tile-major
@@ -287,7 +268,7 @@ __device__ __forceinline__ void scores(f32x16 (&s)[2], const uint8_t* sK, const 
 template <bool kTok, bool kGen, int kR>
 __global__ __launch_bounds__(kR * 2) __attribute__((amdgpu_waves_per_eu(kR == 128 ? 2 : 1)))
 void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
-  // K slots at 0 and 16 KB, V^T slots at 32 and 48 KB.
+  // K slots at 0 and 16 KB, V (or V^T) slots at 32 and 48 KB.
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kSlotBytes];
 
   // Text query blocks first, then head-synchronous XCD slices of the clip
@@ -348,7 +329,7 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // Unit u = keys 64*(u%kUnits) .. of the (u/kUnits)-th kept block, in slot
-  // u%2 of the K and V^T rings; unit u+1 is loaded while unit u is computed.
+  // u%2 of the K and V rings; unit u+1 is loaded while unit u is computed.
   const int units = kUnits * cnt;
   const DmaOffsets<kR> doff = dma_offsets<kTok, kR>(g, wv, lane);
   // token-major K spans S rows of 256 B; tiles span n_rows x 32 KB
@@ -409,6 +390,10 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
 
     // S^T: 16 products in the order (st, t); their K operands are read
     // kKAhead products ahead so the LDS latency overlaps the matrix cores.
+    // The A operand row of lane l32 is key kperm(l32), so output register r
+    // of lane (l32, hl) of s[t] holds query l32 and key
+    // 32*t + 16*(r/8) + 8*hl + r%8: each group of 8 registers is 8
+    // consecutive keys.
     constexpr int kKAhead = 8;
     __builtin_amdgcn_s_setprio(1);
     f32x16 s[2];
@@ -442,7 +427,7 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
           if (!((vl >> (32 * t + 16 * (r >> 3) + (r & 7))) & 1u)) s[t][r] = -1.0e30f;
     }
 
-    // V^T operands of the first kVAhead P.V products (order (t, ks, db)),
+    // V operands of the first kVAhead P.V products (order (t, ks, db)),
     // requested before the softmax so they arrive while it runs.
     constexpr int kVAhead = 8;
     bf16x8 vr[kVAhead];
@@ -504,8 +489,8 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
     l += lu;
 
     __builtin_amdgcn_s_setprio(1);
-    // O^T += V^T P^T in the order (t, ks, db); A operand: row d of V^T, the
-    // same 8 consecutive keys (chunk 4*t + 2*ks + hl of the unit's keys).
+    // O^T += V^T P^T in the order (t, ks, db); A operand: channel d of the
+    // same 8 consecutive keys 32t + 16ks + 8hl + (0..7) (see v_operand).
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int t = i >> 3, ks = (i >> 2) & 1, db = i & 3;
