@@ -226,28 +226,31 @@ __global__ __launch_bounds__(256) void k_topk(Geo g, const float* __restrict__ s
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int lane = threadIdx.x & 63;
-  const int64_t n = g.n_tiles;
-  const int64_t i = row % n;
+  const int n = (int)g.n_tiles;                 // at most kMaxTopkTiles (host check)
   const float* s = scores + row * n;
-  const int ti = (int)(i / ((int64_t)g.ny * g.nx)), yi = (int)((i / g.nx) % g.ny),
-            xi = (int)(i % g.nx);
+  // All E loads are issued before any is used: a lane past the row's end
+  // reads the row's last score (in bounds) and drops it.
+  float v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e] = s[min(lane + 64 * e, n - 1)];
   uint32_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = lane + 64 * e < n ? order_key(v[e]) : 0u;
+  if (excl) {
+    // top-k outside the window: blocks inside query block i's window are
+    // not candidates
+    const int i = (int)(row % n), nyx = g.ny * g.nx;
+    const int ti = i / nyx, yi = (i / g.nx) % g.ny, xi = i % g.nx;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = lane + 64 * e;
+      const int tj = j / nyx, yj = (j / g.nx) % g.ny, xj = j % g.nx;
+      if (abs(tj - ti) <= wt && abs(yj - yi) <= wh && abs(xj - xi) <= ww) key[e] = 0u;
+    }
+  }
   int ncand = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int64_t j = lane + 64 * e;
-    uint32_t kk = 0u;
-    if (j < n) {
-      kk = order_key(s[j]);
-      if (excl) {
-        const int tj = (int)(j / ((int64_t)g.ny * g.nx)), yj = (int)((j / g.nx) % g.ny),
-                  xj = (int)(j % g.nx);
-        if (abs(tj - ti) <= wt && abs(yj - yi) <= wh && abs(xj - xi) <= ww) kk = 0u;
-      }
-    }
-    key[e] = kk;
-    ncand += __popcll(__ballot(kk != 0u));
-  }
+  for (int e = 0; e < E; ++e) ncand += __popcll(__ballot(key[e] != 0u));
   const int want = min(min(k, width), ncand);
   int32_t* o = out + row * width;
   int pos = 0;
