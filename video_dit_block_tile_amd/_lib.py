@@ -49,7 +49,7 @@ class SstaGeom(ctypes.Structure):
 
     @property
     def n_rows(self) -> int:
-        """Blocks per (batch, head): the clip's n_tiles, then the text's 128-token blocks."""
+        """Blocks per (batch, head): the clip's n_tiles, then the text's blocks of tile_tokens."""
         return self.n_tiles + -(-self.text_len // self.tile_tokens)
 
     @property
@@ -182,6 +182,29 @@ def _tiled_shape(g):
     return (g.batch, g.heads, g.n_rows, g.tile_tokens, g.head_dim)
 
 
+def _kept_lists(g, kv_idx, kv_cnt) -> int:
+    """Checks the kept lists and returns their row stride max_kept (0: dense,
+    both None)."""
+    if kv_cnt is None:
+        if kv_idx is not None:
+            raise ValueError("dense attention takes neither kv_idx nor kv_cnt")
+        return 0
+    if not isinstance(kv_idx, torch.Tensor) or kv_idx.dim() != 4:
+        raise ValueError("kv_idx must be an int32 [B, h, n_tiles, max_kept] tensor with kv_cnt")
+    _expect("kv_cnt", kv_cnt, (g.batch, g.heads, g.n_tiles), torch.int32)
+    mk = kv_idx.shape[-1]
+    _expect("kv_idx", kv_idx, (g.batch, g.heads, g.n_tiles, mk), torch.int32)
+    return mk
+
+
+def _workspace(workspace) -> int:
+    """Checks a device byte buffer and returns its size."""
+    if not isinstance(workspace, torch.Tensor):
+        raise ValueError("workspace must be a uint8 device tensor")
+    _expect("workspace", workspace, (workspace.numel(),), torch.uint8)
+    return workspace.numel()
+
+
 # ------------------------------------------------------------------ entry points
 
 def ssta_block_rows(g: SstaGeom) -> int:
@@ -239,9 +262,9 @@ def ssta_score_select(g: SstaGeom, p: SstaParams, q_pooled, k_pooled, topk_idx, 
     _expect("k_pooled", k_pooled, pshape, torch.float32)
     _expect("topk_idx", topk_idx, (g.batch, g.heads, g.n_tiles, ssta_topk_width(g, p)),
             torch.int32)
-    _expect("workspace", workspace, (workspace.numel(),), torch.uint8)
+    ws_bytes = _workspace(workspace)
     _call("ssta_score_select", ctypes.byref(g), ctypes.byref(p), _ptr(q_pooled), _ptr(k_pooled),
-          _ptr(topk_idx), _ptr(workspace), workspace.numel(), _stream(stream))
+          _ptr(topk_idx), _ptr(workspace), ws_bytes, _stream(stream))
 
 
 def ssta_scores(g: SstaGeom, p: SstaParams, q_pooled, k_pooled, scores, red, workspace,
@@ -251,9 +274,9 @@ def ssta_scores(g: SstaGeom, p: SstaParams, q_pooled, k_pooled, scores, red, wor
     _expect("k_pooled", k_pooled, pshape, torch.float32)
     _expect("scores", scores, (g.batch, g.heads, g.n_tiles, g.n_tiles), torch.float32)
     _expect("red", red, (g.batch, g.heads, g.n_tiles), torch.float32, allow_none=True)
-    _expect("workspace", workspace, (workspace.numel(),), torch.uint8)
+    ws_bytes = _workspace(workspace)
     _call("ssta_scores", ctypes.byref(g), ctypes.byref(p), _ptr(q_pooled), _ptr(k_pooled),
-          _ptr(scores), _ptr(red), _ptr(workspace), workspace.numel(), _stream(stream))
+          _ptr(scores), _ptr(red), _ptr(workspace), ws_bytes, _stream(stream))
 
 
 def ssta_build_mask(g: SstaGeom, p: SstaParams, topk_idx, kv_idx, kv_cnt, bitmask=None,
@@ -278,14 +301,7 @@ def ssta_attention_fwd(g: SstaGeom, p: SstaParams, q_t, k_t, v_t, kv_idx, kv_cnt
     _expect("o_t", o_t, _tiled_shape(g), torch.bfloat16)
     _expect("lse", lse, (g.batch, g.heads, g.n_rows, g.tile_tokens), torch.float32,
             allow_none=True)
-    if kv_cnt is None:
-        if kv_idx is not None:
-            raise ValueError("dense attention takes neither kv_idx nor kv_cnt")
-        mk = 0
-    else:
-        _expect("kv_cnt", kv_cnt, (g.batch, g.heads, g.n_tiles), torch.int32)
-        mk = kv_idx.shape[-1]
-        _expect("kv_idx", kv_idx, (g.batch, g.heads, g.n_tiles, mk), torch.int32)
+    mk = _kept_lists(g, kv_idx, kv_cnt)
     _call("ssta_attention_fwd", ctypes.byref(g), ctypes.byref(p), _ptr(q_t), _ptr(k_t), _ptr(v_t),
           _ptr(kv_idx), _ptr(kv_cnt), mk, _ptr(o_t), _ptr(lse), _stream(stream))
 
@@ -301,14 +317,7 @@ def ssta_attention_fwd_tokens(g: SstaGeom, p: SstaParams, q, k, v, kv_idx, kv_cn
     _expect("o", o, tok, torch.bfloat16)
     _expect("lse", lse, (g.batch, g.heads, g.n_rows, g.tile_tokens), torch.float32,
             allow_none=True)
-    if kv_cnt is None:
-        if kv_idx is not None:
-            raise ValueError("dense attention takes neither kv_idx nor kv_cnt")
-        mk = 0
-    else:
-        _expect("kv_cnt", kv_cnt, (g.batch, g.heads, g.n_tiles), torch.int32)
-        mk = kv_idx.shape[-1]
-        _expect("kv_idx", kv_idx, (g.batch, g.heads, g.n_tiles, mk), torch.int32)
+    mk = _kept_lists(g, kv_idx, kv_cnt)
     _call("ssta_attention_fwd_tokens", ctypes.byref(g), ctypes.byref(p), _ptr(q), _ptr(k),
           _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), mk, _ptr(o), _ptr(lse), _stream(stream))
 
@@ -331,20 +340,14 @@ def ssta_attention_bwd_workspace_bytes(g: SstaGeom) -> int:
 def ssta_attention_bwd(g: SstaGeom, p: SstaParams, q, k, v, o, dout, lse, kv_idx, kv_cnt, dq, dk,
                        dv, workspace, stream=None):
     """Gradients of the block-sparse attention with the kept lists fixed; all
-    tensors token-major bf16 [B, h, N, 128] except lse (tile-major fp32)."""
+    tensors token-major bf16 [B, h, S, 128] except lse (tile-major fp32)."""
     tok = (g.batch, g.heads, g.seq_len, g.head_dim)
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
                     ("dk", dk), ("dv", dv)):
         _expect(name, t, tok, torch.bfloat16)
     _expect("lse", lse, (g.batch, g.heads, g.n_rows, g.tile_tokens), torch.float32)
-    if kv_cnt is None:
-        if kv_idx is not None:
-            raise ValueError("dense attention takes neither kv_idx nor kv_cnt")
-        mk = 0
-    else:
-        _expect("kv_cnt", kv_cnt, (g.batch, g.heads, g.n_tiles), torch.int32)
-        mk = kv_idx.shape[-1]
-        _expect("kv_idx", kv_idx, (g.batch, g.heads, g.n_tiles, mk), torch.int32)
+    mk = _kept_lists(g, kv_idx, kv_cnt)
+    ws_bytes = _workspace(workspace)
     _call("ssta_attention_bwd", ctypes.byref(g), ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
           _ptr(o), _ptr(dout), _ptr(lse), _ptr(kv_idx), _ptr(kv_cnt), mk, _ptr(dq), _ptr(dk),
-          _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream))
+          _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream))
