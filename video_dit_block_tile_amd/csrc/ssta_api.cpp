@@ -317,14 +317,14 @@ int ssta_build_mask(const ssta_geom_t* g, const ssta_params_t* p, const int32_t*
 
 namespace {
 int attention_common(const ssta_geom_t* g, const ssta_params_t* p, const void* q, const void* k,
-                     const void* v_t, const int32_t* kv_idx, const int32_t* kv_cnt,
+                     const void* v, const int32_t* kv_idx, const int32_t* kv_cnt,
                      int32_t max_kept_, void* o, float* lse, void* stream, int token_io) {
   Geo geo;
   SSTA_TRY(check_geom(g, &geo));
   SSTA_TRY(check_params(p));
   SSTA_TRY(check_ptr(q, false));
   SSTA_TRY(check_ptr(k, false));
-  SSTA_TRY(check_ptr(v_t, false));
+  SSTA_TRY(check_ptr(v, false));
   SSTA_TRY(check_ptr(o, false));
   SSTA_TRY(check_ptr(lse, true));
   // One head's K and V (token-major or tiles) are addressed with 32-bit
@@ -343,7 +343,7 @@ int attention_common(const ssta_geom_t* g, const ssta_params_t* p, const void* q
   ssta::AttnArgs aa;
   aa.q_t = q;
   aa.k_t = k;
-  aa.v_t = v_t;
+  aa.v_t = v;   // token-major (token_io) or dim-major tiles
   aa.kv_idx = kv_idx;
   aa.kv_cnt = kv_cnt;
   aa.max_kept = max_kept_;
