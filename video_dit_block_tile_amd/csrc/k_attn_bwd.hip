@@ -10,32 +10,31 @@
 // with lse_a the forward's log-sum-exp, so the probabilities are recomputed
 // exactly instead of with a running max.
 //
-// gfx950 design.  Three kernels, each one workgroup of 4 waves per block and
-// the matrix-core layouts of the forward kernel (v_mfma_f32_32x32x16_bf16; a
-// lane feeds row kperm(lane) of the A operand, bits 2 and 3 swapped, so every
-// 8 output registers are 8 consecutive rows and feed the next product as its
-// B operand straight from registers):
-//   k_attn_bwd_dq  per query block, over its kept key blocks in units of 32
-//                  keys: S^T = K Q^T and dP^T = V dO^T (Q, dO of the wave's 32
-//                  queries held in registers), dS^T in registers, then
-//                  dQ^T += K^T dS^T with K^T read transposed from the K rows;
-//   k_attn_bwd_dv  per key block, over the query blocks that keep it, in
-//                  units of 32 queries: S = Q K^T (the wave's 32 keys held in
-//                  registers), P in registers, dV^T += dO^T P;
-//   k_attn_bwd_dk  per key block likewise: S = Q K^T, dP = dO V^T, dS in
-//                  registers, dK^T += Q^T dS.
+// gfx950 design.  Two kernels, each one workgroup of kR/32 waves per block
+// and the matrix-core layouts of the forward kernel (v_mfma_f32_32x32x16_bf16;
+// a lane feeds row kperm(lane) of the A operand, bits 2 and 3 swapped, so
+// every 8 output registers are 8 consecutive rows and feed the next product
+// as its B operand straight from registers):
+//   k_attn_bwd_dq    per query block, over its kept key blocks in units of 32
+//                    keys: S^T = K Q^T and dP^T = V dO^T (Q, dO of the wave's
+//                    32 queries held in registers), dS^T in registers, then
+//                    dQ^T += K^T dS^T with K^T read transposed from the K rows;
+//   k_attn_bwd_dkdv  per key block, over the query blocks that keep it, in
+//                    units of 32 queries: S = Q K^T and dP = dO V^T (the
+//                    wave's 32 keys and their values held in registers), P and
+//                    dS in registers, then dV^T += dO^T P and dK^T += Q^T dS.
 // The transposed operands (K^T, dO^T, Q^T: channel d of 8 consecutive rows)
 // come from the same token rows in LDS through the transposing reads
 // (ds_read_b64_tr_b16), so nothing is copied to a dim-major layout first.
-// dV and dK are separate kernels so that each keeps two waves per SIMD (their
-// fused accumulators would not fit 256 VGPRs).  Every streamed unit (token
-// rows gathered from token-major memory and the per-query (lse*log2 e, D)
-// pairs) goes straight into LDS with
-// buffer_load_dwordx4 ... lds into a two-slot ring, as in the forward kernel.
+// k_attn_bwd_dq keeps two waves per SIMD; k_attn_bwd_dkdv's two accumulators
+// need more than 256 VGPRs, so it runs one.  Every streamed unit (token rows
+// gathered from token-major memory and the per-query (lse*log2 e, D) pairs)
+// goes straight into LDS with buffer_load_dwordx4 ... lds into a two-slot
+// ring, as in the forward kernel.
 //
 // Algorithmic work per kept (query block, key block) pair: five 128^3
-// products (S, dP, dQ, dK, dV) = 21.0 MFLOP; the split recomputes S twice and
-// dP once more, 33.6 MFLOP executed.
+// products (S, dP, dQ, dK, dV) = 21.0 MFLOP; the two kernels compute S and dP
+// once each more, 29.4 MFLOP executed.
 //
 // Joint video + text sequences: blocks from n_tiles on are text blocks of
 // consecutive tokens after the clip's.  A clip query block keeps its list and
@@ -334,12 +333,14 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, AttnGrid grid) {
   if (qvalid) store_row(static_cast<uint16_t*>(a.dq) + qtok * kHeadDim, acc, a.scale, hl);
 }
 
-// ------------------------------------------------------------------ dV, dK
+// ------------------------------------------------------------------ dK, dV
 
-// kDK = false: dV^T += dO^T P.  kDK = true: dK^T += Q^T dS with dS = P (dP - D).
-template <bool kDK, bool kGen, int kR>
-__global__ __launch_bounds__(kR * 2) __attribute__((amdgpu_waves_per_eu(2)))
-void k_attn_bwd_kv(Geo g, BwdArgs a, AttnGrid grid) {
+// dV^T += dO^T P and dK^T += Q^T dS with dS = P (dP - D), from the same S and
+// dP.  The two accumulators and the K and V operands need more than 256
+// VGPRs, so the kernel runs one wave per SIMD.
+template <bool kGen, int kR>
+__global__ __launch_bounds__(kR * 2) __attribute__((amdgpu_waves_per_eu(1)))
+void k_attn_bwd_dkdv(Geo g, BwdArgs a, AttnGrid grid) {
   constexpr int kUnits = Blk<kR>::kUnits;
   // slot: Q rows | dO rows | 32 (lse2, D) pairs; dO^T (dV) and Q^T (dK) are
   // read transposed from the rows
@@ -372,14 +373,14 @@ void k_attn_bwd_kv(Geo g, BwdArgs a, AttnGrid grid) {
   // B operands: the wave's 32 keys (and their values for dP).
   bf16x8 kf[8], vf[8];
   load_row_operand(kf, static_cast<const uint16_t*>(a.k) + ktok * kHeadDim, hl);
-  if (kDK) load_row_operand(vf, static_cast<const uint16_t*>(a.v) + ktok * kHeadDim, hl);
+  load_row_operand(vf, static_cast<const uint16_t*>(a.v) + ktok * kHeadDim, hl);
   const float c = a.scale_log2;
 
-  f32x16 acc[4];
+  f32x16 acc_v[4], acc_k[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) acc_v[db][r] = acc_k[db][r] = 0.0f;
 
   // query blocks that keep this key block: its transposed list, then every
   // text query block; every query block keeps a text key block (and all
@@ -437,14 +438,13 @@ void k_attn_bwd_kv(Geo g, BwdArgs a, AttnGrid grid) {
     for (int st = 0; st < 8; ++st) {
       const bf16x8 qa = *reinterpret_cast<const bf16x8*>(sQ + swz_row(kperm, 2 * st + hl));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[st], s, 0, 0, 0);
-      if (kDK) {
-        const bf16x8 da = *reinterpret_cast<const bf16x8*>(sD + swz_row(kperm, 2 * st + hl));
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[st], dp, 0, 0, 0);
-      }
+      const bf16x8 da = *reinterpret_cast<const bf16x8*>(sD + swz_row(kperm, 2 * st + hl));
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[st], dp, 0, 0, 0);
     }
-    // P (dV) or dS (dK) as the B operand of k-step ks (queries 16*ks + 8*hl + e);
-    // zero for a query its block lacks (its rows hold the block's first token).
-    bf16x8 bf[2];
+    // P (for dV) and dS (for dK) as B operands of k-step ks (queries
+    // 16*ks + 8*hl + e); zero for a query its block lacks (its rows hold the
+    // block's first token).
+    bf16x8 bp[2], bs[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const f32x4* lp = reinterpret_cast<const f32x4*>(sL + 2 * (16 * ks + 8 * hl));
@@ -455,29 +455,29 @@ void k_attn_bwd_kv(Geo g, BwdArgs a, AttnGrid grid) {
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * ks + e;
         const float lse2 = lv[e >> 1][(e & 1) * 2];
-        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
-        float w = pr;
-        if (kDK) {
-          const float dd = lv[e >> 1][(e & 1) * 2 + 1];
-          w = pr * (dp[r] - dd);
-        }
-        if (kGen && !((valid >> (16 * ks + 8 * hl + e)) & 1u)) w = 0.0f;
-        bf[ks][e] = (__bf16)w;
+        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
+        float ds = pr * (dp[r] - lv[e >> 1][(e & 1) * 2 + 1]);
+        if (kGen && !((valid >> (16 * ks + 8 * hl + e)) & 1u)) pr = ds = 0.0f;
+        bp[ks][e] = (__bf16)pr;
+        bs[ks][e] = (__bf16)ds;
       }
     }
-    // dV^T += dO^T P  or  dK^T += Q^T dS: A operand row d, the same 8 queries,
-    // read transposed from the dO or Q rows.
+    // dV^T += dO^T P and dK^T += Q^T dS: A operand row d, the same 8 queries,
+    // read transposed from the dO and Q rows.
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const bf16x8 ca = row_t_operand(kDK ? sQ : sD, tb, ks, db);
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca, bf[ks], acc[db], 0, 0, 0);
+        acc_v[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_t_operand(sD, tb, ks, db),
+                                                            bp[ks], acc_v[db], 0, 0, 0);
+        acc_k[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_t_operand(sQ, tb, ks, db),
+                                                            bs[ks], acc_k[db], 0, 0, 0);
       }
   }
-  if (kvalid)
-    store_row(static_cast<uint16_t*>(kDK ? a.dk : a.dv) + ktok * kHeadDim, acc,
-              kDK ? a.scale : 1.0f, hl);
+  if (kvalid) {
+    store_row(static_cast<uint16_t*>(a.dv) + ktok * kHeadDim, acc_v, 1.0f, hl);
+    store_row(static_cast<uint16_t*>(a.dk) + ktok * kHeadDim, acc_k, a.scale, hl);
+  }
 }
 
 // ------------------------------------------------------------------ helpers
@@ -663,35 +663,23 @@ hipError_t launch_transpose_lists(const Geo& g, const int32_t* kv_idx, const int
   return hipGetLastError();
 }
 
+template <bool kGen, int kR>
+hipError_t launch_bwd_kernels(const Geo& g, const BwdArgs& a, const AttnGrid& ag,
+                              hipStream_t s) {
+  const dim3 grid((unsigned)ag.blocks), block(2 * kR);
+  hipLaunchKernelGGL((k_attn_bwd_dq<kGen, kR>), grid, block, 0, s, g, a, ag);
+  hipLaunchKernelGGL((k_attn_bwd_dkdv<kGen, kR>), grid, block, 0, s, g, a, ag);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention_bwd(const Geo& g, const BwdArgs& a, hipStream_t s) {
   const AttnGrid ag = attn_grid(g);
-  const int64_t blocks = ag.blocks;
-  const dim3 grid((unsigned)blocks);
   const bool gen = g.ragged || g.L > 0;   // partial blocks or text blocks
-  if (g.R == kSmallTile) {
-    const dim3 block(2 * kSmallTile);
-    if (gen) {
-      hipLaunchKernelGGL((k_attn_bwd_dq<true, kSmallTile>), grid, block, 0, s, g, a, ag);
-      hipLaunchKernelGGL((k_attn_bwd_kv<false, true, kSmallTile>), grid, block, 0, s, g, a, ag);
-      hipLaunchKernelGGL((k_attn_bwd_kv<true, true, kSmallTile>), grid, block, 0, s, g, a, ag);
-    } else {
-      hipLaunchKernelGGL((k_attn_bwd_dq<false, kSmallTile>), grid, block, 0, s, g, a, ag);
-      hipLaunchKernelGGL((k_attn_bwd_kv<false, false, kSmallTile>), grid, block, 0, s, g, a, ag);
-      hipLaunchKernelGGL((k_attn_bwd_kv<true, false, kSmallTile>), grid, block, 0, s, g, a, ag);
-    }
-  } else {
-    const dim3 block(2 * kTileTokens);
-    if (gen) {
-      hipLaunchKernelGGL((k_attn_bwd_dq<true, kTileTokens>), grid, block, 0, s, g, a, ag);
-      hipLaunchKernelGGL((k_attn_bwd_kv<false, true, kTileTokens>), grid, block, 0, s, g, a, ag);
-      hipLaunchKernelGGL((k_attn_bwd_kv<true, true, kTileTokens>), grid, block, 0, s, g, a, ag);
-    } else {
-      hipLaunchKernelGGL((k_attn_bwd_dq<false, kTileTokens>), grid, block, 0, s, g, a, ag);
-      hipLaunchKernelGGL((k_attn_bwd_kv<false, false, kTileTokens>), grid, block, 0, s, g, a, ag);
-      hipLaunchKernelGGL((k_attn_bwd_kv<true, false, kTileTokens>), grid, block, 0, s, g, a, ag);
-    }
-  }
-  return hipGetLastError();
+  if (g.R == kSmallTile)
+    return gen ? launch_bwd_kernels<true, kSmallTile>(g, a, ag, s)
+               : launch_bwd_kernels<false, kSmallTile>(g, a, ag, s);
+  return gen ? launch_bwd_kernels<true, kTileTokens>(g, a, ag, s)
+             : launch_bwd_kernels<false, kTileTokens>(g, a, ag, s);
 }
 
 }  // namespace ssta
