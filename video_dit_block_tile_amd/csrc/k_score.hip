@@ -217,8 +217,12 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 
 // Per-row top-k, one wave per query-block row.  Each lane keeps E keys
 // (columns lane, lane+64, ...).  The k-th largest key T is found bit by bit
-// from the top (32 wave-wide counts), then the row keeps every key above T and
-// the lowest-id columns equal to T until k are kept, writing ids ascending.
+// from the top (one wave-wide count per bit), then the row keeps every key
+// above T and the lowest-id columns equal to T until k are kept, writing ids
+// ascending.  Two shortcuts leave T's role unchanged: the bits that all the
+// row's candidate keys share are taken as they are, and the search stops at
+// a prefix that exactly k keys reach (those k are then the row's top k, so
+// the selection below keeps exactly them).
 template <int E>
 __global__ __launch_bounds__(256) void k_topk(Geo g, const float* __restrict__ scores,
                                               int32_t* __restrict__ out, int64_t rows, int k,
@@ -255,13 +259,33 @@ __global__ __launch_bounds__(256) void k_topk(Geo g, const float* __restrict__ s
   int32_t* o = out + row * width;
   int pos = 0;
   if (want > 0) {
-    uint32_t thr = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
+    uint32_t kmax = 0u, kmin = ~0u;   // over the candidates (key != 0)
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (key[e] != 0u) {
+        kmax = max(kmax, key[e]);
+        kmin = min(kmin, key[e]);
+      }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+    }
+    const uint32_t diff = kmax ^ kmin;
+    // top: highest bit in which two candidates differ; the bits above it are
+    // common to all candidates, so the search would set exactly those of them
+    // that are set in every key
+    const int top = diff ? 31 - __builtin_clz(diff) : -1;
+    uint32_t thr = top < 0 ? kmax : (top == 31 ? 0u : kmax & ~((2u << top) - 1u));
+    for (int bit = top; bit >= 0; --bit) {
       const uint32_t cand = thr | (1u << bit);
       int cnt = 0;
 #pragma unroll
       for (int e = 0; e < E; ++e) cnt += __popcll(__ballot(key[e] >= cand));
-      if (cnt >= want) thr = cand;
+      if (cnt >= want) {
+        thr = cand;
+        if (cnt == want) break;
+      }
     }
     int above = 0;
 #pragma unroll
