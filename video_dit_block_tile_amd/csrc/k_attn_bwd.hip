@@ -431,15 +431,28 @@ void k_attn_bwd_dkdv(Geo g, BwdArgs a, AttnGrid grid) {
     const float* sL = reinterpret_cast<const float*>(cur + 2 * kUnitBytes);
 
     // S (queries x keys, lane = key l32): register r is query 16*(r/8) + 8*hl + r%8.
+    // The Q and dO operands are requested kAhead k-steps ahead of their
+    // products (one wave per SIMD: nothing else covers the LDS latency).
+    constexpr int kAhead = 4;
     f32x16 s, dp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.0f;
+    bf16x8 qa[kAhead], da[kAhead];
+#pragma unroll
+    for (int st = 0; st < kAhead; ++st) {
+      qa[st] = *reinterpret_cast<const bf16x8*>(sQ + swz_row(kperm, 2 * st + hl));
+      da[st] = *reinterpret_cast<const bf16x8*>(sD + swz_row(kperm, 2 * st + hl));
+    }
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
-      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(sQ + swz_row(kperm, 2 * st + hl));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[st], s, 0, 0, 0);
-      const bf16x8 da = *reinterpret_cast<const bf16x8*>(sD + swz_row(kperm, 2 * st + hl));
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[st], dp, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st % kAhead], kf[st], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[st % kAhead], vf[st], dp, 0, 0, 0);
+      const int n = st + kAhead;
+      if (n < 8) {
+        qa[st % kAhead] = *reinterpret_cast<const bf16x8*>(sQ + swz_row(kperm, 2 * n + hl));
+        da[st % kAhead] = *reinterpret_cast<const bf16x8*>(sD + swz_row(kperm, 2 * n + hl));
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     // P (for dV) and dS (for dK) as B operands of k-step ks (queries
     // 16*ks + 8*hl + e); zero for a query its block lacks (its rows hold the
