@@ -27,10 +27,12 @@
 // come from the same token rows in LDS through the transposing reads
 // (ds_read_b64_tr_b16), so nothing is copied to a dim-major layout first.
 // k_attn_bwd_dq keeps two waves per SIMD; k_attn_bwd_dkdv's two accumulators
-// need more than 256 VGPRs, so it runs one.  Every streamed unit (token rows
-// gathered from token-major memory and the per-query (lse*log2 e, D) pairs)
-// goes straight into LDS with buffer_load_dwordx4 ... lds into a two-slot
-// ring, as in the forward kernel.
+// need more than 256 VGPRs, so it runs one, and software-pipelines its units
+// instead (P and dS of one unit on the vector ALU while the matrix cores
+// compute S and dP of the next).  Every streamed unit (token rows gathered
+// from token-major memory and the per-query (lse*log2 e, D) pairs) goes
+// straight into LDS with buffer_load_dwordx4 ... lds into a ring of slots
+// (two in k_attn_bwd_dq, three in k_attn_bwd_dkdv), as in the forward kernel.
 //
 // Algorithmic work per kept (query block, key block) pair: five 128^3
 // products (S, dP, dQ, dK, dV) = 21.0 MFLOP; the two kernels compute S and dP
@@ -345,7 +347,9 @@ void k_attn_bwd_dkdv(Geo g, BwdArgs a, AttnGrid grid) {
   // slot: Q rows | dO rows | 32 (lse2, D) pairs; dO^T (dV) and Q^T (dK) are
   // read transposed from the rows
   constexpr int kSlot = 2 * kUnitBytes + 256;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kSlot];
+  // three slots: unit u (dV, dK), unit u+1 (S, dP) and unit u+2 (loading);
+  // LDS does not limit this kernel's occupancy (VGPRs do)
+  __shared__ __attribute__((aligned(16))) uint8_t smem[3 * kSlot];
   // text key blocks (kept by every query block) first; then, with the kept
   // lists, each head's key blocks longest first (k_order_blocks), dealt
   // round-robin over the XCDs; under dense attention, XCD slices
@@ -417,66 +421,88 @@ void k_attn_bwd_dkdv(Geo g, BwdArgs a, AttnGrid grid) {
     return valid;
   };
 
+  // Software pipeline over units (one wave per SIMD, so the wave overlaps its
+  // own vector and matrix work): iteration u forms P and dS of unit u on the
+  // vector ALU while the matrix cores compute S and dP of unit u+1, then runs
+  // dV^T += dO^T P and dK^T += Q^T dS of unit u.  S and dP alternate between
+  // two register sets (units come in pairs: kUnits is even).
   const int units = kUnits * cnt;
-  uint32_t valid_next = ~0u;
-  if (units > 0) valid_next = load_unit(0, smem);
-  for (int u = 0; u < units; ++u) {
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
-    uint8_t* cur = smem + (u & 1) * kSlot;
-    const uint32_t valid = valid_next;
-    if (u + 1 < units) valid_next = load_unit(u + 1, smem + ((u + 1) & 1) * kSlot);
-    const uint8_t* sQ = cur;
-    const uint8_t* sD = cur + kUnitBytes;
-    const float* sL = reinterpret_cast<const float*>(cur + 2 * kUnitBytes);
-
-    // S (queries x keys, lane = key l32): register r is query 16*(r/8) + 8*hl + r%8.
-    // The Q and dO operands are requested kAhead k-steps ahead of their
-    // products (one wave per SIMD: nothing else covers the LDS latency).
-    constexpr int kAhead = 4;
-    f32x16 s, dp;
+  auto slot = [&](int u) -> uint8_t* { return smem + (u % 3) * kSlot; };
+  constexpr int kAhead = 4;   // Q and dO operands requested ahead of their products
+  // S (queries x keys, lane = key l32): register r is query 16*(r/8) + 8*hl +
+  // r%8; dP likewise.  score_step(st) issues k-step st of both products.
+  auto score_step = [&](const uint8_t* sQ, const uint8_t* sD, int st, bf16x8* qa, bf16x8* da,
+                        f32x16& s, f32x16& dp) {
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st % kAhead], kf[st], s, 0, 0, 0);
+    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[st % kAhead], vf[st], dp, 0, 0, 0);
+    const int n = st + kAhead;
+    if (n < 8) {
+      qa[st % kAhead] = *reinterpret_cast<const bf16x8*>(sQ + swz_row(kperm, 2 * n + hl));
+      da[st % kAhead] = *reinterpret_cast<const bf16x8*>(sD + swz_row(kperm, 2 * n + hl));
+    }
+  };
+  auto score_begin = [&](const uint8_t* sQ, const uint8_t* sD, bf16x8* qa, bf16x8* da,
+                         f32x16& s, f32x16& dp) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.0f;
-    bf16x8 qa[kAhead], da[kAhead];
 #pragma unroll
     for (int st = 0; st < kAhead; ++st) {
       qa[st] = *reinterpret_cast<const bf16x8*>(sQ + swz_row(kperm, 2 * st + hl));
       da[st] = *reinterpret_cast<const bf16x8*>(sD + swz_row(kperm, 2 * st + hl));
     }
+  };
+  // P (for dV) and dS (for dK) of score registers r and r+1 as B operands of
+  // k-step r/8 (queries 16*ks + 8*hl + e); zero for a query its block lacks
+  // (its rows hold the block's first token).
+  auto prob_pair = [&](int r, const f32x16& s, const f32x16& dp, const f32x4* lv,
+                       uint32_t valid, bf16x8* bp, bf16x8* bs) {
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st % kAhead], kf[st], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[st % kAhead], vf[st], dp, 0, 0, 0);
-      const int n = st + kAhead;
-      if (n < 8) {
-        qa[st % kAhead] = *reinterpret_cast<const bf16x8*>(sQ + swz_row(kperm, 2 * n + hl));
-        da[st % kAhead] = *reinterpret_cast<const bf16x8*>(sD + swz_row(kperm, 2 * n + hl));
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int x = 0; x < 2; ++x) {
+      const int rr = r + x, ks = rr >> 3, e = rr & 7;
+      const f32x4 l2 = lv[4 * ks + (e >> 1)];   // (lse2, D) of queries e&~1, e|1
+      const float lse2 = l2[(e & 1) * 2];
+      float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], c, -lse2));
+      float ds = pr * (dp[rr] - l2[(e & 1) * 2 + 1]);
+      if (kGen && !((valid >> (16 * ks + 8 * hl + e)) & 1u)) pr = ds = 0.0f;
+      bp[ks][e] = (__bf16)pr;
+      bs[ks][e] = (__bf16)ds;
     }
-    // P (for dV) and dS (for dK) as B operands of k-step ks (queries
-    // 16*ks + 8*hl + e); zero for a query its block lacks (its rows hold the
-    // block's first token).
+  };
+  // iteration u: S, dP of unit u are in (s0, dp0); those of unit u+1 go to (s1, dp1)
+  auto iteration = [&](int u, uint32_t& v0, uint32_t& v1, f32x16& s0, f32x16& dp0,
+                       f32x16& s1, f32x16& dp1) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's loads of unit u+1 have landed
+    __syncthreads();                        // ... every wave's; unit u-1 is done
+    uint32_t v2 = ~0u;
+    if (u + 2 < units) v2 = load_unit(u + 2, slot(u + 2));   // into unit u-1's slot
+    const uint8_t* cur = slot(u);
+    const uint8_t* sQ = cur;
+    const uint8_t* sD = cur + kUnitBytes;
+    const f32x4* sL = reinterpret_cast<const f32x4*>(cur + 2 * kUnitBytes);
+    f32x4 lv[8];   // (lse2, D) of this lane's 16 queries: 8*ks + 8*hl .. in pairs
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) lv[4 * ks + x] = sL[(16 * ks + 8 * hl) / 2 + x];
     bf16x8 bp[2], bs[2];
+    if (u + 1 < units) {
+      const uint8_t* nQ = slot(u + 1);
+      const uint8_t* nD = nQ + kUnitBytes;
+      bf16x8 qa[kAhead], da[kAhead];
+      score_begin(nQ, nD, qa, da, s1, dp1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const f32x4* lp = reinterpret_cast<const f32x4*>(sL + 2 * (16 * ks + 8 * hl));
-      f32x4 lv[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) lv[x] = lp[x];   // (lse2, D) of 8 consecutive queries
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = 8 * ks + e;
-        const float lse2 = lv[e >> 1][(e & 1) * 2];
-        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
-        float ds = pr * (dp[r] - lv[e >> 1][(e & 1) * 2 + 1]);
-        if (kGen && !((valid >> (16 * ks + 8 * hl + e)) & 1u)) pr = ds = 0.0f;
-        bp[ks][e] = (__bf16)pr;
-        bs[ks][e] = (__bf16)ds;
+      for (int st = 0; st < 8; ++st) {
+        score_step(nQ, nD, st, qa, da, s1, dp1);
+        prob_pair(2 * st, s0, dp0, lv, v0, bp, bs);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    } else {
+#pragma unroll
+      for (int st = 0; st < 8; ++st) prob_pair(2 * st, s0, dp0, lv, v0, bp, bs);
     }
     // dV^T += dO^T P and dK^T += Q^T dS: A operand row d, the same 8 queries,
-    // read transposed from the dO and Q rows.
+    // read transposed from the dO and Q rows of unit u.
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -486,6 +512,25 @@ void k_attn_bwd_dkdv(Geo g, BwdArgs a, AttnGrid grid) {
         acc_k[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_t_operand(sQ, tb, ks, db),
                                                             bs[ks], acc_k[db], 0, 0, 0);
       }
+    v0 = v1;
+    v1 = v2;
+  };
+
+  f32x16 sa, dpa, sb, dpb;
+  uint32_t v0 = ~0u, v1 = ~0u;   // which queries of units u and u+1 exist
+  if (units > 0) {
+    v0 = load_unit(0, slot(0));
+    if (units > 1) v1 = load_unit(1, slot(1));
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    bf16x8 qa[kAhead], da[kAhead];
+    score_begin(slot(0), slot(0) + kUnitBytes, qa, da, sa, dpa);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) score_step(slot(0), slot(0) + kUnitBytes, st, qa, da, sa, dpa);
+  }
+  for (int u = 0; u < units; u += 2) {
+    iteration(u, v0, v1, sa, dpa, sb, dpb);
+    iteration(u + 1, v0, v1, sb, dpb, sa, dpa);
   }
   if (kvalid) {
     store_row(static_cast<uint16_t*>(a.dv) + ktok * kHeadDim, acc_v, 1.0f, hl);
