@@ -177,7 +177,8 @@ def bwd_bounds(wl, q, k, v, do, kv_idx, kv_cnt, q_rows, k_rows):
         at most P_ab |dD_a| (both folded into dD_a): scale * sum_b P_ab |dD_a| |k_b|
         for dq, scale * sum_a P_ab |dD_a| |q_a| for dk;
       - the bf16 output rounding: 2^-8 |value| (with margin).
-    Positions without a token get bound 0."""
+    Positions without a token, query rows that keep nothing and key blocks
+    that no row keeps get bound 0 (their gradients must be exactly 0)."""
     R, scale = wl.tile_tokens, oracle.default_scale(wl)
     tmap = _token_map(wl)
     sh = (wl.batch, wl.heads, wl.seq_len, 128)
@@ -190,6 +191,8 @@ def bwd_bounds(wl, q, k, v, do, kv_idx, kv_cnt, q_rows, k_rows):
         qt = tmap[i]
         there = qt >= 0
         keys = _row_keys(wl, tmap, kv_idx, kv_cnt, b, h, i)
+        if keys.size == 0:
+            continue          # a row that keeps nothing: dq is exactly 0 (bound 0)
         Q, K, dO, P, dS, eps_d = _row_terms(wl, qf, kf, vf, dof, b, h, qt[there], keys, scale)
         dq = scale * dS @ K
         bq[a, there] = (scale * (2.0 ** -7 * np.abs(dS) @ np.abs(K)

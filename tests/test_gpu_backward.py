@@ -75,6 +75,29 @@ def test_backward_vs_oracle(name):
     _check("dv", _rows_of(wl, dv, rows), rv, bv)
 
 
+@pytest.mark.parametrize("name", ["grid32-w1-k2", "t64-grid"])
+def test_backward_partial_lists(name):
+    """Window AND top-k: some rows and key blocks keep nothing, the rest few
+    blocks, so the key-block lists are short, uneven or empty."""
+    wl = si.ALL[name]
+    q, k, v = si.make_qkv(wl)
+    do = si.generate(wl, 3)
+    flags = oracle.COMBINE_AND
+    print("[%s AND]" % name, flush=True)
+    plan, dq, dk, dv = _run(wl, q, k, v, do, flags)
+    sel = oracle.select(wl, q, k, flags)
+    assert np.array_equal(plan.kv_cnt.cpu().numpy(), sel["kv_cnt"])
+    assert np.array_equal(plan.kv_idx.cpu().numpy(), sel["kv_idx"])
+    cnt = sel["kv_cnt"].reshape(-1)
+    assert (cnt == 0).any() and (cnt > 0).any()
+    rows = np.arange(wl.batch * wl.heads * wl.n_rows)
+    rq, rk, rv = oracle.attention_bwd(wl, q, k, v, do, sel["kv_idx"], sel["kv_cnt"])
+    bq, bk, bv = bwd_bounds(wl, q, k, v, do, sel["kv_idx"], sel["kv_cnt"], rows, rows)
+    _check("dq", _rows_of(wl, dq, rows), rq, bq)
+    _check("dk", _rows_of(wl, dk, rows), rk, bk)
+    _check("dv", _rows_of(wl, dv, rows), rv, bv)
+
+
 def test_backward_dense_equals_all_kept():
     wl = si.ALL["wide-k"]                          # every block kept
     q, k, v = si.make_qkv(wl)
