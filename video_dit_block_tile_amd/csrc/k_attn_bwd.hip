@@ -151,13 +151,12 @@ __device__ __forceinline__ uint32_t rows_valid(const Geo& g, uint32_t j, int p, 
 // A text block's rows are consecutive tokens.
 template <bool kGen, int kR>
 __device__ __forceinline__ void dma_rows(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, const Geo& g,
-                                         uint32_t j, int p, int wave, int lane, uint32_t valid,
-                                         const UnitOffsets<kR>& off) {
+                                         uint32_t j, uint32_t clip_origin, int p, int wave,
+                                         int lane, uint32_t valid, const UnitOffsets<kR>& off) {
   constexpr int kL = Blk<kR>::kLoads;
   const bool part = kGen && valid != ~0u;
   const bool text = kGen && j >= g.n_tiles;
-  const uint32_t origin =
-      text ? (uint32_t)(g.N + (j - g.n_tiles) * kR) : block_origin32(g, j);
+  const uint32_t origin = text ? (uint32_t)(g.N + (j - g.n_tiles) * kR) : clip_origin;
   const uint32_t half = (text ? 32u * p : in_block_offset(g, 32 * p)) * 256u;
   const uint32_t so = origin * 256u + (part ? 0u : half);
 #pragma unroll
@@ -178,23 +177,32 @@ __device__ __forceinline__ int64_t row_token(const Geo& g, int64_t j, int r, boo
   return block_first_token(g, (uint32_t)j) + (exists ? in_block_offset(g, r) : 0u);
 }
 
-// Kept-block ids of one list, 64 at a time (lane i holds entry base + i);
-// positions are requested in non-decreasing order.
+// Kept-block ids of one list, 64 at a time (lane i holds entry base + i, or
+// block base + i for a dense list), with the first token of each such clip
+// block, so that a unit's gather base is a v_readlane rather than a scalar
+// division; positions are requested in non-decreasing order.
 struct IdStream {
   const int32_t* idx;
   int cnt, base, ids;
+  uint32_t org;
   bool dense;
-  __device__ __forceinline__ void init(const int32_t* p, int c, bool d, int lane) {
-    idx = p; cnt = c; dense = d; base = 0;
-    ids = (!d && lane < c) ? p[lane] : 0;
+  __device__ __forceinline__ void fill(const Geo& g, int lane) {
+    const int pos = base + lane;
+    ids = dense ? pos : (pos < cnt ? idx[pos] : 0);
+    org = block_origin32(g, (uint32_t)min(ids, (int)g.n_tiles - 1));
   }
-  __device__ __forceinline__ uint32_t at(int pos, int lane) {
-    if (dense) return (uint32_t)pos;
+  __device__ __forceinline__ void init(const Geo& g, const int32_t* p, int c, bool d, int lane) {
+    idx = p; cnt = c; dense = d; base = 0;
+    fill(g, lane);
+  }
+  // block at list position pos; origin: its first token (clip blocks)
+  __device__ __forceinline__ uint32_t at(const Geo& g, int pos, int lane, uint32_t& origin) {
     if (pos >= base + 64) {
       base += 64;
-      ids = (base + lane < cnt) ? idx[base + lane] : 0;
+      fill(g, lane);
     }
-    return (uint32_t)__builtin_amdgcn_readlane(ids, pos - base);
+    origin = (uint32_t)__builtin_amdgcn_readlane((int)org, pos - base);
+    return dense ? (uint32_t)pos : (uint32_t)__builtin_amdgcn_readlane(ids, pos - base);
   }
 };
 
@@ -263,7 +271,7 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, AttnGrid grid) {
   const int listed = all_blocks ? 0 : a.kv_cnt[kvrow];
   const int cnt = all_blocks ? (int)g.n_rows : listed + (kGen ? g.n_txt : 0);
   IdStream ids;
-  ids.init(all_blocks ? nullptr : a.kv_idx + kvrow * a.max_kept, listed, all_blocks, lane);
+  ids.init(g, all_blocks ? nullptr : a.kv_idx + kvrow * a.max_kept, listed, all_blocks, lane);
   const UnitOffsets<kR> off = unit_offsets<kR>(g, wv, lane);
   const int tb = row_t_base(lane);
   // token-major: S rows of 256 B per head
@@ -275,13 +283,14 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, AttnGrid grid) {
   // returns which of the unit's 32 keys exist
   auto load_unit = [&](int u, uint8_t* dst) -> uint32_t {
     const int pos = u / kUnits;
+    uint32_t org = 0;
     const uint32_t j = kGen && pos >= listed && !all_blocks
                            ? (uint32_t)(g.n_tiles + pos - listed)
-                           : ids.at(pos, lane);
+                           : ids.at(g, pos, lane, org);
     const int p = u % kUnits;
     const uint32_t valid = rows_valid<kGen, kR>(g, j, p, lane);
-    dma_rows<kGen, kR>(dst, krs, g, j, p, wv, lane, valid, off);
-    dma_rows<kGen, kR>(dst + kUnitBytes, vrs, g, j, p, wv, lane, valid, off);
+    dma_rows<kGen, kR>(dst, krs, g, j, org, p, wv, lane, valid, off);
+    dma_rows<kGen, kR>(dst + kUnitBytes, vrs, g, j, org, p, wv, lane, valid, off);
     return valid;
   };
 
@@ -394,7 +403,7 @@ void k_attn_bwd_dkdv(Geo g, BwdArgs a, AttnGrid grid) {
   const int listed = all_blocks ? 0 : a.q_cnt[klist];
   const int cnt = all_blocks ? (int)g.n_rows : listed + (kGen ? g.n_txt : 0);
   IdStream ids;
-  ids.init(all_blocks ? nullptr : a.q_idx + klist * a.q_width, listed, all_blocks, lane);
+  ids.init(g, all_blocks ? nullptr : a.q_idx + klist * a.q_width, listed, all_blocks, lane);
   const UnitOffsets<kR> off = unit_offsets<kR>(g, wv, lane);
   const int tb = row_t_base(lane);
   const int64_t tok_bytes = g.S * (int64_t)(kHeadDim * 2);
@@ -407,13 +416,14 @@ void k_attn_bwd_dkdv(Geo g, BwdArgs a, AttnGrid grid) {
   // returns which of the unit's 32 queries exist
   auto load_unit = [&](int u, uint8_t* dst) -> uint32_t {
     const int pos = u / kUnits;
+    uint32_t org = 0;
     const uint32_t i = kGen && pos >= listed && !all_blocks
                            ? (uint32_t)(g.n_tiles + pos - listed)
-                           : ids.at(pos, lane);
+                           : ids.at(g, pos, lane, org);
     const int p = u % kUnits;
     const uint32_t valid = rows_valid<kGen, kR>(g, i, p, lane);
-    dma_rows<kGen, kR>(dst, qrs, g, i, p, wv, lane, valid, off);
-    dma_rows<kGen, kR>(dst + kUnitBytes, drs, g, i, p, wv, lane, valid, off);
+    dma_rows<kGen, kR>(dst, qrs, g, i, org, p, wv, lane, valid, off);
+    dma_rows<kGen, kR>(dst + kUnitBytes, drs, g, i, org, p, wv, lane, valid, off);
     if (wv == 0 && lane < 16)   // 32 (lse2, D) pairs = 256 B
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           lrs, (lds_u8*)(dst + 2 * kUnitBytes), 16, (uint32_t)lane * 16,
