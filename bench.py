@@ -12,8 +12,14 @@ synchronisations.  Prints one JSON line.
   phase_ms     per phase (tile_pool, score_select, build_mask, attention,
                unpermute): mean, median, p10, p90 over the K steps, from HIP
                events recorded on the launch stream
-  phase_rates  algorithmic bytes, GB/s and % of HBM peak per phase; VALU FLOP
-               and % of the fp32 vector peak for the block scoring
+  phase_rates  algorithmic bytes, GB/s and % of HBM peak per phase (attention:
+               the logical K/V block bytes it requests, most served by L2/MALL,
+               as a rate only); VALU FLOP and % of the usable (unpacked) fp32
+               vector peak for the block scoring
+  per_config   the five workload shapes: step and attention time, attention
+               TFLOP/s, kept fraction and speedup over the dense path
+  materialised_io  the block gather with tile writes and the output
+               unpermute (the non-fused path) timed once, with their HBM rate
   cold_cache   steps timed right after overwriting a 512 MB buffer
   roofline     the attention kernel (the dominant kernel): kept FLOP / its
                mean launch time vs the dense bf16 MFMA peak of 2.5 PFLOP/s;
@@ -46,6 +52,9 @@ METRIC = "SSTA fwd effective TFLOP/s on kept blocks (% bf16 MFMA peak) + speedup
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 PEAK_FP32_VECTOR_TFLOPS = 157.3    # MI355X published fp32 vector peak (packed FMA)
+# the fp32 vector rate this build can reach: packed fp32 instructions are
+# disabled, so one FMA per lane per cycle: 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz
+PEAK_FP32_UNPACKED_TFLOPS = 78.6
 
 
 def parse():
@@ -63,6 +72,9 @@ def parse():
     ap.add_argument("--variant-steps", type=int, default=5,
                     help="timed forward steps of each variant workload (64-token blocks, "
                          "joint text, ragged latent grid); 0 to skip")
+    ap.add_argument("--config-steps", type=int, default=5,
+                    help="timed forward steps of each of the five workload shapes (per_config; "
+                         "dense on the same inputs for the speedup); 0 to skip")
     ap.add_argument("--no-mfma-ceiling", action="store_true",
                     help="skip the sustained bf16 matrix-core rate measurement")
     ap.add_argument("--materialised", action="store_true",
@@ -267,6 +279,106 @@ def variant_runs(torch, m, si, steps):
     return out
 
 
+def per_config_runs(torch, m, si, steps, dense_steps):
+    """The five workload shapes in turn (inputs generated, timed, freed): step
+    and attention time from HIP events on the launch stream, attention
+    TFLOP/s on kept blocks, kept fraction, and the same pipeline with every
+    block kept (dense) on the same inputs for the speedup."""
+    import numpy as np
+    out = {}
+    for name, wl in si.CONFIGS.items():
+        q, k, v = si.make_qkv(wl)
+        dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        qd, kd, vd = dev(q), dev(k), dev(v)
+        g = m.make_geom(wl.batch, wl.heads, wl.T, wl.H, wl.W, tile=wl.tile,
+                        text_len=wl.text_len)
+        p = m.make_params(win=wl.win, topk=wl.topk)
+        res = {}
+        for mode in ("sparse", "dense"):
+            plan = m.SstaPlan(g, p, dense=(mode == "dense"))
+            n_steps = steps if mode == "sparse" else dense_steps
+            for _ in range(2):
+                plan.run(qd, kd, vd)
+            torch.cuda.synchronize()
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_steps)]
+            for e in ev:
+                e[0].record()
+                plan.tile_pool(qd, kd, vd)
+                if mode == "sparse":
+                    plan.select()
+                e[1].record()
+                plan.attend()
+                e[2].record()
+            torch.cuda.synchronize()
+            res[mode] = (float(np.median([e[0].elapsed_time(e[2]) for e in ev])),
+                         float(np.median([e[1].elapsed_time(e[2]) for e in ev])),
+                         block_pairs(wl, plan) if mode == "sparse" else
+                         wl.batch * wl.heads * wl.n_rows * wl.n_rows)
+            del plan
+        step, attn, pairs = res["sparse"]
+        dstep, dattn, dpairs = res["dense"]
+        flop = pairs * 4 * wl.tile_tokens ** 2 * 128
+        tf = flop / (attn * 1e-3) / 1e12
+        out[name] = {"grid": [wl.T, wl.H, wl.W], "n_tiles": wl.n_tiles, "topk": wl.topk,
+                     "kept_pairs": pairs, "kept_fraction": round(pairs / dpairs, 5),
+                     "step_ms": round(step, 4), "attention_ms": round(attn, 4),
+                     "attention_tflops": round(tf, 2),
+                     "pct_bf16_peak_attention": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                     "dense_step_ms": round(dstep, 3), "dense_attention_ms": round(dattn, 3),
+                     "speedup_vs_dense_step": round(dstep / step, 3),
+                     "speedup_vs_dense_attention": round(dattn / attn, 3)}
+        print("[bench] config %s: step %.3f ms, attention %.3f ms (%.1f TFLOP/s), kept %.4f, "
+              "dense step %.2f ms" % (name, step, attn, tf, pairs / dpairs, dstep),
+              file=sys.stderr, flush=True)
+        del qd, kd, vd
+        torch.cuda.empty_cache()
+    return out
+
+
+def materialised_io(torch, m, wl, g, qd, reps=5):
+    """The block gather that writes tile-major copies (token-major for Q and
+    K, dim-major for V; plus the block means) and the unpermute of a
+    tile-major output back to token order, each timed with HIP events.
+    Algorithmic bytes: one tensor read + one written (+ the fp32 means)."""
+    import numpy as np
+    bh = wl.batch * wl.heads
+    tiled = torch.empty(wl.batch, wl.heads, wl.n_rows, wl.tile_tokens, 128,
+                        dtype=torch.bfloat16, device="cuda")
+    tiled_d = torch.empty(wl.batch, wl.heads, wl.n_rows, 128, wl.tile_tokens,
+                          dtype=torch.bfloat16, device="cuda")
+    pooled = torch.empty(wl.batch, wl.heads, wl.n_tiles, 128, dtype=torch.float32,
+                         device="cuda")
+    out = torch.empty_like(qd)
+    calls = {
+        "tile_pool_token_major": lambda: m.ssta_tile_pool(g, qd, tiled, m.LAYOUT_TOKEN_MAJOR,
+                                                          pooled),
+        "tile_pool_dim_major": lambda: m.ssta_tile_pool(g, qd, tiled_d, m.LAYOUT_DIM_MAJOR,
+                                                        None),
+        "unpermute": lambda: m.ssta_tile_unpermute(g, tiled, out),
+    }
+    tensor = bh * wl.seq_len * 128 * 2
+    nbytes = {"tile_pool_token_major": 2 * tensor + bh * wl.n_tiles * 128 * 4,
+              "tile_pool_dim_major": 2 * tensor, "unpermute": 2 * tensor}
+    res = {}
+    for name, call in calls.items():
+        call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record()
+            call()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        gbs = nbytes[name] / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "bytes": nbytes[name], "gbs": round(gbs, 1),
+                     "pct_hbm": round(100 * gbs / PEAK_HBM_GBS, 1)}
+    del tiled, tiled_d, pooled, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def mfma_ceiling(torch, m, iters=160000, reps=3):
     """Sustained bf16 matrix-core rate with the chip fully loaded (2 workgroups
     of 4 waves per CU, as the attention kernel runs), for random and for
@@ -426,6 +538,9 @@ def main():
               flush=True)
 
     variants = variant_runs(torch, m, si, args.variant_steps) if args.variant_steps > 0 else None
+    mat_io = materialised_io(torch, m, wl, g, qd) if args.variant_steps > 0 else None
+    configs = (per_config_runs(torch, m, si, args.config_steps, 1)
+               if args.config_steps > 0 else None)
 
     ceiling = None if args.no_mfma_ceiling else mfma_ceiling(torch, m)
     if ceiling is not None:
@@ -473,6 +588,12 @@ def main():
     for ph in phases:
         ms = phase_stats[ph]["median"]
         gbs = phase_bytes[ph] / (ms * 1e-3) / 1e9 if ms > 0 and phase_bytes[ph] else None
+        if ph == "attention":
+            # requested K/V block bytes: served mostly by L2 and the MALL, so no
+            # fraction of HBM is claimed (the HBM-side bytes are roofline.traffic)
+            phase_rates[ph] = {"logical_bytes": phase_bytes[ph],
+                               "logical_gbs": None if gbs is None else round(gbs, 1)}
+            continue
         phase_rates[ph] = {"bytes": phase_bytes[ph],
                            "gbs": None if gbs is None else round(gbs, 1),
                            "pct_hbm": None if gbs is None else round(100 * gbs / PEAK_HBM_GBS, 1)}
@@ -483,7 +604,8 @@ def main():
     score_tflops = score_flop / (ss_ms * 1e-3) / 1e12 if ss_ms > 0 else 0.0
     phase_rates["score_select"].update({
         "valu_flop": score_flop, "valu_tflops": round(score_tflops, 2),
-        "pct_fp32_vector_peak": round(100 * score_tflops / PEAK_FP32_VECTOR_TFLOPS, 1)})
+        "pct_fp32_unpacked_peak": round(100 * score_tflops / PEAK_FP32_UNPACKED_TFLOPS, 1),
+        "pct_fp32_vector_peak_packed": round(100 * score_tflops / PEAK_FP32_VECTOR_TFLOPS, 1)})
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -524,6 +646,8 @@ def main():
         "mfma_sustained": ceiling,
         "backward": backward,
         "variants": variants,
+        "per_config": configs,
+        "materialised_io": mat_io,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

@@ -41,8 +41,17 @@
  *     text blocks (ssta_block_rows).  Only clip blocks are pooled, scored and
  *     selected; in attention every clip query block also keeps every text
  *     block and a text query block keeps every block.
- *   - Current limits: head_dim == 128, tile_t*tile_h*tile_w == 128 tokens;
- *     ssta_score_select needs n_tiles <= 4096;
+ *   - Kept lists (kv_idx, kv_cnt) are inputs the kernels trust for their
+ *     meaning: every row lists distinct clip block ids in [0, n_tiles),
+ *     ascending, and kv_cnt is in [0, max_kept].  ssta_build_mask writes
+ *     lists of that form.  For memory safety only, the attention kernels
+ *     clamp each count to [0, max_kept] and each id to [0, n_tiles), and the
+ *     backward ignores ids outside that range when it transposes the lists,
+ *     so a malformed list never reads or writes outside the caller's
+ *     buffers; its results are then unspecified.
+ *   - Current limits: head_dim == 128, tile_t*tile_h*tile_w == 128 or 64 tokens;
+ *     ssta_score_select and ssta_scores need n_tiles <= 4096 and
+ *     batch*heads <= 65535;
  *     the attention entry points need n_rows < 65536 (one head's blocks are
  *     addressed with 32-bit offsets).
  */
@@ -71,7 +80,7 @@ typedef enum ssta_status {
 typedef struct ssta_geom {
   int32_t batch, heads, head_dim;   /* head_dim must be 128 */
   int32_t T, H, W;                  /* latent grid, tokens row-major (t, y, x) */
-  int32_t tile_t, tile_h, tile_w;   /* block size; product 128 (so powers of two) */
+  int32_t tile_t, tile_h, tile_w;   /* block size; product 128 or 64 (so powers of two) */
   int32_t text_len;                 /* >= 0 text tokens after the clip's (0: clip only) */
 } ssta_geom_t;
 
@@ -89,6 +98,17 @@ typedef struct ssta_params {
                                    equation */
   uint32_t flags;               /* SSTA_* flags below */
 } ssta_params_t;
+
+/*
+ * Fills *p with the parameters the pages use: window half-widths (1, 1, 1),
+ * topk 0 (set it to the number of blocks to select), lambda_ = 0.9f and
+ * beta = 1 - lambda_ (the importance_sampling excerpt's weights: its 0.9
+ * and 1 - 0.9 applied to fp32 scores act as the fp32 values 0.9f and 0.1f),
+ * scale = 1/sqrt(head_dim) rounded to fp32 (the attention equation's
+ * 1/sqrt(d_k)), no flags.  head_dim must be >= 1.
+ * Returns SSTA_OK, or SSTA_ERR_ARG for a null pointer or head_dim < 1.
+ */
+int ssta_default_params(ssta_params_t* p, int32_t head_dim);
 
 /* Step 4 prints the combination as a logical AND; the default is the union of
  * window and selection.  With this flag the kept set is their intersection

@@ -95,8 +95,9 @@ def lse_bound(wl, q, k, rows) -> np.ndarray:
 
     Three error sources, each bounded generously:
     - the denominator sums the probabilities after rounding them to bf16 (the
-      same weights the P.V product uses): relative error at most 2^-9, so
-      the LSE moves by at most log(1 + 2^-9);
+      same weights the P.V product uses): round-to-nearest bf16 keeps 8
+      significand bits, so each weight is off by at most a relative 2^-8
+      (the unit roundoff), and the LSE moves by at most log(1 + 2^-8);
     - each score is a 128-term fp32 accumulation on the matrix cores: error at
       most 128 * 2^-23 * sum_d |q_d k_d| <= 2^-16 * |q| * |k| (Cauchy-Schwarz),
       times the softmax scale; the LSE, a smooth maximum of the scores, moves
@@ -112,7 +113,7 @@ def lse_bound(wl, q, k, rows) -> np.ndarray:
     bh = rows // wl.n_rows
     tok = token_rows(wl, rows)
     scale = oracle.default_scale(wl)
-    return (np.log1p(2.0 ** -9) + 2.0 ** -16 * scale * qn[bh[:, None], tok] * kmax[bh][:, None]
+    return (np.log1p(2.0 ** -8) + 2.0 ** -16 * scale * qn[bh[:, None], tok] * kmax[bh][:, None]
             + 2.0 ** -12)
 
 
@@ -167,7 +168,8 @@ def bwd_bounds(wl, q, k, v, do, kv_idx, kv_cnt, q_rows, k_rows):
     """Per-element error bounds [len(rows), R, 128] on dq (q_rows) and dk, dv
     (k_rows) of the GPU backward, derived from its arithmetic (worst case,
     every error of one sign):
-      - dS and P enter the products rounded to bf16 (relative 2^-9) and P is
+      - dS and P enter the products rounded to bf16 (relative 2^-8, the unit
+        roundoff of an 8-bit significand) and P is
         recomputed from an LSE that carries its own small error; both are
         covered by 2^-7 relative on each term, so dq gets
         scale * 2^-7 * sum_b |dS_ab| |k_b| (dk likewise with |q_a|, dv with

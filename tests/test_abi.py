@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import video_dit_block_tile_amd as m
@@ -44,9 +45,14 @@ def test_header_is_plain_c(tmp_path):
 #include "ssta.h"
 int main(void) {
   ssta_geom_t g = {1, 2, 128, 4, 16, 16, 2, 8, 8, 77};
-  ssta_params_t p = {1, 1, 1, 2, 0.9f, 0.1f, 0.08838834764831845f, 0u};
-  printf("%lld %d %d %s\n", (long long)ssta_block_rows(&g), ssta_topk_width(&g, &p),
-         ssta_max_kept(&g, &p), ssta_status_string(SSTA_ERR_SHAPE));
+  ssta_params_t p;
+  if (ssta_default_params(&p, 128) != SSTA_OK) return 1;
+  if (ssta_default_params(NULL, 128) != SSTA_ERR_ARG) return 2;
+  p.topk = 2;
+  printf("%lld %d %d %a %a %a %d %d %d %u %s\n", (long long)ssta_block_rows(&g),
+         ssta_topk_width(&g, &p), ssta_max_kept(&g, &p), (double)p.lambda_, (double)p.beta,
+         (double)p.scale, p.win_t, p.win_h, p.win_w, p.flags,
+         ssta_status_string(SSTA_ERR_SHAPE));
   return 0;
 }
 """)
@@ -56,8 +62,14 @@ int main(void) {
                     str(src), lib, "-o", str(exe)], check=True)
     env = dict(os.environ, LD_LIBRARY_PATH=os.path.dirname(lib))
     out = subprocess.run([str(exe)], capture_output=True, text=True, env=env, check=True).stdout
-    rows, width, kept, text = out.split(maxsplit=3)
+    rows, width, kept, lam, beta, scale, wt, wh, ww, flags, text = out.split(maxsplit=10)
     assert (int(rows), int(width), int(kept)) == (9, 2, 8)
+    # the pages' defaults as the library states them: lambda 0.9 and 1 - 0.9 as
+    # fp32 values, the attention equation's 1/sqrt(128), window +-1, no flags
+    assert float.fromhex(lam) == float(np.float32(0.9))
+    assert float.fromhex(beta) == float(np.float32(1.0 - 0.9))
+    assert float.fromhex(scale) == float(np.float32(1.0 / np.sqrt(128.0)))
+    assert (int(wt), int(wh), int(ww), int(flags)) == (1, 1, 1, 0)
     assert text.strip() == lib_status_text(SHAPE)
 
 
@@ -163,6 +175,37 @@ def test_workspace_and_score_validation():
     big = m.make_geom(1, 1, 80, 64, 128)                # 40 x 8 x 16 = 5120 blocks
     assert lib.ssta_score_select(ctypes.byref(big), ctypes.byref(p), 16, 16, 16, 16, 1 << 40,
                                  None) == SHAPE
+
+
+def test_default_params_through_the_binding():
+    """make_params takes its defaults from ssta_default_params (no formula in
+    the binding) and agrees with the oracle's constants."""
+    import oracle
+    p = m.make_params(topk=7)
+    assert np.float32(p.lambda_) == oracle.DEFAULT_LAMBDA
+    assert np.float32(p.beta) == oracle.DEFAULT_BETA
+    assert np.float32(p.scale) == np.float32(1.0 / np.sqrt(128.0))
+    assert (p.win_t, p.win_h, p.win_w, p.topk, p.flags) == (1, 1, 1, 7, 0)
+    q = m.make_params(head_dim=64)
+    assert np.float32(q.scale) == np.float32(0.125)
+    assert m.load().ssta_default_params(None, 128) == ARG
+    r = L.SstaParams()
+    assert m.load().ssta_default_params(ctypes.byref(r), 0) == ARG
+
+
+def test_score_heads_limit():
+    """The scoring grids put batch*heads on a grid axis: more than 65535 is a
+    shape error, not a launch failure."""
+    lib = m.load()
+    p = m.make_params(topk=2)
+    ok = m.make_geom(5, 13107, 2, 8, 8)                  # 65535 heads, one block each
+    over = m.make_geom(2, 32768, 2, 8, 8)                # 65536
+    assert lib.ssta_score_select(ctypes.byref(ok), ctypes.byref(p), 16, 16, 16, 16, 1,
+                                 None) == WS
+    assert lib.ssta_score_select(ctypes.byref(over), ctypes.byref(p), 16, 16, 16, 16, 1 << 40,
+                                 None) == SHAPE
+    assert lib.ssta_scores(ctypes.byref(over), ctypes.byref(p), 16, 16, 16, None, 16, 1 << 40,
+                           None) == SHAPE
 
 
 def test_size_limits_at_the_boundary():

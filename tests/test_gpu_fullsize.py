@@ -6,9 +6,12 @@ does not divide, at 720p 10 s with 256 text tokens after the clip, and at
 selection takes (4096 blocks in one head).
 
 Block means, top-k ids, kept lists and counts are compared in full, bit for
-bit.  The attention output is compared on a deterministic sample of rows that
-includes every corner and edge block, against the fp64 oracle.  Dense
-attention (every block kept) is checked on the 480p shapes.
+bit.  The attention output and LSE are compared against the fp64 oracle on
+every row at tiny, 480p-short and 480p-5s, on every query block of the
+first head at the 720p shapes (plus the corner and edge blocks of the last
+head), and on a sample that includes every corner and edge block at the
+largest grid.  Dense attention (every block kept) is checked on the 480p
+shapes.
 """
 import numpy as np
 import pytest
@@ -20,6 +23,22 @@ from _helpers import (O_MAX_ABS, O_MEAN_ABS, check_lse, compare_o, geom_of, o_ro
                       sample_rows, to_dev)
 
 pytestmark = pytest.mark.gpu
+
+
+EVERY_ROW = ("tiny", "480p-short", "480p-5s")
+HEAD_ROWS = ("720p-5s", "720p-10s", "720p-10s-latent", "720p-10s-text", "720p-10s-t64")
+
+
+def parity_rows(wl, name):
+    """Rows (b*heads + h)*n_rows + i compared with the oracle: all of them, all of
+    the first head's (plus the sampled corner and edge blocks of the last), or
+    the corner/edge sample."""
+    if name in EVERY_ROW:
+        return np.arange(wl.batch * wl.heads * wl.n_rows, dtype=np.int64)
+    if name in HEAD_ROWS:
+        sample = sample_rows(wl, 0, seed=1)
+        return np.union1d(np.arange(wl.n_rows, dtype=np.int64), sample)
+    return sample_rows(wl, 16, seed=1)
 
 
 @pytest.mark.parametrize("name", ["tiny", "480p-short", "480p-5s", "720p-5s", "720p-10s",
@@ -44,13 +63,14 @@ def test_full_shape(name):
     assert np.array_equal(plan.topk_idx.cpu().numpy(), sel["topk"])
     assert np.array_equal(plan.kv_cnt.cpu().numpy(), sel["kv_cnt"])
     assert np.array_equal(plan.kv_idx.cpu().numpy(), sel["kv_idx"])
-    rows = sample_rows(wl, 16, seed=1)
+    rows = parity_rows(wl, name)
     o_ref, lse_ref = oracle.attention(wl, q, k, v, sel["kv_idx"], sel["kv_cnt"], rows)
     mx, mean = compare_o(o_rows(wl, plan.o, rows), o_ref)
-    print("[%s] O max-abs %.3e mean-abs %.3e" % (name, mx, mean), flush=True)
-    assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS
     lse = plan.lse.cpu().numpy().reshape(-1, wl.tile_tokens)[rows]
-    check_lse(wl, q, k, rows, lse, lse_ref)
+    ratio = check_lse(wl, q, k, rows, lse, lse_ref)
+    print("[%s] %d rows: O max-abs %.3e mean-abs %.3e, LSE error / bound %.3f"
+          % (name, len(rows), mx, mean, ratio), flush=True)
+    assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS
 
 
 @pytest.mark.parametrize("name", ["480p-short", "480p-5s"])
@@ -67,7 +87,8 @@ def test_dense_shape(name):
     rows = sample_rows(wl, 4, seed=2)[:12]
     o_ref, lse_ref = oracle.attention(wl, q, k, v, kv_idx, kv_cnt, rows)
     mx, mean = compare_o(o_rows(wl, plan.o, rows), o_ref)
-    print("[%s dense] O max-abs %.3e mean-abs %.3e" % (name, mx, mean), flush=True)
-    assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS
     lse = plan.lse.cpu().numpy().reshape(-1, wl.tile_tokens)[rows]
-    check_lse(wl, q, k, rows, lse, lse_ref)
+    ratio = check_lse(wl, q, k, rows, lse, lse_ref)
+    print("[%s dense] O max-abs %.3e mean-abs %.3e, LSE error / bound %.3f"
+          % (name, mx, mean, ratio), flush=True)
+    assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS

@@ -10,7 +10,6 @@ kernels; there is no fallback when the library is missing.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import torch
@@ -87,6 +86,7 @@ SIGNATURES = {
     "ssta_attention_bwd_workspace_bytes": (_i64, [_G]),
     "ssta_attention_bwd": (ctypes.c_int, [_G, _P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                           _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "ssta_default_params": (ctypes.c_int, [_P, _i32]),
     "ssta_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ssta_last_hip_error": (ctypes.c_int, []),
 }
@@ -132,14 +132,22 @@ def make_geom(batch, heads, T, H, W, tile=(2, 8, 8), head_dim=128, text_len=0) -
     return SstaGeom(batch, heads, head_dim, T, H, W, *tile, text_len)
 
 
-def make_params(win=(1, 1, 1), topk=0, lambda_=0.9, beta=None, scale=None, flags=0,
+def make_params(win=(1, 1, 1), topk=0, lambda_=None, beta=None, scale=None, flags=0,
                 head_dim=128) -> SstaParams:
-    """Defaults follow the pages: lambda 0.9, redundancy weight 1 - lambda, scale 1/sqrt(d)."""
-    if beta is None:
-        beta = 1.0 - lambda_
-    if scale is None:
-        scale = 1.0 / math.sqrt(head_dim)
-    return SstaParams(win[0], win[1], win[2], topk, lambda_, beta, scale, flags)
+    """ssta_default_params (the pages' lambda, redundancy weight and 1/sqrt(d)
+    scale, from the library) with the given fields overridden."""
+    p = SstaParams()
+    _call("ssta_default_params", ctypes.byref(p), head_dim)
+    p.win_t, p.win_h, p.win_w = win
+    p.topk = topk
+    p.flags = flags
+    if lambda_ is not None:
+        p.lambda_ = lambda_
+    if beta is not None:
+        p.beta = beta
+    if scale is not None:
+        p.scale = scale
+    return p
 
 
 def _ptr(t):

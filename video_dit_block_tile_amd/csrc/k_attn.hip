@@ -197,31 +197,37 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint8_t* base,
 // Tile-major: 64 contiguous rows.  Token-major: the rows of the block's
 // tokens; in-block positions are a bit-field code of (t, y, x) offsets, so
 // position 64p + r lies at token offset in_block_offset(64p) +
-// in_block_offset(r) from the block's origin.  kGen (ragged grids, joint
-// text): bit r of `valid` says whether position 64p + r of the block exists;
-// a token-major gather redirects the rows that do not to an existing row
-// (their probabilities are zero).  Blocks from n_tiles on are text blocks,
-// whose positions are consecutive tokens after the clip's.  `offs`: the K or
-// V offsets of a DmaOffsets<kR>.
+// in_block_offset(r) from the block's origin.  Blocks from n_tiles on are
+// text blocks, whose positions are consecutive tokens after the clip's.
+// kGen (ragged grids, joint text): bit r of `valid` says whether position
+// 64p + r of the block exists.  In a unit with missing positions the scalar
+// base is the block's first token, which every block has, and a missing row
+// reads that row (both K and V: a missing key's probability is exactly zero,
+// and the row it reads is a finite row of the same head).  The scalar offset
+// is outside the buffer range check, so no base may point past the head's
+// tokens.  `offs`: the K or V offsets of a DmaOffsets<kR>.
 template <bool kTokK, bool kGen, int kR, bool kV>
 __device__ __forceinline__ void dma_rows(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, const Geo& g,
                                          int64_t j, int p, int wave, int lane, uint64_t valid,
                                          const uint32_t* offs) {
   constexpr int kL = Blk<kR>::kLoads;
   const bool text = kGen && kTokK && j >= g.n_tiles;
-  uint32_t so =
-      kTokK ? (block_origin32(g, (uint32_t)j) + (p ? in_block_offset(g, 64) : 0u)) * 256u
-            : (uint32_t)(j * Blk<kR>::kBytes + p * kSlotBytes);
-  if (text) so = (uint32_t)((g.N + (j - g.n_tiles) * kR + 64 * p) * 256);
+  const bool part = kGen && kTokK && valid != ~0ull;
+  uint32_t so, half = 0u;
+  if (kTokK) {
+    const uint32_t origin =
+        text ? (uint32_t)(g.N + (j - g.n_tiles) * kR) : block_origin32(g, (uint32_t)j);
+    half = p ? (text ? 64u : in_block_offset(g, 64)) * 256u : 0u;
+    so = origin * 256u + (part ? 0u : half);
+  } else {
+    so = (uint32_t)(j * Blk<kR>::kBytes + p * kSlotBytes);
+  }
 #pragma unroll
   for (int mm = 0; mm < kL; ++mm) {
     uint32_t vo = offs[mm];
     const int r = 4 * (kL * wave + mm) + (lane >> 4);
     if (text) vo = r * 256 + (((lane & 15) ^ row_swz<kV>(r)) << 4);
-    // (V rows need no redirect: a missing key's probability is exactly zero,
-    // and its row holds another token of the head or, past the head, the
-    // zeros of the range check)
-    if (!kV && kGen && kTokK && valid != ~0ull && !((valid >> r) & 1u)) vo &= 255u;
+    if (part) vo = ((valid >> r) & 1u) ? vo + half : (vo & 255u);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (kL * wave + mm) * 1024), 16,
                                              vo, so, 0, 0);
   }
@@ -308,7 +314,10 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
   // a text query block, or dense attention, takes every block in order.
   const bool all_blocks = a.kv_cnt == nullptr || qtext;
   const int64_t kvrow = bh * g.n_tiles + qi;
-  const int listed = all_blocks ? 0 : a.kv_cnt[kvrow];
+  // Lists come from the caller: the count is clamped to the row's capacity
+  // and every id to a clip block, so a malformed list reads only the head's
+  // own blocks.
+  const int listed = all_blocks ? 0 : min(max(a.kv_cnt[kvrow], 0), a.max_kept);
   const int cnt = all_blocks ? (int)g.n_rows : listed + (kGen ? g.n_txt : 0);
   const int32_t* idx = all_blocks ? nullptr : a.kv_idx + kvrow * a.max_kept;
 
@@ -346,6 +355,7 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
   const int vofs = kTok ? v_lane_offset(lane) : 0;
   // Kept-block ids, 64 at a time: lane i holds entry ibase + i.
   int ibase = 0;
+  const int last_tile = (int)g.n_tiles - 1;
   int ids = (!all_blocks && lane < listed) ? idx[lane] : 0;
   auto block_at = [&](int pos) -> int64_t {
     if (all_blocks) return pos;
@@ -354,7 +364,7 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
       ibase += 64;
       ids = (ibase + lane < listed) ? idx[ibase + lane] : 0;
     }
-    return __builtin_amdgcn_readlane(ids, pos - ibase);
+    return min(max(__builtin_amdgcn_readlane(ids, pos - ibase), 0), last_tile);
   };
   uint64_t valid_next = ~0ull;   // positions of the unit loaded last that exist
   if (units > 0) {

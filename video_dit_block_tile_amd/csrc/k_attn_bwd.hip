@@ -188,7 +188,9 @@ struct IdStream {
   bool dense;
   __device__ __forceinline__ void fill(const Geo& g, int lane) {
     const int pos = base + lane;
-    ids = dense ? pos : (pos < cnt ? idx[pos] : 0);
+    // a caller's id outside the clip's blocks is clamped to one, so a
+    // malformed list reads only the head's own blocks
+    ids = dense ? pos : (pos < cnt ? min(max(idx[pos], 0), (int)g.n_tiles - 1) : 0);
     org = block_origin32(g, (uint32_t)min(ids, (int)g.n_tiles - 1));
   }
   __device__ __forceinline__ void init(const Geo& g, const int32_t* p, int c, bool d, int lane) {
@@ -268,7 +270,7 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, AttnGrid grid) {
   // (or dense attention) takes every block
   const bool all_blocks = a.kv_cnt == nullptr || (kGen && qi >= g.n_tiles);
   const int64_t kvrow = bh * g.n_tiles + qi;
-  const int listed = all_blocks ? 0 : a.kv_cnt[kvrow];
+  const int listed = all_blocks ? 0 : min(max(a.kv_cnt[kvrow], 0), a.max_kept);
   const int cnt = all_blocks ? (int)g.n_rows : listed + (kGen ? g.n_txt : 0);
   IdStream ids;
   ids.init(g, all_blocks ? nullptr : a.kv_idx + kvrow * a.max_kept, listed, all_blocks, lane);
@@ -611,6 +613,7 @@ __global__ __launch_bounds__(256) void k_set_bits(Geo g, const int32_t* __restri
   if (row >= g.bh * g.n_tiles || c >= kv_cnt[row]) return;
   const int64_t bh = row / g.n_tiles, i = row % g.n_tiles;
   const int64_t j = kv_idx[row * max_kept + c];
+  if (j < 0 || j >= g.n_tiles) return;   // not a clip block: no bit to set
   atomicOr(mask_t + (bh * g.n_tiles + j) * words + (i >> 5), 1u << (i & 31));
 }
 

@@ -175,6 +175,7 @@ int score_common(const ssta_geom_t* g, const ssta_params_t* p, const float* qp,
   SSTA_TRY(check_ptr(qp, false));
   SSTA_TRY(check_ptr(kp, false));
   if (geo->n_tiles > ssta::kMaxTopkTiles) return SSTA_ERR_SHAPE;
+  if (geo->bh > ssta::kMaxScoreHeads) return SSTA_ERR_SHAPE;
   *lay = ws_layout(*geo);
   if (ws == nullptr || (int64_t)ws_bytes < lay->total) return SSTA_ERR_WORKSPACE;
   SSTA_TRY(check_ptr(ws, false));
@@ -184,6 +185,19 @@ int score_common(const ssta_geom_t* g, const ssta_params_t* p, const float* qp,
 }  // namespace
 
 extern "C" {
+
+int ssta_default_params(ssta_params_t* p, int32_t head_dim) {
+  if (p == nullptr || head_dim < 1) return SSTA_ERR_ARG;
+  p->win_t = p->win_h = p->win_w = 1;
+  p->topk = 0;
+  // The excerpt's Python scalars 0.9 and 1 - 0.9 scale fp32 tensors, so they
+  // act as their fp32 roundings (1 - 0.9 is formed in double first).
+  p->lambda_ = 0.9f;
+  p->beta = (float)(1.0 - 0.9);
+  p->scale = (float)(1.0 / std::sqrt((double)head_dim));
+  p->flags = 0u;
+  return SSTA_OK;
+}
 
 int ssta_tile_pool(const ssta_geom_t* g, const void* x, void* x_tiled, int32_t layout,
                    float* pooled, void* stream) {

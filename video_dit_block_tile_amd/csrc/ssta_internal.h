@@ -11,6 +11,7 @@ constexpr int kHeadDim = 128;     // channels per head
 constexpr int kTileTokens = 128;  // tokens per 3D block (the default 2x8x8 block)
 constexpr int kSmallTile = 64;    // tokens per block of the smaller shape (e.g. 4x4x4)
 constexpr int kMaxTopkTiles = 4096;
+constexpr int64_t kMaxScoreHeads = 65535;   // batch*heads of the scoring grids
 
 // Geometry with every derived quantity precomputed on the host.
 struct Geo {
