@@ -196,20 +196,32 @@ static float dot_f32(const float* a, const float* b, int32_t D) {
  * [TR] Step 2, Score_r; [BLOG] gate_unique with the diagonal removed and a
  * mean over the remaining key blocks.
  * u(i, j) = (khat_i . khat_j + 1) * 0.5;
- * red[j] = (sum over i != j, ascending i, fp32, of u(i, j)) / (n - 1);
- * red = 0 when n == 1.  Reading: the normaliser counts key blocks (n - 1);
- * the summary page's "N - 1" reuses the letter it gave the block size.
+ * red[j] = (sum over the groups G = [128g, 128g + 128) of key blocks, in
+ *           ascending g, of (sum over i in G, i != j, ascending i, fp32,
+ *           starting from 0, of u(i, j))) / (n - 1);
+ * red = 0 when n == 1.  Readings: the normaliser counts key blocks (n - 1);
+ * the summary page's "N - 1" reuses the letter it gave the block size.  The
+ * pages' mean over the other key blocks leaves the order of the sum open;
+ * this two-level order (a partial sum per group of 128 key blocks, the
+ * partials added in ascending group order) is fixed here because the
+ * selection must be reproducible bit for bit.  With n <= 128 it is the plain
+ * ascending sum.
  */
+enum { RED_GROUP = 128 };
 void orc_redundancy(int64_t BH, int64_t n, int32_t D, const float* khat, float* red) {
 #pragma omp parallel for schedule(dynamic, 16)
   for (int64_t bhj = 0; bhj < BH * n; ++bhj) {
     const int64_t bh = bhj / n, j = bhj % n;
     const float* kb = khat + bh * n * D;
     float s = 0.0f;
-    for (int64_t i = 0; i < n; ++i) {
-      if (i == j) continue;
-      const float u = (dot_f32(kb + i * D, kb + j * D, D) + 1.0f) * 0.5f;
-      s = s + u;
+    for (int64_t g0 = 0; g0 < n; g0 += RED_GROUP) {
+      float part = 0.0f;
+      for (int64_t i = g0; i < n && i < g0 + RED_GROUP; ++i) {
+        if (i == j) continue;
+        const float u = (dot_f32(kb + i * D, kb + j * D, D) + 1.0f) * 0.5f;
+        part = part + u;
+      }
+      s = s + part;
     }
     red[bhj] = (n > 1) ? s / (float)(n - 1) : 0.0f;
   }

@@ -110,6 +110,45 @@ def test_redundancy_identity_fp64():
     assert np.max(np.abs(red - want)) < 2e-6
 
 
+def test_redundancy_many_blocks():
+    """280 key blocks (three groups of the two-level sum): the value still meets
+    the fp64 identity, and the order is the stated one: group partials from 0
+    in ascending i, added in ascending group order (replayed in float32; the
+    plain ascending sum differs from it in the last bits somewhere)."""
+    wl = si.ALL["480p-5s"].with_(heads=2)
+    kh = oracle.normalize(oracle.pool(wl, si.generate(wl, 1)))
+    red = oracle.redundancy(kh)
+    k64 = kh.astype(np.float64)
+    n = k64.shape[-2]
+    assert n == 280
+    tot = k64.sum(axis=-2, keepdims=True)
+    off = (k64 * tot).sum(-1) - (k64 * k64).sum(-1)
+    assert np.max(np.abs(red - (off + (n - 1)) / 2.0 / (n - 1))) < 2e-6
+    u = ((np.einsum("hid,hjd->hij", kh[0].astype(np.float32), kh[0].astype(np.float32))
+          + np.float32(1)) * np.float32(0.5)).astype(np.float32)
+    grouped = np.empty((2, n), np.float32)
+    plain = np.empty((2, n), np.float32)
+    for h in range(2):
+        for j in range(n):
+            col = u[h, :, j].copy()
+            col[j] = 0.0                                   # +0 in place of the diagonal
+            s = np.float32(0)
+            for g0 in range(0, n, 128):
+                part = np.float32(0)
+                for x in col[g0:g0 + 128]:
+                    part = np.float32(part + x)
+                s = np.float32(s + part)
+            grouped[h, j] = s / np.float32(n - 1)
+            t = np.float32(0)
+            for x in col:
+                t = np.float32(t + x)
+            plain[h, j] = t / np.float32(n - 1)
+    # the dot products here come from numpy, not the oracle's fmaf chain, so
+    # compare the sum orders through their rounding, not bit for bit
+    assert np.max(np.abs(grouped - red[0])) < 1e-6
+    assert not np.array_equal(grouped, plain)
+
+
 def test_scores_fp64_formula():
     wl = si.ALL["ragged"]
     q, k = si.generate(wl, 0), si.generate(wl, 1)
