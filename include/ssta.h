@@ -169,9 +169,12 @@ int64_t ssta_workspace_bytes(const ssta_geom_t* g, const ssta_params_t* p);
  * division; a zero vector stays zero); Score_s(i,j) = (qhat_i.khat_j+1)/2;
  * Score_r(j) = mean over key blocks i != j of (khat_i.khat_j+1)/2;
  * Score_i = lambda_*Score_s - beta*Score_r.  Every dot product is an fp32
- * fused-multiply-add chain in ascending channel order, the redundancy sum
- * runs in ascending i, and nothing else is fused, so the selection is a
- * deterministic function of the inputs.  Ties go to the lower block id.
+ * fused-multiply-add chain in ascending channel order; the redundancy sum
+ * adds, from +0, the terms of each group of 128 key blocks in ascending i,
+ * then the group sums in ascending group order; nothing else is fused.  The
+ * selection is thus a deterministic function of the inputs.  Ties go to the
+ * lower block id.  The workspace holds qhat, khat, Score_r, its group sums
+ * and the Score_i matrix (bh * n_tiles^2 floats) that the top-k reads.
  */
 int ssta_score_select(const ssta_geom_t* g, const ssta_params_t* p, const float* q_pooled,
                       const float* k_pooled, int32_t* topk_idx, void* workspace,

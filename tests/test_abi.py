@@ -159,8 +159,11 @@ def test_widths_and_capacity():
     assert m.ssta_topk_width(g, p) == 1799
     gt = m.make_geom(1, 2, 4, 16, 16)                   # 2 x 2 x 2 blocks
     assert m.ssta_max_kept(gt, m.make_params(topk=2)) == 8
+    # the normalised means, Score_r, its partial sums per group of 128 key
+    # blocks and Score_i (16 x 1800 x 1800 fp32), each region 256-byte aligned
     ws = m.ssta_workspace_bytes(g, m.make_params(topk=48))
-    assert ws >= 16 * 1800 * 1800 * 4 + 2 * 16 * 1800 * 128 * 4
+    need = 2 * 16 * 1800 * 128 * 4 + 16 * 1800 * 4 + 16 * 15 * 1800 * 4 + 16 * 1800 * 1800 * 4
+    assert need <= ws < need + 5 * 256
 
 
 def test_workspace_and_score_validation():

@@ -114,8 +114,10 @@ int32_t max_kept(const Geo& g, const ssta_params_t* p) {
 
 constexpr int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
+// Scoring workspace: the normalised means, Score_r, its group partials and
+// the Score_i matrix the top-k reads.
 struct WsLayout {
-  int64_t qhat, khat, red, scores, total;
+  int64_t qhat, khat, red, part, scores, total;
 };
 
 WsLayout ws_layout(const Geo& g) {
@@ -124,7 +126,8 @@ WsLayout ws_layout(const Geo& g) {
   w.qhat = 0;
   w.khat = align256(vec);
   w.red = w.khat + align256(vec);
-  w.scores = w.red + align256(g.bh * g.n_tiles * 4);
+  w.part = w.red + align256(g.bh * g.n_tiles * 4);
+  w.scores = w.part + align256(g.bh * ssta::red_groups(g.n_tiles) * g.n_tiles * 4);
   w.total = w.scores + align256(g.bh * g.n_tiles * g.n_tiles * 4);
   return w;
 }
@@ -248,6 +251,39 @@ int64_t ssta_workspace_bytes(const ssta_geom_t* g, const ssta_params_t* p) {
   return ws_layout(geo).total;
 }
 
+namespace {
+ssta::ScoreArgs score_args(const ssta_params_t* p, const float* q_pooled, const float* k_pooled,
+                           uint8_t* ws, const WsLayout& lay) {
+  ssta::ScoreArgs sa;
+  sa.q_pooled = q_pooled;
+  sa.k_pooled = k_pooled;
+  sa.qhat = reinterpret_cast<float*>(ws + lay.qhat);
+  sa.khat = reinterpret_cast<float*>(ws + lay.khat);
+  sa.red = reinterpret_cast<float*>(ws + lay.red);
+  sa.part = reinterpret_cast<float*>(ws + lay.part);
+  sa.lambda_ = p->lambda_;
+  sa.beta = p->beta;
+  return sa;
+}
+
+int score_select_into(const Geo& geo, const ssta_params_t* p, const float* q_pooled,
+                      const float* k_pooled, int32_t* topk_idx, uint8_t* ws, const WsLayout& lay,
+                      int32_t width, hipStream_t st) {
+  const ssta::ScoreArgs sa = score_args(p, q_pooled, k_pooled, ws, lay);
+  SSTA_TRY(hip_status(ssta::launch_score_prepare(geo, sa, st)));
+  ssta::TopkArgs ta;
+  ta.scores = reinterpret_cast<float*>(ws + lay.scores);
+  ta.topk_idx = topk_idx;
+  ta.k = p->topk;
+  ta.width = width;
+  ta.exclude_window = (p->flags & SSTA_TOPK_EXCLUDE_WINDOW) ? 1 : 0;
+  ta.wt = p->win_t;
+  ta.wh = p->win_h;
+  ta.ww = p->win_w;
+  return hip_status(ssta::launch_select(geo, sa, ta, st));
+}
+}  // namespace
+
 int ssta_score_select(const ssta_geom_t* g, const ssta_params_t* p, const float* q_pooled,
                       const float* k_pooled, int32_t* topk_idx, void* workspace,
                       size_t ws_bytes, void* stream) {
@@ -258,27 +294,8 @@ int ssta_score_select(const ssta_geom_t* g, const ssta_params_t* p, const float*
   SSTA_TRY(check_ptr(topk_idx, width == 0));
   SSTA_TRY(check_device());
   if (width == 0) return SSTA_OK;   // nothing to select: topk_idx has no columns
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  ssta::ScoreArgs sa;
-  sa.q_pooled = q_pooled;
-  sa.k_pooled = k_pooled;
-  sa.qhat = reinterpret_cast<float*>(ws + lay.qhat);
-  sa.khat = reinterpret_cast<float*>(ws + lay.khat);
-  sa.red = reinterpret_cast<float*>(ws + lay.red);
-  sa.scores = reinterpret_cast<float*>(ws + lay.scores);
-  sa.lambda_ = p->lambda_;
-  sa.beta = p->beta;
-  SSTA_TRY(hip_status(ssta::launch_scores(geo, sa, as_stream(stream))));
-  ssta::TopkArgs ta;
-  ta.scores = sa.scores;
-  ta.topk_idx = topk_idx;
-  ta.k = p->topk;
-  ta.width = width;
-  ta.exclude_window = (p->flags & SSTA_TOPK_EXCLUDE_WINDOW) ? 1 : 0;
-  ta.wt = p->win_t;
-  ta.wh = p->win_h;
-  ta.ww = p->win_w;
-  return hip_status(ssta::launch_topk(geo, ta, as_stream(stream)));
+  return score_select_into(geo, p, q_pooled, k_pooled, topk_idx,
+                           static_cast<uint8_t*>(workspace), lay, width, as_stream(stream));
 }
 
 int ssta_scores(const ssta_geom_t* g, const ssta_params_t* p, const float* q_pooled,
@@ -290,17 +307,10 @@ int ssta_scores(const ssta_geom_t* g, const ssta_params_t* p, const float* q_poo
   SSTA_TRY(check_ptr(scores, false));
   SSTA_TRY(check_ptr(red, true));
   SSTA_TRY(check_device());
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  ssta::ScoreArgs sa;
-  sa.q_pooled = q_pooled;
-  sa.k_pooled = k_pooled;
-  sa.qhat = reinterpret_cast<float*>(ws + lay.qhat);
-  sa.khat = reinterpret_cast<float*>(ws + lay.khat);
-  sa.red = red != nullptr ? red : reinterpret_cast<float*>(ws + lay.red);
-  sa.scores = scores;
-  sa.lambda_ = p->lambda_;
-  sa.beta = p->beta;
-  return hip_status(ssta::launch_scores(geo, sa, as_stream(stream)));
+  ssta::ScoreArgs sa = score_args(p, q_pooled, k_pooled, static_cast<uint8_t*>(workspace), lay);
+  if (red != nullptr) sa.red = red;
+  SSTA_TRY(hip_status(ssta::launch_score_prepare(geo, sa, as_stream(stream))));
+  return hip_status(ssta::launch_score_matrix(geo, sa, scores, as_stream(stream)));
 }
 
 int ssta_build_mask(const ssta_geom_t* g, const ssta_params_t* p, const int32_t* topk_idx,

@@ -126,26 +126,35 @@ hipError_t launch_tile_pool(const Geo& g, const void* x, void* x_tiled, int layo
                             float* pooled, hipStream_t s);
 hipError_t launch_tile_unpermute(const Geo& g, const void* x_tiled, void* x, hipStream_t s);
 
+// Step 2 scoring.  qhat, khat: [bh][n][128] normalised means; red: [bh][n]
+// Score_r; part: [bh][red_groups(n)][n] partial sums of Score_r (one per
+// group of kRedGroup key blocks).
+constexpr int kRedGroup = 128;
+int red_groups(int64_t n);
 struct ScoreArgs {
   const float* q_pooled;
   const float* k_pooled;
   float* qhat;
   float* khat;
   float* red;
-  float* scores;
+  float* part;
   float lambda_, beta;
 };
-hipError_t launch_scores(const Geo& g, const ScoreArgs& a, hipStream_t s);
+// normalise both means, then Score_r
+hipError_t launch_score_prepare(const Geo& g, const ScoreArgs& a, hipStream_t s);
+// the Score_i matrix [bh][n][n] (after launch_score_prepare)
+hipError_t launch_score_matrix(const Geo& g, const ScoreArgs& a, float* scores, hipStream_t s);
 
 struct TopkArgs {
-  const float* scores;
+  float* scores;        // [bh][n][n] Score_i, written then read by launch_select
   int32_t* topk_idx;
   int32_t k;            // requested top-k
   int32_t width;        // row width of topk_idx
   int32_t exclude_window;
   int32_t wt, wh, ww;
 };
-hipError_t launch_topk(const Geo& g, const TopkArgs& a, hipStream_t s);
+// Score_i into t.scores, then the per-row top-k (after launch_score_prepare)
+hipError_t launch_select(const Geo& g, const ScoreArgs& a, const TopkArgs& t, hipStream_t s);
 
 struct MaskArgs {
   const int32_t* topk_idx;
