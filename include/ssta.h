@@ -181,6 +181,26 @@ int ssta_score_select(const ssta_geom_t* g, const ssta_params_t* p, const float*
                       size_t ws_bytes, void* stream);
 
 /*
+ * ssta_score_select without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc).  Same inputs, output and results as
+ * ssta_score_select.  The scratch is a static device array of 64 MiB that
+ * the library holds on every GPU it runs on until the process ends; the heads
+ * are scored in groups that fit it.  Allocates nothing and calls no
+ * allocating routine.
+ *   Errors: as ssta_score_select (no SSTA_ERR_WORKSPACE), and SSTA_ERR_SHAPE
+ *   when one head's scoring state (normalised means, Score_r and its group
+ *   sums, the n_tiles^2 Score_i matrix: about n_tiles^2 * 4 bytes) exceeds
+ *   the 64 MiB, i.e. beyond about 3,940 blocks per head.
+ *   Every call on a GPU uses that GPU's one array: calls that overlap on one
+ *   GPU (other streams, other host threads) race and give wrong ids;
+ *   serialise them.  Nothing in the array needs to start at zero.
+ */
+int ssta_score_select_noalloc(const ssta_geom_t* g, const ssta_params_t* p,
+                              const float* q_pooled, const float* k_pooled, int32_t* topk_idx,
+                              void* stream);
+
+/*
  * Inspection entry point for the same scoring: writes the full fp32
  * Score_i matrix scores [batch, heads, n_tiles, n_tiles] (row = query block)
  * and, if non-NULL, red [batch, heads, n_tiles] (Score_r).

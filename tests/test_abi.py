@@ -268,3 +268,21 @@ def test_no_device_is_an_error_not_a_fallback():
     assert lib.ssta_calibrate_mfma(16, 16, 4, 10, None) == NO_DEV
     with pytest.raises(m.SstaError):
         L._call("ssta_tile_pool", ctypes.byref(g), 16, 32, 0, None, None)
+
+
+def test_noalloc_scratch_limit():
+    """The entry point without a workspace scores at least one head per pass
+    of its 64 MiB scratch: a 4,096-block head (64 MiB of Score_i alone) is a
+    shape error; a 3,600-block head fits, and the call gets as far as the
+    output pointer's check (a misaligned one here, so nothing runs)."""
+    lib = m.load()
+    p = m.make_params(topk=2)
+    big = m.make_geom(1, 1, 32, 128, 128)                # 16 x 16 x 16 = 4096 blocks
+    fits = m.make_geom(1, 16, 60, 48, 80, tile=(4, 4, 4))  # 15 x 12 x 20 = 3600 blocks
+    assert big.n_tiles == 4096 and fits.n_tiles == 3600
+    assert lib.ssta_score_select_noalloc(ctypes.byref(big), ctypes.byref(p), 16, 16, 16,
+                                         None) == SHAPE
+    assert lib.ssta_score_select_noalloc(ctypes.byref(fits), ctypes.byref(p), 16, 16, 8,
+                                         None) == ALIGN
+    assert lib.ssta_score_select_noalloc(ctypes.byref(fits), ctypes.byref(p), None, 16, 16,
+                                         None) == ARG

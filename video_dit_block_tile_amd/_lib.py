@@ -77,6 +77,7 @@ SIGNATURES = {
     "ssta_max_kept": (_i32, [_G, _P]),
     "ssta_workspace_bytes": (_i64, [_G, _P]),
     "ssta_score_select": (ctypes.c_int, [_G, _P, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "ssta_score_select_noalloc": (ctypes.c_int, [_G, _P, _vp, _vp, _vp, _vp]),
     "ssta_scores": (ctypes.c_int, [_G, _P, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "ssta_build_mask": (ctypes.c_int, [_G, _P, _vp, _vp, _vp, _vp, _vp]),
     "ssta_attention_fwd": (ctypes.c_int, [_G, _P, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
@@ -273,6 +274,17 @@ def ssta_score_select(g: SstaGeom, p: SstaParams, q_pooled, k_pooled, topk_idx, 
     ws_bytes = _workspace(workspace)
     _call("ssta_score_select", ctypes.byref(g), ctypes.byref(p), _ptr(q_pooled), _ptr(k_pooled),
           _ptr(topk_idx), _ptr(workspace), ws_bytes, _stream(stream))
+
+
+def ssta_score_select_noalloc(g: SstaGeom, p: SstaParams, q_pooled, k_pooled, topk_idx,
+                              stream=None):
+    pshape = (g.batch, g.heads, g.n_tiles, g.head_dim)
+    _expect("q_pooled", q_pooled, pshape, torch.float32)
+    _expect("k_pooled", k_pooled, pshape, torch.float32)
+    _expect("topk_idx", topk_idx, (g.batch, g.heads, g.n_tiles, ssta_topk_width(g, p)),
+            torch.int32)
+    _call("ssta_score_select_noalloc", ctypes.byref(g), ctypes.byref(p), _ptr(q_pooled),
+          _ptr(k_pooled), _ptr(topk_idx), _stream(stream))
 
 
 def ssta_scores(g: SstaGeom, p: SstaParams, q_pooled, k_pooled, scores, red, workspace,

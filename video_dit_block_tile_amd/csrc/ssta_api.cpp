@@ -132,6 +132,13 @@ WsLayout ws_layout(const Geo& g) {
   return w;
 }
 
+// Scratch of ssta_score_select_noalloc: one array per GPU, held until the
+// process ends.  Its name is a host-side stand-in; host code uses only the
+// device address hipGetSymbolAddress returns for the current device.
+constexpr int64_t kNoAllocScratchBytes = int64_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+std::atomic<uint8_t*> g_scratch_ptr[kMaxDevices];
+
 int check_device() {
   int count = 0;
   if (hipGetDeviceCount(&count) != hipSuccess || count < 1) {
@@ -170,6 +177,26 @@ int hip_status(hipError_t e) {
   } while (0)
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device (with the device current) and kept.
+int scratch_ptr(uint8_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return SSTA_ERR_NO_DEVICE;
+  }
+  uint8_t* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    void* addr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || addr == nullptr) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol);
+    ptr = static_cast<uint8_t*>(addr);
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return SSTA_OK;
+}
 
 int score_common(const ssta_geom_t* g, const ssta_params_t* p, const float* qp,
                  const float* kp, void* ws, size_t ws_bytes, Geo* geo, WsLayout* lay) {
@@ -296,6 +323,44 @@ int ssta_score_select(const ssta_geom_t* g, const ssta_params_t* p, const float*
   if (width == 0) return SSTA_OK;   // nothing to select: topk_idx has no columns
   return score_select_into(geo, p, q_pooled, k_pooled, topk_idx,
                            static_cast<uint8_t*>(workspace), lay, width, as_stream(stream));
+}
+
+int ssta_score_select_noalloc(const ssta_geom_t* g, const ssta_params_t* p,
+                              const float* q_pooled, const float* k_pooled, int32_t* topk_idx,
+                              void* stream) {
+  Geo geo;
+  SSTA_TRY(check_geom(g, &geo));
+  SSTA_TRY(check_params(p));
+  SSTA_TRY(check_ptr(q_pooled, false));
+  SSTA_TRY(check_ptr(k_pooled, false));
+  if (geo.n_tiles > ssta::kMaxTopkTiles) return SSTA_ERR_SHAPE;
+  if (geo.bh > ssta::kMaxScoreHeads) return SSTA_ERR_SHAPE;
+  // heads per pass: as many as the scratch holds; one head must fit
+  Geo part = geo;
+  part.bh = 1;
+  if (ws_layout(part).total > kNoAllocScratchBytes) return SSTA_ERR_SHAPE;
+  int64_t hc = kNoAllocScratchBytes / ws_layout(part).total;
+  hc = hc < geo.bh ? hc : geo.bh;
+  for (;;) {
+    part.bh = hc;
+    if (hc == 1 || ws_layout(part).total <= kNoAllocScratchBytes) break;
+    --hc;
+  }
+  const int32_t width = topk_width(geo, p);
+  SSTA_TRY(check_ptr(topk_idx, width == 0));
+  SSTA_TRY(check_device());
+  if (width == 0) return SSTA_OK;
+  uint8_t* ws = nullptr;
+  SSTA_TRY(scratch_ptr(&ws));
+  const int64_t n = geo.n_tiles;
+  for (int64_t h0 = 0; h0 < geo.bh; h0 += hc) {
+    part.bh = geo.bh - h0 < hc ? geo.bh - h0 : hc;
+    const WsLayout lay = ws_layout(part);
+    SSTA_TRY(score_select_into(part, p, q_pooled + h0 * n * ssta::kHeadDim,
+                               k_pooled + h0 * n * ssta::kHeadDim, topk_idx + h0 * n * width, ws,
+                               lay, width, as_stream(stream)));
+  }
+  return SSTA_OK;
 }
 
 int ssta_scores(const ssta_geom_t* g, const ssta_params_t* p, const float* q_pooled,
