@@ -297,3 +297,48 @@ def test_similarity_only_variant(name):
     assert np.array_equal(plan.kv_cnt.cpu().numpy(), sel["kv_cnt"])
     rows = sample_rows(wl, 24, seed=4)
     _check_attention(wl, q, k, v, sel, plan, rows)
+
+
+@pytest.mark.parametrize("text_len", [0, 70])
+def test_t64_half_units_without_keys(text_len):
+    """With 64-token blocks two waves share each query group, one 32-key half
+    of every unit each.  Here every query block keeps only blocks of the last
+    block row in t, which holds 2 of its 4 frames: the second half of each
+    such unit has no key at all, so one wave of each pair sees no real key in
+    its first unit (or, without text, in any); every third query block keeps
+    nothing.  O and LSE of every row against the oracle."""
+    import video_dit_block_tile_amd as m
+    wl = si.ALL["t64-partial"].with_(text_len=text_len)
+    q, k, v = si.make_qkv(wl)
+    nt, ny, nx = wl.tile_grid
+    n = wl.n_tiles
+    last = np.arange((nt - 1) * ny * nx, n, dtype=np.int32)
+    assert len(last) >= 3
+    for j in last:     # positions 32..63 of these blocks lie past the clip
+        assert all(oracle.tile_to_token(wl, int(j), r) < 0 for r in range(32, 64))
+    kv_idx = np.full((wl.batch, wl.heads, n, len(last)), -1, np.int32)
+    kv_cnt = np.zeros((wl.batch, wl.heads, n), np.int32)
+    for bh in range(wl.batch * wl.heads):
+        b, h = divmod(bh, wl.heads)
+        for i in range(n):
+            if i % 3 == 2:
+                continue
+            keep = np.sort(np.roll(last, i + bh)[: 1 + (i + bh) % len(last)])
+            kv_idx[b, h, i, :len(keep)] = keep
+            kv_cnt[b, h, i] = len(keep)
+    g, p = geom_of(wl), params_of(wl)
+    o = torch.zeros(wl.batch, wl.heads, wl.seq_len, 128, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(wl.batch, wl.heads, wl.n_rows, wl.tile_tokens, dtype=torch.float32,
+                      device="cuda")
+    m.ssta_attention_fwd_tokens(g, p, to_dev(q), to_dev(k), to_dev(v),
+                                torch.from_numpy(kv_idx).cuda(), torch.from_numpy(kv_cnt).cuda(),
+                                o, lse)
+    torch.cuda.synchronize()
+    rows = np.arange(wl.batch * wl.heads * wl.n_rows)
+    o_ref, lse_ref = oracle.attention(wl, q, k, v, kv_idx, kv_cnt, rows)
+    mx, mean = compare_o(o_rows(wl, o, rows), o_ref)
+    ratio = check_lse(wl, q, k, rows, lse.cpu().numpy().reshape(-1, wl.tile_tokens)[rows],
+                      lse_ref)
+    print("[t64 half units, text %d] O max-abs %.3e mean-abs %.3e, LSE error / bound %.3f"
+          % (text_len, mx, mean, ratio), flush=True)
+    assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS, (mx, mean)

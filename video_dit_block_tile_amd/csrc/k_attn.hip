@@ -63,11 +63,19 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Blocks hold kR = 128 or 64 tokens; a workgroup has kR/32 waves (32 queries
-// each) and takes a key block in kR/64 units of 64 keys.
+// Blocks hold kR = 128 or 64 tokens; a workgroup has 4 waves and takes a key
+// block in kR/64 units of 64 keys.  128-token blocks: each wave owns 32
+// queries and every key of a unit.  64-token blocks (kSplit): the block's 64
+// queries form two groups of 32, and each group is shared by two waves that
+// take one 32-key half of every unit each, with their own running max and
+// sums; the pair merges its two partial results at the end.  Both shapes
+// thus run 4-wave workgroups, two per CU (64 KB of LDS each): two waves per
+// SIMD.
 template <int kR>
 struct Blk {
-  static constexpr int kWaves = kR / 32;
+  static constexpr int kWaves = 4;
+  static constexpr bool kSplit = kR == 64;
+  static constexpr int kTiles = kSplit ? 1 : 2;       // 32-key tiles of a unit per wave
   static constexpr int kLoads = 16 / kWaves;          // 1 KB loads per wave per 16 KB slot
   static constexpr int kUnits = kR / 64;              // 64-key units per block
   static constexpr int kBytes = kR * kHeadDim * 2;    // one block of one tensor
@@ -268,11 +276,10 @@ __device__ __forceinline__ void dma_v(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, i
 // kGen: the instance for ragged grids and joint text (masked partial blocks,
 // text blocks always kept, text query blocks dense); grids the block size
 // divides, without text, run the other instance.
-// kR: tokens per block (128: 4 waves; 64: 2 waves, one unit per key block).
-// 64-token blocks: 2-wave workgroups hold 64 KB of LDS each, so a SIMD runs one
-// wave of them.
+// kR: tokens per block (128: two units per key block; 64: one unit, its two
+// halves taken by two waves per query group, see Blk).
 template <bool kTok, bool kGen, int kR>
-__global__ __launch_bounds__(kR * 2) __attribute__((amdgpu_waves_per_eu(kR == 128 ? 2 : 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
   // K slots at 0 and 16 KB, V (or V^T) slots at 32 and 48 KB.
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kSlotBytes];
@@ -290,13 +297,21 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   constexpr int64_t kTileElems = kR * kHeadDim;
   constexpr int kUnits = Blk<kR>::kUnits;
+  constexpr bool kSplit = Blk<kR>::kSplit;
+  constexpr int kT = Blk<kR>::kTiles;
+  // query group (32 queries) and, with split units, the 32-key half of each
+  // unit this wave takes
+  const int qg = kSplit ? (wave & 1) : wave;
+  const int kh = kSplit ? (wave >> 1) : 0;
+  // unit tile tt of this wave is the unit's keys 32 * tile(tt) .. + 31
+  auto tile = [&](int tt) { return kSplit ? kh : tt; };
 
   // qb: this lane's query row is qb + (kTok ? 0 : qrow * 128).  A query
   // position its block lacks (ragged edge, past the text) reads the block's
   // first token instead; its output is not written.
-  const int qrow = wave * 32 + l32;
+  const int qrow = qg * 32 + l32;
   const bool qvalid =
-      (unit_valid<kGen, kR>(g, qi, wave >> 1, lane) >> (32 * (wave & 1) + l32)) & 1u;
+      (unit_valid<kGen, kR>(g, qi, qg >> 1, lane) >> (32 * (qg & 1) + l32)) & 1u;
   // token of the query within its head (clip tokens first, then the text)
   const int64_t qtok =
       qtext ? g.N + (qi - g.n_tiles) * kR + (qvalid ? qrow : 0)
@@ -398,52 +413,56 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
     const uint8_t* sK = smem + slot * kSlotBytes;
     const uint8_t* sV = smem + (2 + slot) * kSlotBytes;
 
-    // S^T: 16 products in the order (st, t); their K operands are read
+    // S^T: 8 * kT products in the order (st, tt); their K operands are read
     // kKAhead products ahead so the LDS latency overlaps the matrix cores.
     // The A operand row of lane l32 is key kperm(l32), so output register r
-    // of lane (l32, hl) of s[t] holds query l32 and key
-    // 32*t + 16*(r/8) + 8*hl + r%8: each group of 8 registers is 8
+    // of lane (l32, hl) of s[tt] holds query l32 and key
+    // 32*tile(tt) + 16*(r/8) + 8*hl + r%8: each group of 8 registers is 8
     // consecutive keys.
     constexpr int kKAhead = 8;
+    constexpr int kSProducts = 8 * kT;
     __builtin_amdgcn_s_setprio(1);
-    f32x16 s[2];
+    f32x16 s[kT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < kT; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
     bf16x8 kr[kKAhead];
 #pragma unroll
     for (int i = 0; i < kKAhead; ++i)
-      kr[i] = *reinterpret_cast<const bf16x8*>(sK + swz_k(32 * (i & 1) + kperm, 2 * (i >> 1) + hl));
+      kr[i] = *reinterpret_cast<const bf16x8*>(
+          sK + swz_k(32 * tile(i % kT) + kperm, 2 * (i / kT) + hl));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int st = i >> 1, t = i & 1;
-      s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i % kKAhead], qf[st], s[t], 0, 0, 0);
+    for (int i = 0; i < kSProducts; ++i) {
+      const int st = i / kT, tt = i % kT;
+      s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i % kKAhead], qf[st], s[tt], 0, 0, 0);
       const int n = i + kKAhead;
-      if (n < 16)
-        kr[i % kKAhead] =
-            *reinterpret_cast<const bf16x8*>(sK + swz_k(32 * (n & 1) + kperm, 2 * (n >> 1) + hl));
+      if (n < kSProducts)
+        kr[i % kKAhead] = *reinterpret_cast<const bf16x8*>(
+            sK + swz_k(32 * tile(n % kT) + kperm, 2 * (n / kT) + hl));
       __builtin_amdgcn_sched_barrier(0);
     }
     // Keys an edge block of a ragged grid lacks get a score far below any
     // real one, so their probabilities vanish (position 0 always exists, so
-    // a row's first unit has a real key).
+    // a row's first unit has a real key; a wave's second half of a unit may
+    // have none, which the softmax below handles).
     if (kGen && valid != ~0ull) {
       const uint64_t vl = valid >> (8 * hl);
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < kT; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (!((vl >> (32 * t + 16 * (r >> 3) + (r & 7))) & 1u)) s[t][r] = -1.0e30f;
+          if (!((vl >> (32 * tile(t) + 16 * (r >> 3) + (r & 7))) & 1u)) s[t][r] = -1.0e30f;
     }
 
-    // V operands of the first kVAhead P.V products (order (t, ks, db)),
+    // V operands of the first kVAhead P.V products (order (tt, ks, db)),
     // requested before the softmax so they arrive while it runs.
     constexpr int kVAhead = 8;
+    constexpr int kVProducts = 8 * kT;
     bf16x8 vr[kVAhead];
 #pragma unroll
     for (int i = 0; i < kVAhead; ++i)
-      vr[i] = v_operand<kTok>(sV, i >> 3, (i >> 2) & 1, i & 3, l32, hl, vofs);
+      vr[i] = v_operand<kTok>(sV, tile(i >> 3), (i >> 2) & 1, i & 3, l32, hl, vofs);
 
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(kFenceKeepDs);
@@ -457,12 +476,12 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
     // P^T as B operand of k-step (t, ks): registers 8*ks .. 8*ks+7, which are
     // keys 32*t + 16*ks + 8*hl + (0..7) of the unit.  The denominator sums the
     // bf16-rounded probabilities (the weights the P.V product uses) with v_dot2.
-    bf16x8 pf[2][2];
+    bf16x8 pf[kT][2];
     float lu;
     auto probabilities = [&]() {
       float l0 = 0.0f, l1 = 0.0f;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < kT; ++t)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -479,14 +498,19 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
     probabilities();
     if (__any(!(lu <= kMaxUnitSum))) {
       float x0 = max3f(s[0][0], s[0][1], s[0][2]);
-      float x1 = max3f(s[1][0], s[1][1], s[1][2]);
+      float x1 = max3f(s[kT - 1][0], s[kT - 1][1], s[kT - 1][2]);
 #pragma unroll
       for (int r = 3; r < 15; r += 2) {
         x0 = max3f(x0, s[0][r], s[0][r + 1]);
-        x1 = max3f(x1, s[1][r], s[1][r + 1]);
+        x1 = max3f(x1, s[kT - 1][r], s[kT - 1][r + 1]);
       }
-      const float mx = pair_max(max3f(max3f(x0, x1, s[0][15]), s[1][15], -INFINITY)) * c;
-      const float m_new = fmaxf(m, mx);
+      const float mx = pair_max(max3f(max3f(x0, x1, s[0][15]), s[kT - 1][15], -INFINITY)) * c;
+      float m_new = fmaxf(m, mx);
+      // With split units a wave's half of a unit can lack every key (scores
+      // -1e30): a floor halfway to that score keeps such keys' probabilities
+      // at 0 before the wave has seen a real key.  Any real score lies above
+      // it, so the floor never changes a real running max.
+      if (kSplit) m_new = fmaxf(m_new, -5.0e29f * c);
       const float alpha = __builtin_amdgcn_exp2f(m - m_new);
       l *= alpha;
 #pragma unroll
@@ -502,12 +526,12 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
     // O^T += V^T P^T in the order (t, ks, db); A operand: channel d of the
     // same 8 consecutive keys 32t + 16ks + 8hl + (0..7) (see v_operand).
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = i >> 3, ks = (i >> 2) & 1, db = i & 3;
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[i % kVAhead], pf[t][ks], o[db], 0, 0, 0);
+    for (int i = 0; i < kVProducts; ++i) {
+      const int tt = i >> 3, ks = (i >> 2) & 1, db = i & 3;
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[i % kVAhead], pf[tt][ks], o[db], 0, 0, 0);
       const int n = i + kVAhead;
-      if (n < 16)
-        vr[i % kVAhead] = v_operand<kTok>(sV, n >> 3, (n >> 2) & 1, n & 3, l32, hl, vofs);
+      if (n < kVProducts)
+        vr[i % kVAhead] = v_operand<kTok>(sV, tile(n >> 3), (n >> 2) & 1, n & 3, l32, hl, vofs);
       __builtin_amdgcn_sched_barrier(kFenceKeepDs);
     }
     __builtin_amdgcn_s_setprio(0);
@@ -516,7 +540,37 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
   // Epilogue: lane holds query qrow, channels 32*db + 8*g4 + 4*hl + (0..3).
   // A query position its block lacks has no output row (token order) or a
   // zero row (tile order), and LSE -inf.
-  const float lt = pair_sum(l);
+  float lt = pair_sum(l);
+  if (kSplit) {
+    // The second wave of each query group hands its running max, sum and O
+    // to the first through LDS (the ring is free: every wave is past its
+    // last unit and no load is in flight); the first rescales both to the
+    // larger max and adds them.
+    float* xs = reinterpret_cast<float*>(smem) + qg * (66 * 64);
+    __syncthreads();
+    if (kh == 1) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xs[(16 * db + r) * 64 + lane] = o[db][r];
+      xs[64 * 64 + lane] = m;
+      xs[65 * 64 + lane] = lt;
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m2 = xs[64 * 64 + lane], lt2 = xs[65 * 64 + lane];
+    const float mt = fmaxf(m, m2);
+    // a side without keys has m = -inf and contributes nothing; if both
+    // have none, lt stays 0 (the row's output is 0, its LSE -inf)
+    const float a1 = mt == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mt);
+    const float a2 = mt == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m2 - mt);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a1 + xs[(16 * db + r) * 64 + lane] * a2;
+    lt = lt * a1 + lt2 * a2;
+    m = mt;
+  }
   const float inv = (lt > 0.0f && qvalid) ? 1.0f / lt : 0.0f;
   uint16_t* ob = static_cast<uint16_t*>(a.o_t) + row * kTileElems + qrow * kHeadDim;
   if (kTok) ob = static_cast<uint16_t*>(a.o_t) + (bh * g.S + qtok) * kHeadDim;
@@ -549,7 +603,7 @@ hipError_t launch_attention(const Geo& g, const AttnArgs& a, hipStream_t s) {
   const bool gen = g.ragged || g.L > 0;
   const dim3 grid((unsigned)blocks);
   if (g.R == kSmallTile) {
-    const dim3 block(2 * kSmallTile);
+    const dim3 block(256);
     if (a.token_io && gen)
       hipLaunchKernelGGL((k_attn_fwd<true, true, kSmallTile>), grid, block, 0, s, g, a, ag);
     else if (a.token_io)
@@ -559,7 +613,7 @@ hipError_t launch_attention(const Geo& g, const AttnArgs& a, hipStream_t s) {
     else
       hipLaunchKernelGGL((k_attn_fwd<false, false, kSmallTile>), grid, block, 0, s, g, a, ag);
   } else {
-    const dim3 block(2 * kTileTokens);
+    const dim3 block(256);
     if (a.token_io && gen)
       hipLaunchKernelGGL((k_attn_fwd<true, true, kTileTokens>), grid, block, 0, s, g, a, ag);
     else if (a.token_io)
