@@ -20,19 +20,19 @@
 //                    32 queries held in registers), dS^T in registers, then
 //                    dQ^T += K^T dS^T with K^T read transposed from the K rows;
 //   k_attn_bwd_dkdv  per key block, over the query blocks that keep it, in
-//                    units of 32 queries: S = Q K^T and dP = dO V^T (the
-//                    wave's 32 keys and their values held in registers), P and
-//                    dS in registers, then dV^T += dO^T P and dK^T += Q^T dS.
+//                    units of 32 queries, two waves per group of 32 keys: a V
+//                    wave forms S = Q K^T (the keys held in registers), P and
+//                    dV^T += dO^T P, and hands P to a K wave, which forms
+//                    dP = dO V^T (the values held in registers),
+//                    dS = P (dP - D) and dK^T += Q^T dS one unit later.
 // The transposed operands (K^T, dO^T, Q^T: channel d of 8 consecutive rows)
 // come from the same token rows in LDS through the transposing reads
 // (ds_read_b64_tr_b16), so nothing is copied to a dim-major layout first.
-// k_attn_bwd_dq keeps two waves per SIMD; k_attn_bwd_dkdv's two accumulators
-// need more than 256 VGPRs, so it runs one, and software-pipelines its units
-// instead (P and dS of one unit on the vector ALU while the matrix cores
-// compute S and dP of the next).  Every streamed unit (token rows gathered
-// from token-major memory and the per-query (lse*log2 e, D) pairs) goes
-// straight into LDS with buffer_load_dwordx4 ... lds into a ring of slots
-// (two in k_attn_bwd_dq, three in k_attn_bwd_dkdv), as in the forward kernel.
+// Both kernels run two waves per SIMD.  Every streamed unit (token rows
+// gathered from token-major memory and the per-query (lse*log2 e, D) pairs)
+// goes straight into LDS with buffer_load_dwordx4 ... lds into a ring of
+// slots (two in k_attn_bwd_dq, three in k_attn_bwd_dkdv), as in the forward
+// kernel.
 //
 // Algorithmic work per kept (query block, key block) pair: five 128^3
 // products (S, dP, dQ, dK, dV) = 21.0 MFLOP; the two kernels compute S and dP
@@ -110,17 +110,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
                                            0x00020000);
 }
 
-// Per-lane source offsets of this wave's 1 KB loads of a row unit.
-template <int kR>
+// Per-lane source offsets of this wave's 1 KB loads of a row unit, for a
+// workgroup of kW waves that shares the unit's eight 1 KB loads.
+template <int kR, int kW = Blk<kR>::kWaves>
 struct UnitOffsets {
-  uint32_t rows[Blk<kR>::kLoads];
+  static constexpr int kLoads = 8 / kW;
+  uint32_t rows[kLoads];
 };
-template <int kR>
-__device__ __forceinline__ UnitOffsets<kR> unit_offsets(const Geo& g, int wave, int lane) {
-  UnitOffsets<kR> o;
+template <int kR, int kW = Blk<kR>::kWaves>
+__device__ __forceinline__ UnitOffsets<kR, kW> unit_offsets(const Geo& g, int wave, int lane) {
+  UnitOffsets<kR, kW> o;
 #pragma unroll
-  for (int mm = 0; mm < Blk<kR>::kLoads; ++mm) {
-    const int b = Blk<kR>::kLoads * wave + mm;     // 1 KB destination block 0..7
+  for (int mm = 0; mm < o.kLoads; ++mm) {
+    const int b = o.kLoads * wave + mm;            // 1 KB destination block 0..7
     const int row = 4 * b + (lane >> 4);           // token rows 4b .. 4b+3
     o.rows[mm] = in_block_offset(g, row) * 256 + (((lane & 15) ^ row_swz(row)) << 4);
   }
@@ -149,11 +151,12 @@ __device__ __forceinline__ uint32_t rows_valid(const Geo& g, uint32_t j, int p, 
 // block's first token instead, so every score it enters stays bounded by
 // the row's log-sum-exp; the kernels zero its dS or P, so it adds nothing.
 // A text block's rows are consecutive tokens.
-template <bool kGen, int kR>
+template <bool kGen, int kR, int kW = Blk<kR>::kWaves>
 __device__ __forceinline__ void dma_rows(uint8_t* dst, __amdgpu_buffer_rsrc_t rs, const Geo& g,
                                          uint32_t j, uint32_t clip_origin, int p, int wave,
-                                         int lane, uint32_t valid, const UnitOffsets<kR>& off) {
-  constexpr int kL = Blk<kR>::kLoads;
+                                         int lane, uint32_t valid,
+                                         const UnitOffsets<kR, kW>& off) {
+  constexpr int kL = UnitOffsets<kR, kW>::kLoads;
   const bool part = kGen && valid != ~0u;
   const bool text = kGen && j >= g.n_tiles;
   const uint32_t origin = text ? (uint32_t)(g.N + (j - g.n_tiles) * kR) : clip_origin;
@@ -348,19 +351,35 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, AttnGrid grid) {
 
 // ------------------------------------------------------------------ dK, dV
 
-// dV^T += dO^T P and dK^T += Q^T dS with dS = P (dP - D), from the same S and
-// dP.  The two accumulators and the K and V operands need more than 256
-// VGPRs, so the kernel runs one wave per SIMD.
+// dV^T += dO^T P and dK^T += Q^T dS with dS = P (dP - D), one workgroup per key
+// block, in units of 32 queries.  The block's keys form kR/32 groups of 32;
+// each group has two waves:
+//   a V wave: S = Q K^T (its keys' K rows held in registers), P, and
+//             dV^T += dO^T P; it hands P (fp32) to its partner through LDS;
+//   a K wave, one unit behind: dP = dO V^T (the keys' V rows in registers),
+//             dS = P (dP - D) from the partner's P, and dK^T += Q^T dS.
+// Each wave thus needs one accumulator and one operand block, so two waves
+// share a SIMD, and each does 16 of the 32 products of a unit.  Iteration u:
+// the V waves take unit u, the K waves unit u-1, and unit u+1 is loading:
+// three slots of Q rows, dO rows and the units' (lse*log2 e, D) pairs, plus
+// two P buffers.  The arithmetic (products, their order, the roundings) is
+// the same as one wave doing both, so the gradients are too.
+template <int kR>
+struct DkdvShape {
+  static constexpr int kGroups = kR / 32;             // 32-key groups per block
+  static constexpr int kWaves = 2 * kGroups;
+  static constexpr int kSlot = 2 * kUnitBytes + 256;  // Q rows | dO rows | 32 pairs
+  static constexpr int kPBuf = kGroups * 64 * 64;     // 16 fp32 per lane per group
+  static constexpr int kLds = 3 * kSlot + 2 * kPBuf;
+};
+
 template <bool kGen, int kR>
-__global__ __launch_bounds__(kR * 2) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(DkdvShape<kR>::kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void k_attn_bwd_dkdv(Geo g, BwdArgs a, AttnGrid grid) {
+  using Sh = DkdvShape<kR>;
   constexpr int kUnits = Blk<kR>::kUnits;
-  // slot: Q rows | dO rows | 32 (lse2, D) pairs; dO^T (dV) and Q^T (dK) are
-  // read transposed from the rows
-  constexpr int kSlot = 2 * kUnitBytes + 256;
-  // three slots: unit u (dV, dK), unit u+1 (S, dP) and unit u+2 (loading);
-  // LDS does not limit this kernel's occupancy (VGPRs do)
-  __shared__ __attribute__((aligned(16))) uint8_t smem[3 * kSlot];
+  constexpr int kSlot = Sh::kSlot;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Sh::kLds];
   // text key blocks (kept by every query block) first; then, with the kept
   // lists, each head's key blocks longest first (k_order_blocks), dealt
   // round-robin over the XCDs; under dense attention, XCD slices
@@ -376,26 +395,28 @@ void k_attn_bwd_dkdv(Geo g, BwdArgs a, AttnGrid grid) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool vwave = wv < Sh::kGroups;           // V wave (else K wave), uniform
+  const int grp = vwave ? wv : wv - Sh::kGroups;
   const int l32 = lane & 31, hl = lane >> 5;
   const int kperm = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
-  const int kr = 32 * wv + l32;                  // this lane's key within the block
+  const int kr = 32 * grp + l32;                 // this lane's key within the block
   const int64_t head = bh * g.S;
   // a key position its block lacks reads the block's first token and stores
   // nothing
-  const bool kvalid = (rows_valid<kGen, kR>(g, (uint32_t)kj, wv, lane) >> l32) & 1u;
+  const bool kvalid = (rows_valid<kGen, kR>(g, (uint32_t)kj, grp, lane) >> l32) & 1u;
   const int64_t ktok = head + row_token<kGen, kR>(g, kj, kr, kvalid);
 
-  // B operands: the wave's 32 keys (and their values for dP).
-  bf16x8 kf[8], vf[8];
-  load_row_operand(kf, static_cast<const uint16_t*>(a.k) + ktok * kHeadDim, hl);
-  load_row_operand(vf, static_cast<const uint16_t*>(a.v) + ktok * kHeadDim, hl);
+  // B operand of the wave's score product: its 32 keys (V wave: S = Q K^T)
+  // or their values (K wave: dP = dO V^T).
+  bf16x8 bop[8];
+  load_row_operand(bop, static_cast<const uint16_t*>(vwave ? a.k : a.v) + ktok * kHeadDim, hl);
   const float c = a.scale_log2;
 
-  f32x16 acc_v[4], acc_k[4];
+  f32x16 acc[4];   // dV^T (V wave) or dK^T (K wave)
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc_v[db][r] = acc_k[db][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
 
   // query blocks that keep this key block: its transposed list, then every
   // text query block; every query block keeps a text key block (and all
@@ -406,7 +427,7 @@ void k_attn_bwd_dkdv(Geo g, BwdArgs a, AttnGrid grid) {
   const int cnt = all_blocks ? (int)g.n_rows : listed + (kGen ? g.n_txt : 0);
   IdStream ids;
   ids.init(g, all_blocks ? nullptr : a.q_idx + klist * a.q_width, listed, all_blocks, lane);
-  const UnitOffsets<kR> off = unit_offsets<kR>(g, wv, lane);
+  const UnitOffsets<kR, Sh::kWaves> off = unit_offsets<kR, Sh::kWaves>(g, wv, lane);
   const int tb = row_t_base(lane);
   const int64_t tok_bytes = g.S * (int64_t)(kHeadDim * 2);
   const __amdgpu_buffer_rsrc_t qrs = rsrc(static_cast<const uint16_t*>(a.q) + head * kHeadDim,
@@ -424,130 +445,105 @@ void k_attn_bwd_dkdv(Geo g, BwdArgs a, AttnGrid grid) {
                            : ids.at(g, pos, lane, org);
     const int p = u % kUnits;
     const uint32_t valid = rows_valid<kGen, kR>(g, i, p, lane);
-    dma_rows<kGen, kR>(dst, qrs, g, i, org, p, wv, lane, valid, off);
-    dma_rows<kGen, kR>(dst + kUnitBytes, drs, g, i, org, p, wv, lane, valid, off);
+    dma_rows<kGen, kR, Sh::kWaves>(dst, qrs, g, i, org, p, wv, lane, valid, off);
+    dma_rows<kGen, kR, Sh::kWaves>(dst + kUnitBytes, drs, g, i, org, p, wv, lane, valid, off);
     if (wv == 0 && lane < 16)   // 32 (lse2, D) pairs = 256 B
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           lrs, (lds_u8*)(dst + 2 * kUnitBytes), 16, (uint32_t)lane * 16,
           (i * (uint32_t)kR + 32u * p) * 8u, 0, 0);
     return valid;
   };
-
-  // Software pipeline over units (one wave per SIMD, so the wave overlaps its
-  // own vector and matrix work): iteration u forms P and dS of unit u on the
-  // vector ALU while the matrix cores compute S and dP of unit u+1, then runs
-  // dV^T += dO^T P and dK^T += Q^T dS of unit u.  S and dP alternate between
-  // two register sets (units come in pairs: kUnits is even).
-  const int units = kUnits * cnt;
   auto slot = [&](int u) -> uint8_t* { return smem + (u % 3) * kSlot; };
-  constexpr int kAhead = 4;   // Q and dO operands requested ahead of their products
-  // S (queries x keys, lane = key l32): register r is query 16*(r/8) + 8*hl +
-  // r%8; dP likewise.  score_step(st) issues k-step st of both products.
-  auto score_step = [&](const uint8_t* sQ, const uint8_t* sD, int st, bf16x8* qa, bf16x8* da,
-                        f32x16& s, f32x16& dp) {
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st % kAhead], kf[st], s, 0, 0, 0);
-    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[st % kAhead], vf[st], dp, 0, 0, 0);
-    const int n = st + kAhead;
-    if (n < 8) {
-      qa[st % kAhead] = *reinterpret_cast<const bf16x8*>(sQ + swz_row(kperm, 2 * n + hl));
-      da[st % kAhead] = *reinterpret_cast<const bf16x8*>(sD + swz_row(kperm, 2 * n + hl));
-    }
+  // P of unit u for this group: 16 fp32 per lane, lane-major float4s
+  auto pbuf = [&](int u) -> f32x4* {
+    return reinterpret_cast<f32x4*>(smem + 3 * kSlot + (u & 1) * Sh::kPBuf + grp * 4096) + lane;
   };
-  auto score_begin = [&](const uint8_t* sQ, const uint8_t* sD, bf16x8* qa, bf16x8* da,
-                         f32x16& s, f32x16& dp) {
+  constexpr int kAhead = 4;   // row operands requested ahead of their products
+
+  const int units = kUnits * cnt;
+  uint32_t v_next = ~0u, v_cur = ~0u, v_prev = ~0u;   // which queries of units u+1, u, u-1 exist
+  if (units > 0) v_next = load_unit(0, slot(0));
+  // Iteration u: the V waves take unit u from slot sv, the K waves unit u-1
+  // from slot sk, and unit u+1 loads into slot sn (which held unit u-2).
+  for (int u = 0; u <= units; ++u) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's loads of unit u have landed
+    __syncthreads();                        // ... every wave's; units u-2 and P(u-2) are done
+    v_prev = v_cur;
+    v_cur = v_next;
+    if (u + 1 < units) v_next = load_unit(u + 1, slot(u + 1));   // into unit u-2's slot
+    const int w = vwave ? u : u - 1;         // the unit this wave takes
+    if (w < 0 || w >= units) continue;
+    const uint8_t* sQ = slot(w);
+    const uint8_t* sD = sQ + kUnitBytes;
+    // the wave's score product: S = Q K^T (V wave) or dP = dO V^T (K wave);
+    // register r of lane (l32, hl) is key l32 and query 16*(r/8) + 8*hl + r%8
+    const uint8_t* sA = vwave ? sQ : sD;
+    f32x16 sc;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.0f;
+    for (int r = 0; r < 16; ++r) sc[r] = 0.0f;
+    bf16x8 ra[kAhead];
 #pragma unroll
-    for (int st = 0; st < kAhead; ++st) {
-      qa[st] = *reinterpret_cast<const bf16x8*>(sQ + swz_row(kperm, 2 * st + hl));
-      da[st] = *reinterpret_cast<const bf16x8*>(sD + swz_row(kperm, 2 * st + hl));
+    for (int st = 0; st < kAhead; ++st)
+      ra[st] = *reinterpret_cast<const bf16x8*>(sA + swz_row(kperm, 2 * st + hl));
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[st % kAhead], bop[st], sc, 0, 0, 0);
+      const int n = st + kAhead;
+      if (n < 8) ra[st % kAhead] = *reinterpret_cast<const bf16x8*>(sA + swz_row(kperm, 2 * n + hl));
     }
-  };
-  // P (for dV) and dS (for dK) of score registers r and r+1 as B operands of
-  // k-step r/8 (queries 16*ks + 8*hl + e); zero for a query its block lacks
-  // (its rows hold the block's first token).
-  auto prob_pair = [&](int r, const f32x16& s, const f32x16& dp, const f32x4* lv,
-                       uint32_t valid, bf16x8* bp, bf16x8* bs) {
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int rr = r + x, ks = rr >> 3, e = rr & 7;
-      const f32x4 l2 = lv[4 * ks + (e >> 1)];   // (lse2, D) of queries e&~1, e|1
-      const float lse2 = l2[(e & 1) * 2];
-      float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], c, -lse2));
-      float ds = pr * (dp[rr] - l2[(e & 1) * 2 + 1]);
-      if (kGen && !((valid >> (16 * ks + 8 * hl + e)) & 1u)) pr = ds = 0.0f;
-      bp[ks][e] = (__bf16)pr;
-      bs[ks][e] = (__bf16)ds;
-    }
-  };
-  // iteration u: S, dP of unit u are in (s0, dp0); those of unit u+1 go to (s1, dp1)
-  auto iteration = [&](int u, uint32_t& v0, uint32_t& v1, f32x16& s0, f32x16& dp0,
-                       f32x16& s1, f32x16& dp1) {
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's loads of unit u+1 have landed
-    __syncthreads();                        // ... every wave's; unit u-1 is done
-    uint32_t v2 = ~0u;
-    if (u + 2 < units) v2 = load_unit(u + 2, slot(u + 2));   // into unit u-1's slot
-    const uint8_t* cur = slot(u);
-    const uint8_t* sQ = cur;
-    const uint8_t* sD = cur + kUnitBytes;
-    const f32x4* sL = reinterpret_cast<const f32x4*>(cur + 2 * kUnitBytes);
-    f32x4 lv[8];   // (lse2, D) of this lane's 16 queries: 8*ks + 8*hl .. in pairs
+    // (lse2, D) of the lane's 16 queries 16*ks + 8*hl + e, in pairs
+    const f32x4* sL = reinterpret_cast<const f32x4*>(sQ + 2 * kUnitBytes);
+    f32x4 lv[8];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int x = 0; x < 4; ++x) lv[4 * ks + x] = sL[(16 * ks + 8 * hl) / 2 + x];
-    bf16x8 bp[2], bs[2];
-    if (u + 1 < units) {
-      const uint8_t* nQ = slot(u + 1);
-      const uint8_t* nD = nQ + kUnitBytes;
-      bf16x8 qa[kAhead], da[kAhead];
-      score_begin(nQ, nD, qa, da, s1, dp1);
-      __builtin_amdgcn_sched_barrier(0);
+    const uint32_t valid = vwave ? v_cur : v_prev;
+    bf16x8 bo[2];   // P (V wave) or dS (K wave) as the B operand of k-step ks
+    if (vwave) {
+      // P = exp2(S c - lse2); zero for a query its block lacks (its rows hold
+      // the block's first token).  The fp32 values go to the K wave.
+      f32x4 pv[4];
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        score_step(nQ, nD, st, qa, da, s1, dp1);
-        prob_pair(2 * st, s0, dp0, lv, v0, bp, bs);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int r = 0; r < 16; ++r) {
+        const int ks = r >> 3, e = r & 7;
+        const f32x4 l2 = lv[4 * ks + (e >> 1)];
+        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c, -l2[(e & 1) * 2]));
+        if (kGen && !((valid >> (16 * ks + 8 * hl + e)) & 1u)) pr = 0.0f;
+        pv[r >> 2][r & 3] = pr;
+        bo[ks][e] = (__bf16)pr;
       }
-    } else {
+      f32x4* pb = pbuf(w);
 #pragma unroll
-      for (int st = 0; st < 8; ++st) prob_pair(2 * st, s0, dp0, lv, v0, bp, bs);
+      for (int x = 0; x < 4; ++x) pb[64 * x] = pv[x];
+    } else {
+      // dS = P (dP - D) with the V wave's P of this unit
+      const f32x4* pb = pbuf(w);
+      f32x4 pv[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) pv[x] = pb[64 * x];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ks = r >> 3, e = r & 7;
+        const f32x4 l2 = lv[4 * ks + (e >> 1)];
+        float ds = pv[r >> 2][r & 3] * (sc[r] - l2[(e & 1) * 2 + 1]);
+        if (kGen && !((valid >> (16 * ks + 8 * hl + e)) & 1u)) ds = 0.0f;
+        bo[ks][e] = (__bf16)ds;
+      }
     }
-    // dV^T += dO^T P and dK^T += Q^T dS: A operand row d, the same 8 queries,
-    // read transposed from the dO and Q rows of unit u.
+    // dV^T += dO^T P (V wave) or dK^T += Q^T dS (K wave): A operand row d of
+    // the same 8 queries, read transposed from the dO or Q rows.
+    const uint8_t* sT = vwave ? sD : sQ;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        acc_v[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_t_operand(sD, tb, ks, db),
-                                                            bp[ks], acc_v[db], 0, 0, 0);
-        acc_k[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_t_operand(sQ, tb, ks, db),
-                                                            bs[ks], acc_k[db], 0, 0, 0);
-      }
-    v0 = v1;
-    v1 = v2;
-  };
-
-  f32x16 sa, dpa, sb, dpb;
-  uint32_t v0 = ~0u, v1 = ~0u;   // which queries of units u and u+1 exist
-  if (units > 0) {
-    v0 = load_unit(0, slot(0));
-    if (units > 1) v1 = load_unit(1, slot(1));
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
-    bf16x8 qa[kAhead], da[kAhead];
-    score_begin(slot(0), slot(0) + kUnitBytes, qa, da, sa, dpa);
-#pragma unroll
-    for (int st = 0; st < 8; ++st) score_step(slot(0), slot(0) + kUnitBytes, st, qa, da, sa, dpa);
+      for (int db = 0; db < 4; ++db)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_t_operand(sT, tb, ks, db), bo[ks],
+                                                          acc[db], 0, 0, 0);
   }
-  for (int u = 0; u < units; u += 2) {
-    iteration(u, v0, v1, sa, dpa, sb, dpb);
-    iteration(u + 1, v0, v1, sb, dpb, sa, dpa);
-  }
-  if (kvalid) {
-    store_row(static_cast<uint16_t*>(a.dv) + ktok * kHeadDim, acc_v, 1.0f, hl);
-    store_row(static_cast<uint16_t*>(a.dk) + ktok * kHeadDim, acc_k, a.scale, hl);
-  }
+  if (kvalid)
+    store_row(static_cast<uint16_t*>(vwave ? a.dv : a.dk) + ktok * kHeadDim, acc,
+              vwave ? 1.0f : a.scale, hl);
 }
 
 // ------------------------------------------------------------------ helpers
@@ -739,7 +735,8 @@ hipError_t launch_bwd_kernels(const Geo& g, const BwdArgs& a, const AttnGrid& ag
                               hipStream_t s) {
   const dim3 grid((unsigned)ag.blocks), block(2 * kR);
   hipLaunchKernelGGL((k_attn_bwd_dq<kGen, kR>), grid, block, 0, s, g, a, ag);
-  hipLaunchKernelGGL((k_attn_bwd_dkdv<kGen, kR>), grid, block, 0, s, g, a, ag);
+  hipLaunchKernelGGL((k_attn_bwd_dkdv<kGen, kR>), grid, dim3(DkdvShape<kR>::kWaves * 64), 0, s,
+                     g, a, ag);
   return hipGetLastError();
 }
 
