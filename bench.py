@@ -280,10 +280,11 @@ def variant_runs(torch, m, si, steps):
 
 
 def per_config_runs(torch, m, si, steps, dense_steps):
-    """The five workload shapes in turn (inputs generated, timed, freed): step
-    and attention time from HIP events on the launch stream, attention
-    TFLOP/s on kept blocks, kept fraction, and the same pipeline with every
-    block kept (dense) on the same inputs for the speedup."""
+    """The five workload shapes in turn (inputs generated, timed, freed): step,
+    phase and attention times from HIP events on the launch stream (medians),
+    the block means' HBM rate, the scoring's fp32 rate, attention TFLOP/s on
+    kept blocks, kept fraction, and the same pipeline with every block kept
+    (dense) on the same inputs for the speedup."""
     import numpy as np
     out = {}
     for name, wl in si.CONFIGS.items():
@@ -300,28 +301,46 @@ def per_config_runs(torch, m, si, steps, dense_steps):
             for _ in range(2):
                 plan.run(qd, kd, vd)
             torch.cuda.synchronize()
-            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_steps)]
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_steps)]
             for e in ev:
                 e[0].record()
                 plan.tile_pool(qd, kd, vd)
-                if mode == "sparse":
-                    plan.select()
                 e[1].record()
-                plan.attend()
+                if mode == "sparse":
+                    plan.score_select()
                 e[2].record()
+                if mode == "sparse":
+                    plan.build_mask()
+                e[3].record()
+                plan.attend()
+                e[4].record()
             torch.cuda.synchronize()
-            res[mode] = (float(np.median([e[0].elapsed_time(e[2]) for e in ev])),
-                         float(np.median([e[1].elapsed_time(e[2]) for e in ev])),
+            med = lambda a, b: float(np.median([e[a].elapsed_time(e[b]) for e in ev]))
+            res[mode] = (med(0, 4), med(3, 4),
                          block_pairs(wl, plan) if mode == "sparse" else
-                         wl.batch * wl.heads * wl.n_rows * wl.n_rows)
+                         wl.batch * wl.heads * wl.n_rows * wl.n_rows,
+                         (med(0, 1), med(1, 2), med(2, 3)), plan.width)
             del plan
-        step, attn, pairs = res["sparse"]
-        dstep, dattn, dpairs = res["dense"]
+        step, attn, pairs, (t_pool, t_score, t_mask), width = res["sparse"]
+        dstep, dattn, dpairs, _, _ = res["dense"]
         flop = pairs * 4 * wl.tile_tokens ** 2 * 128
         tf = flop / (attn * 1e-3) / 1e12
+        bh = wl.batch * wl.heads
+        # block means: read Q and K, write both fp32 mean arrays
+        pool_bytes = 2 * bh * wl.seq_len * 128 * 2 + 2 * bh * wl.n_tiles * 128 * 4
+        pool_gbs = pool_bytes / (t_pool * 1e-3) / 1e9
+        score_flop = 2 * bh * wl.n_tiles ** 2 * 128 * 2 if width > 0 else 0
+        score_tf = score_flop / (t_score * 1e-3) / 1e12 if t_score > 0 else 0.0
         out[name] = {"grid": [wl.T, wl.H, wl.W], "n_tiles": wl.n_tiles, "topk": wl.topk,
                      "kept_pairs": pairs, "kept_fraction": round(pairs / dpairs, 5),
-                     "step_ms": round(step, 4), "attention_ms": round(attn, 4),
+                     "step_ms": round(step, 4),
+                     "tile_pool_ms": round(t_pool, 4), "tile_pool_gbs": round(pool_gbs, 1),
+                     "tile_pool_pct_hbm": round(100 * pool_gbs / PEAK_HBM_GBS, 1),
+                     "score_select_ms": round(t_score, 4),
+                     "score_valu_tflops": round(score_tf, 2),
+                     "score_pct_fp32_unpacked": round(100 * score_tf / PEAK_FP32_UNPACKED_TFLOPS, 1),
+                     "build_mask_ms": round(t_mask, 4),
+                     "attention_ms": round(attn, 4),
                      "attention_tflops": round(tf, 2),
                      "pct_bf16_peak_attention": round(100 * tf / PEAK_BF16_TFLOPS, 2),
                      "dense_step_ms": round(dstep, 3), "dense_attention_ms": round(dattn, 3),

@@ -174,3 +174,31 @@ def test_backward_full_size_sampled(name):
     if len(krows):
         _check("dk", _rows_of(wl, dk, krows), rk, bk, mk)
         _check("dv", _rows_of(wl, dv, krows), rv, bv, mv)
+
+
+@pytest.mark.parametrize("name", ["ragged", "joint-partial", "t64-partial", "720p-5s"])
+def test_same_head_in_two_launch_configurations(name):
+    """Every step is per (batch, head), so a head's results must not depend
+    on the launch it runs in.  Each head of a multi-head batch is run again
+    alone, as a one-head batch: the grids differ (other workgroup counts,
+    XCD slices, and dK/dV order of key blocks), the block means, ids, kept
+    lists, O, LSE, dq, dk and dv of that head must be bit-identical."""
+    import video_dit_block_tile_amd as m
+    wl = si.ALL[name]
+    if name == "720p-5s":
+        wl = wl.with_(heads=2)
+    q, k, v = si.make_qkv(wl)
+    do = si.generate(wl, 3)
+    print("[%s] %d heads" % (name, wl.batch * wl.heads), flush=True)
+    plan, dq, dk, dv = _run(wl, q, k, v, do)
+    one = wl.with_(batch=1, heads=1)
+    for bh in range(wl.batch * wl.heads):
+        b, h = divmod(bh, wl.heads)
+        pick = lambda x: np.ascontiguousarray(x[b:b + 1, h:h + 1])
+        p1, dq1, dk1, dv1 = _run(one, pick(q), pick(k), pick(v), pick(do))
+        for label, x_all, x_one in (("topk", plan.topk_idx, p1.topk_idx),
+                                    ("kv_idx", plan.kv_idx, p1.kv_idx),
+                                    ("kv_cnt", plan.kv_cnt, p1.kv_cnt),
+                                    ("o", plan.o, p1.o), ("lse", plan.lse, p1.lse),
+                                    ("dq", dq, dq1), ("dk", dk, dk1), ("dv", dv, dv1)):
+            assert torch.equal(x_all[b:b + 1, h:h + 1], x_one), (label, b, h)
