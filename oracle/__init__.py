@@ -36,6 +36,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssta_oracle.c")
 _LIB = os.path.join(_HERE, "libssta_oracle.so")
+# A prebuilt library (e.g. an instrumented build for sanitizer runs) named by
+# SSTA_ORACLE_LIB is loaded instead, and build() leaves it alone.
+_PREBUILT = os.environ.get("SSTA_ORACLE_LIB")
 _lib = None
 
 COMBINE_AND = 1 << 0
@@ -50,6 +53,8 @@ DEFAULT_BETA = np.float32(1.0 - 0.9)
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc into ``libssta_oracle.so`` next to its source."""
     global _lib
+    if _PREBUILT:
+        return _PREBUILT
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
@@ -78,9 +83,12 @@ def _p(a: np.ndarray):
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=False)
-        lib = ctypes.CDLL(_LIB)
+        if _PREBUILT:
+            lib = ctypes.CDLL(_PREBUILT)
+        else:
+            if not os.path.exists(_LIB):
+                build(force=False)
+            lib = ctypes.CDLL(_LIB)
         G = ctypes.POINTER(_Geom)
         vp, i32, i64, f32, f64, u32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                        ctypes.c_float, ctypes.c_double, ctypes.c_uint32)

@@ -27,12 +27,17 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "philox_gen.c")
 _LIB = os.path.join(_HERE, "libsynth.so")
+# A prebuilt library (e.g. an instrumented build for sanitizer runs) named by
+# SSTA_SYNTH_LIB is loaded instead, and build() leaves it alone.
+_PREBUILT = os.environ.get("SSTA_SYNTH_LIB")
 _lib = None
 
 
 def build(force: bool = True) -> str:
     """Compile the generator with gcc into ``libsynth.so`` (next to the source)."""
     global _lib
+    if _PREBUILT:
+        return _PREBUILT
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
@@ -46,9 +51,12 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=False)
-        lib = ctypes.CDLL(_LIB)
+        if _PREBUILT:
+            lib = ctypes.CDLL(_PREBUILT)
+        else:
+            if not os.path.exists(_LIB):
+                build(force=False)
+            lib = ctypes.CDLL(_LIB)
         lib.synth_generate.restype = ctypes.c_int
         lib.synth_generate.argtypes = [
             ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,

@@ -14,7 +14,10 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssta.so")
+# SSTA_LIB may name another build of the same library (e.g. one with an
+# instrumented host half for sanitizer runs).
+_LIB_PATH = os.environ.get("SSTA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                       "libssta.so")
 
 SSTA_OK = 0
 STATUS_NAMES = {0: "SSTA_OK", -1: "SSTA_ERR_ARG", -2: "SSTA_ERR_SHAPE", -3: "SSTA_ERR_ALIGN",

@@ -44,27 +44,41 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str, extra: list) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+def _host_only(flags) -> list:
+    """Each flag for the host compilation only (device code is built as usual)."""
+    out = []
+    for f in flags:
+        out += ["-Xarch_host", f]
+    return out
+
+
+def _compile(src: str, extra: list, build_dir: str = BUILD, host_flags=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *COMMON, *extra, *_host_only(host_flags), "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
     return obj
 
 
-def build(jobs: int = 8) -> str:
-    """Compile every HIP source for gfx950 and link libssta.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int = 8, lib: str = LIB, build_dir: str = BUILD, host_flags=()) -> str:
+    """Compile every HIP source for gfx950 and link libssta.so; returns its path.
+
+    ``lib``, ``build_dir`` and ``host_flags`` (applied to the host compilation
+    only, e.g. for an instrumented host build) default to the in-tree library.
+    """
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda kv: _compile(*kv), SOURCES.items()))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda kv: _compile(kv[0], kv[1], build_dir, host_flags),
+                           SOURCES.items()))
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
