@@ -39,41 +39,46 @@ struct Geo {
 // the head's blocks in a visiting order.  The text part is padded to a
 // multiple of 8 workgroups so every slice keeps its XCD (the hardware deals
 // workgroup ids round-robin over the 8 XCDs).  The visiting order is the
-// block ids themselves, or, with 64-token blocks, each frame row of blocks
-// walked in spatial tiles of ty x tx blocks (row-major over the tiles, then
-// inside each tile), so that the workgroups an XCD runs at once cover a
-// compact patch whose windows share more key blocks in its L2.
+// block ids themselves, or, with 64-token blocks, groups of tt frame rows of
+// blocks, each walked in tiles of tt x ty x tx blocks (row-major over the
+// tiles, then inside each tile in (t, y, x) order), so that the workgroups
+// an XCD runs at once cover a compact 3D patch whose windows share more key
+// blocks in its L2.
 struct AttnGrid {
   int64_t text_wgs;   // workgroups of the text blocks (multiple of 8)
   int64_t slice;      // clip blocks per XCD per head
   int64_t blocks;     // total workgroups
-  int32_t ty, tx;     // spatial tile of the visiting order (0: block id order)
+  int32_t tt, ty, tx; // tile of the visiting order (tx = 0: block id order)
 };
 inline AttnGrid attn_grid(const Geo& g) {
   AttnGrid a;
   a.text_wgs = (g.bh * g.n_txt + 7) / 8 * 8;
   a.slice = (g.n_tiles + 7) / 8;
   a.blocks = a.text_wgs + g.bh * a.slice * 8;
-  a.ty = a.tx = 0;
+  a.tt = a.ty = a.tx = 0;
   if (g.R == kSmallTile) {
-    a.ty = g.ny < 4 ? g.ny : 4;
-    a.tx = g.nx < 4 ? g.nx : 4;
+    a.tt = g.nt < 4 ? g.nt : 4;
+    a.ty = g.ny < 2 ? g.ny : 2;
+    a.tx = g.nx < 2 ? g.nx : 2;
   }
   return a;
 }
 // Block at position pos of the visiting order (a bijection on [0, n_tiles)):
-// frame row t = pos / (ny*nx); in it, rows of tiles ty high (the last one
-// possibly lower), tiles tx wide (the last one possibly narrower).
+// frame-row group f = pos / (tt*ny*nx) of ht rows (the last group possibly
+// fewer); in it, rows of tiles ty high (the last possibly lower), tiles tx
+// wide (the last possibly narrower), each tile in (t, y, x) order.
 __device__ __forceinline__ int64_t visit_block(const Geo& g, const AttnGrid& a, int64_t pos) {
   if (a.tx == 0) return pos;
   const int64_t nyx = (int64_t)g.ny * g.nx;
-  const int64_t t = pos / nyx, r = pos - t * nyx;
-  const int64_t row = r / ((int64_t)a.ty * g.nx), rr = r - row * a.ty * g.nx;
-  const int64_t h = min((int64_t)a.ty, g.ny - row * a.ty);
-  const int64_t col = rr / (h * a.tx), off = rr - col * h * a.tx;
-  const int64_t w = min((int64_t)a.tx, g.nx - col * a.tx);
-  const int64_t yi = off / w, xi = off - yi * w;
-  return t * nyx + (row * a.ty + yi) * g.nx + col * a.tx + xi;
+  const int64_t f = pos / (a.tt * nyx), r = pos - f * a.tt * nyx;
+  const int64_t ht = min((int64_t)a.tt, g.nt - f * a.tt);
+  const int64_t row = r / (ht * a.ty * g.nx), rr = r - row * ht * a.ty * g.nx;
+  const int64_t hy = min((int64_t)a.ty, g.ny - row * a.ty);
+  const int64_t col = rr / (ht * hy * a.tx), off = rr - col * ht * hy * a.tx;
+  const int64_t wx = min((int64_t)a.tx, g.nx - col * a.tx);
+  const int64_t ti = off / (hy * wx), rem = off - ti * hy * wx;
+  const int64_t yi = rem / wx, xi = rem - yi * wx;
+  return (f * a.tt + ti) * nyx + (row * a.ty + yi) * g.nx + col * a.tx + xi;
 }
 // (batch*head, block) of workgroup bid; false for the padding workgroups.
 // kText = false: the instance for sequences without text (text_wgs == 0).
