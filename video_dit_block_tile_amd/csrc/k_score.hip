@@ -22,9 +22,8 @@
 // so the key-key products are evaluated once per pair of 128-block groups
 // (the upper triangle of tiles): a tile's column sums give the partials of
 // its column group and its row sums those of its row group.  Score_i is
-// never stored on the selection path: each workgroup scores 16 query rows
-// against every key block, keeps each row's scores as order keys in
-// registers and selects the row's top-k there.
+// written once as an [n][n] matrix (128 x 128 tiles) and read back once by
+// the per-row top-k, one wave per row.
 // Work per (batch, head): n(n+1)/2 * 128 FMAs for the key-key products
 // (about half of n^2 * 128) and n^2 * 128 for Score_s; bound by the fp32
 // vector ALU, not by HBM.
@@ -34,8 +33,6 @@
 
 namespace ssta {
 namespace {
-
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 // ------------------------------------------------------------------ normalise
 
@@ -438,7 +435,7 @@ __global__ __launch_bounds__(256) void k_topk(Geo g, const float* __restrict__ s
       uint32_t L = 0u;
       for (int b = 31; b >= 0; --b) {
         const uint32_t cand = L | (1u << b);
-        if (__popcll(__ballot(lm >= cand)) >= want) L = cand;
+        if ((int)__popcll(__ballot(lm >= cand)) >= want) L = cand;
       }
       if (L != 0u) {
         int base = 0;
