@@ -372,19 +372,33 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
   int ibase = 0;
   const int last_tile = (int)g.n_tiles - 1;
   int ids = (!all_blocks && lane < listed) ? idx[lane] : 0;
+  // On a ragged grid, which of the 64 entries are whole blocks (one vector
+  // test per 64 entries instead of a scalar one per unit).
+  auto whole = [&]() -> uint64_t {
+    if (!kGen || all_blocks || !g.ragged) return 0ull;
+    const uint32_t j = (uint32_t)min(max(ids, 0), last_tile);
+    return __ballot(ibase + lane < listed && block_extent(g, j).full);
+  };
+  uint64_t whole_m = whole();
   auto block_at = [&](int pos) -> int64_t {
     if (all_blocks) return pos;
     if (kGen && pos >= listed) return g.n_tiles + (pos - listed);   // a text block
     if (pos >= ibase + 64) {   // uniform: next 64 entries
       ibase += 64;
       ids = (ibase + lane < listed) ? idx[ibase + lane] : 0;
+      whole_m = whole();
     }
     return min(max(__builtin_amdgcn_readlane(ids, pos - ibase), 0), last_tile);
+  };
+  // positions of unit p of the block at list position pos (after block_at)
+  auto valid_at = [&](int pos, int64_t j, int p) -> uint64_t {
+    if (kGen && !all_blocks && pos < listed && ((whole_m >> (pos - ibase)) & 1u)) return ~0ull;
+    return unit_valid<kGen, kR>(g, j, p, lane);
   };
   uint64_t valid_next = ~0ull;   // positions of the unit loaded last that exist
   if (units > 0) {
     const int64_t j = block_at(0);
-    valid_next = unit_valid<kGen, kR>(g, j, 0, lane);
+    valid_next = valid_at(0, j, 0);
     dma_rows<kTok, kGen, kR, false>(smem, krs, g, j, 0, wv, lane, valid_next, doff.k);
     if (kTok)
       dma_rows<kTok, kGen, kR, true>(smem + 2 * kSlotBytes, vrs, g, j, 0, wv, lane, valid_next,
@@ -401,7 +415,7 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
     if (u + 1 < units) {
       const int64_t j = block_at((u + 1) / kUnits);
       const int p = (u + 1) % kUnits;
-      valid_next = unit_valid<kGen, kR>(g, j, p, lane);
+      valid_next = valid_at((u + 1) / kUnits, j, p);
       dma_rows<kTok, kGen, kR, false>(smem + (1 - slot) * kSlotBytes, krs, g, j, p, wv, lane,
                                       valid_next, doff.k);
       if (kTok)
