@@ -5,7 +5,9 @@
 // the kept key blocks only, then the weighted sum of their values.
 //
 // gfx950 design.  One workgroup (4 waves) per query block of 128 tokens;
-// each wave owns 32 queries.  The kernel computes the transposed scores
+// each wave owns 32 queries (64-token blocks: two waves per 32 queries, each
+// taking one 32-key half of every unit; see Blk).  The kernel computes the
+// transposed scores
 // S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the
 // wave's Q^T held in registers for the whole row), so each lane ends up with
 // one query's scores for 64 of the 128 keys of a block and the row softmax
@@ -23,7 +25,9 @@
 // chunk ^ (row/2)%8) so the MFMA operand reads are conflict-free.
 // Schedule: the hardware deals workgroup ids round-robin over the 8 XCDs.
 // The grid is laid out so that XCD x receives, head after head, the
-// contiguous slice [x*c, (x+1)*c) of that head's query blocks (c = ceil(n/8)).
+// contiguous slice [x*c, (x+1)*c) of that head's query blocks (c = ceil(n/8))
+// in a visiting order (block ids; 3D tiles of blocks for 64-token grids, see
+// AttnGrid).
 // All XCDs therefore work on the same one or two heads at any time, whose K
 // and V (118 MB per head at the 720p 10 s shape) stay resident in the 256 MB
 // MALL, while within an XCD neighbouring query blocks share most of their
