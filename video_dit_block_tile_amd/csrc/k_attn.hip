@@ -245,6 +245,34 @@ __device__ __forceinline__ void dma_rows(uint8_t* dst, __amdgpu_buffer_rsrc_t rs
   }
 }
 
+// Unit p of block j from token-major K and V.  The common case, a clip
+// block whose unit has every position, takes one straight path shared with
+// the instance without partial blocks (one uniform test), so its set-up stays
+// short between the barrier and the unit's products; text blocks and units
+// with missing positions take the general path of dma_rows.
+template <bool kGen, int kR>
+__device__ __forceinline__ void dma_unit_tok(uint8_t* dk, uint8_t* dv, __amdgpu_buffer_rsrc_t krs,
+                                             __amdgpu_buffer_rsrc_t vrs, const Geo& g, int64_t j,
+                                             int p, int wave, int lane, uint64_t valid,
+                                             const uint32_t* ok, const uint32_t* ov) {
+  constexpr int kL = Blk<kR>::kLoads;
+  if (!kGen || (j < g.n_tiles && valid == ~0ull)) {
+    const uint32_t so =
+        block_origin32(g, (uint32_t)j) * 256u + (p ? in_block_offset(g, 64) * 256u : 0u);
+#pragma unroll
+    for (int mm = 0; mm < kL; ++mm)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_u8*)(dk + (kL * wave + mm) * 1024), 16,
+                                               ok[mm], so, 0, 0);
+#pragma unroll
+    for (int mm = 0; mm < kL; ++mm)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_u8*)(dv + (kL * wave + mm) * 1024), 16,
+                                               ov[mm], so, 0, 0);
+    return;
+  }
+  dma_rows<true, kGen, kR, false>(dk, krs, g, j, p, wave, lane, valid, ok);
+  dma_rows<true, kGen, kR, true>(dv, vrs, g, j, p, wave, lane, valid, ov);
+}
+
 // Which of positions 64p .. 64p+63 of block j exist: all of them unless the
 // block is an edge block of a ragged grid or the last, partial text block.
 template <bool kGen, int kR>
@@ -403,12 +431,13 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
   if (units > 0) {
     const int64_t j = block_at(0);
     valid_next = valid_at(0, j, 0);
-    dma_rows<kTok, kGen, kR, false>(smem, krs, g, j, 0, wv, lane, valid_next, doff.k);
-    if (kTok)
-      dma_rows<kTok, kGen, kR, true>(smem + 2 * kSlotBytes, vrs, g, j, 0, wv, lane, valid_next,
-                                     doff.v);
-    else
+    if (kTok) {
+      dma_unit_tok<kGen, kR>(smem, smem + 2 * kSlotBytes, krs, vrs, g, j, 0, wv, lane,
+                             valid_next, doff.k, doff.v);
+    } else {
+      dma_rows<kTok, kGen, kR, false>(smem, krs, g, j, 0, wv, lane, valid_next, doff.k);
       dma_v<kR>(smem + 2 * kSlotBytes, vrs, j, 0, wv, doff.v);
+    }
   }
 
   for (int u = 0; u < units; ++u) {
@@ -420,13 +449,14 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
       const int64_t j = block_at((u + 1) / kUnits);
       const int p = (u + 1) % kUnits;
       valid_next = valid_at((u + 1) / kUnits, j, p);
-      dma_rows<kTok, kGen, kR, false>(smem + (1 - slot) * kSlotBytes, krs, g, j, p, wv, lane,
-                                      valid_next, doff.k);
-      if (kTok)
-        dma_rows<kTok, kGen, kR, true>(smem + (3 - slot) * kSlotBytes, vrs, g, j, p, wv, lane,
-                                       valid_next, doff.v);
-      else
+      if (kTok) {
+        dma_unit_tok<kGen, kR>(smem + (1 - slot) * kSlotBytes, smem + (3 - slot) * kSlotBytes,
+                               krs, vrs, g, j, p, wv, lane, valid_next, doff.k, doff.v);
+      } else {
+        dma_rows<kTok, kGen, kR, false>(smem + (1 - slot) * kSlotBytes, krs, g, j, p, wv, lane,
+                                        valid_next, doff.k);
         dma_v<kR>(smem + (3 - slot) * kSlotBytes, vrs, j, p, wv, doff.v);
+      }
     }
     const uint8_t* sK = smem + slot * kSlotBytes;
     const uint8_t* sV = smem + (2 + slot) * kSlotBytes;
