@@ -157,8 +157,18 @@ __device__ __forceinline__ void dma_rows(uint8_t* dst, __amdgpu_buffer_rsrc_t rs
                                          int lane, uint32_t valid,
                                          const UnitOffsets<kR, kW>& off) {
   constexpr int kL = UnitOffsets<kR, kW>::kLoads;
-  const bool part = kGen && valid != ~0u;
-  const bool text = kGen && j >= g.n_tiles;
+  if (!kGen || (j < g.n_tiles && valid == ~0u)) {
+    // a clip block's unit with every row: one straight path, the same in both
+    // instances (the general one below handles text blocks and missing rows)
+    const uint32_t so = clip_origin * 256u + in_block_offset(g, 32 * p) * 256u;
+#pragma unroll
+    for (int mm = 0; mm < kL; ++mm)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8*)(dst + (kL * wave + mm) * 1024), 16,
+                                               off.rows[mm], so, 0, 0);
+    return;
+  }
+  const bool part = valid != ~0u;
+  const bool text = j >= g.n_tiles;
   const uint32_t origin = text ? (uint32_t)(g.N + (j - g.n_tiles) * kR) : clip_origin;
   const uint32_t half = (text ? 32u * p : in_block_offset(g, 32 * p)) * 256u;
   const uint32_t so = origin * 256u + (part ? 0u : half);
@@ -332,10 +342,14 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, AttnGrid grid) {
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * ks + e;
         const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
-        float ds = pr * (dp[r] - dq_d);
-        if (kGen && !((valid >> (16 * ks + 8 * hl + e)) & 1u)) ds = 0.0f;
-        dsf[ks][e] = (__bf16)ds;
+        dsf[ks][e] = (__bf16)(pr * (dp[r] - dq_d));
       }
+    if (kGen && valid != ~0u)   // uniform: only units with missing keys
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (!((valid >> (16 * ks + 8 * hl + e)) & 1u)) dsf[ks][e] = (__bf16)0.0f;
     // dQ^T += K^T dS^T: A operand row d of K^T, the same 8 keys, read
     // transposed from the K rows.
 #pragma unroll
@@ -508,11 +522,17 @@ void k_attn_bwd_dkdv(Geo g, BwdArgs a, AttnGrid grid) {
       for (int r = 0; r < 16; ++r) {
         const int ks = r >> 3, e = r & 7;
         const f32x4 l2 = lv[4 * ks + (e >> 1)];
-        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c, -l2[(e & 1) * 2]));
-        if (kGen && !((valid >> (16 * ks + 8 * hl + e)) & 1u)) pr = 0.0f;
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c, -l2[(e & 1) * 2]));
         pv[r >> 2][r & 3] = pr;
         bo[ks][e] = (__bf16)pr;
       }
+      if (kGen && valid != ~0u)   // uniform: only units with missing queries
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!((valid >> (16 * (r >> 3) + 8 * hl + (r & 7))) & 1u)) {
+            pv[r >> 2][r & 3] = 0.0f;
+            bo[r >> 3][r & 7] = (__bf16)0.0f;
+          }
       f32x4* pb = pbuf(w);
 #pragma unroll
       for (int x = 0; x < 4; ++x) pb[64 * x] = pv[x];
@@ -526,10 +546,12 @@ void k_attn_bwd_dkdv(Geo g, BwdArgs a, AttnGrid grid) {
       for (int r = 0; r < 16; ++r) {
         const int ks = r >> 3, e = r & 7;
         const f32x4 l2 = lv[4 * ks + (e >> 1)];
-        float ds = pv[r >> 2][r & 3] * (sc[r] - l2[(e & 1) * 2 + 1]);
-        if (kGen && !((valid >> (16 * ks + 8 * hl + e)) & 1u)) ds = 0.0f;
-        bo[ks][e] = (__bf16)ds;
+        bo[ks][e] = (__bf16)(pv[r >> 2][r & 3] * (sc[r] - l2[(e & 1) * 2 + 1]));
       }
+      if (kGen && valid != ~0u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!((valid >> (16 * (r >> 3) + 8 * hl + (r & 7))) & 1u)) bo[r >> 3][r & 7] = (__bf16)0.0f;
     }
     // dV^T += dO^T P (V wave) or dK^T += Q^T dS (K wave): A operand row d of
     // the same 8 queries, read transposed from the dO or Q rows.
