@@ -190,33 +190,48 @@ __device__ __forceinline__ int64_t row_token(const Geo& g, int64_t j, int r, boo
   return block_first_token(g, (uint32_t)j) + (exists ? in_block_offset(g, r) : 0u);
 }
 
-// Kept-block ids of one list, 64 at a time (lane i holds entry base + i, or
-// block base + i for a dense list), with the first token of each such clip
-// block, so that a unit's gather base is a v_readlane rather than a scalar
-// division; positions are requested in non-decreasing order.
+// The blocks a row runs over, 64 at a time: lane i holds list position
+// base + i, which is the caller's id (clamped to the clip's blocks) below
+// `listed` and, in the kGen instance, text block n_tiles + (pos - listed)
+// after it; in a dense list position i is block i.  With each id the first
+// token of the block (clip blocks) and, in the kGen instance, a ballot of
+// which of the 64 are clip blocks holding every position, so that a unit's
+// set-up is two v_readlane and a bit test; positions are requested in
+// non-decreasing order.
+template <bool kGen>
 struct IdStream {
   const int32_t* idx;
-  int cnt, base, ids;
+  int listed, base, ids;
   uint32_t org;
+  uint64_t whole;
   bool dense;
   __device__ __forceinline__ void fill(const Geo& g, int lane) {
     const int pos = base + lane;
+    const int last = (int)g.n_tiles - 1;
     // a caller's id outside the clip's blocks is clamped to one, so a
     // malformed list reads only the head's own blocks
-    ids = dense ? pos : (pos < cnt ? min(max(idx[pos], 0), (int)g.n_tiles - 1) : 0);
-    org = block_origin32(g, (uint32_t)min(ids, (int)g.n_tiles - 1));
+    ids = dense ? pos
+                : (pos < listed ? min(max(idx[pos], 0), last)
+                                : (kGen ? (int)g.n_tiles + (pos - listed) : 0));
+    org = block_origin32(g, (uint32_t)min(ids, last));
+    if (kGen)
+      whole = __ballot(ids <= last &&
+                       (!g.ragged || block_extent(g, (uint32_t)min(ids, last)).full));
   }
-  __device__ __forceinline__ void init(const Geo& g, const int32_t* p, int c, bool d, int lane) {
-    idx = p; cnt = c; dense = d; base = 0;
+  __device__ __forceinline__ void init(const Geo& g, const int32_t* p, int n, bool d, int lane) {
+    idx = p; listed = n; dense = d; base = 0;
     fill(g, lane);
   }
-  // block at list position pos; origin: its first token (clip blocks)
-  __device__ __forceinline__ uint32_t at(const Geo& g, int pos, int lane, uint32_t& origin) {
+  // block at list position pos; origin: its first token (clip blocks);
+  // full: a clip block with every position (always, outside kGen)
+  __device__ __forceinline__ uint32_t at(const Geo& g, int pos, int lane, uint32_t& origin,
+                                         bool& full) {
     if (pos >= base + 64) {
       base += 64;
       fill(g, lane);
     }
     origin = (uint32_t)__builtin_amdgcn_readlane((int)org, pos - base);
+    full = !kGen || ((whole >> (pos - base)) & 1u);
     return dense ? (uint32_t)pos : (uint32_t)__builtin_amdgcn_readlane(ids, pos - base);
   }
 };
@@ -285,7 +300,7 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, AttnGrid grid) {
   const int64_t kvrow = bh * g.n_tiles + qi;
   const int listed = all_blocks ? 0 : min(max(a.kv_cnt[kvrow], 0), a.max_kept);
   const int cnt = all_blocks ? (int)g.n_rows : listed + (kGen ? g.n_txt : 0);
-  IdStream ids;
+  IdStream<kGen> ids;
   ids.init(g, all_blocks ? nullptr : a.kv_idx + kvrow * a.max_kept, listed, all_blocks, lane);
   const UnitOffsets<kR> off = unit_offsets<kR>(g, wv, lane);
   const int tb = row_t_base(lane);
@@ -297,13 +312,11 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, AttnGrid grid) {
                                           tok_bytes);
   // returns which of the unit's 32 keys exist
   auto load_unit = [&](int u, uint8_t* dst) -> uint32_t {
-    const int pos = u / kUnits;
-    uint32_t org = 0;
-    const uint32_t j = kGen && pos >= listed && !all_blocks
-                           ? (uint32_t)(g.n_tiles + pos - listed)
-                           : ids.at(g, pos, lane, org);
+    uint32_t org;
+    bool full;
+    const uint32_t j = ids.at(g, u / kUnits, lane, org, full);
     const int p = u % kUnits;
-    const uint32_t valid = rows_valid<kGen, kR>(g, j, p, lane);
+    const uint32_t valid = full ? ~0u : rows_valid<kGen, kR>(g, j, p, lane);
     dma_rows<kGen, kR>(dst, krs, g, j, org, p, wv, lane, valid, off);
     dma_rows<kGen, kR>(dst + kUnitBytes, vrs, g, j, org, p, wv, lane, valid, off);
     return valid;
@@ -439,7 +452,7 @@ void k_attn_bwd_dkdv(Geo g, BwdArgs a, AttnGrid grid) {
   const int64_t klist = bh * g.n_tiles + kj;
   const int listed = all_blocks ? 0 : a.q_cnt[klist];
   const int cnt = all_blocks ? (int)g.n_rows : listed + (kGen ? g.n_txt : 0);
-  IdStream ids;
+  IdStream<kGen> ids;
   ids.init(g, all_blocks ? nullptr : a.q_idx + klist * a.q_width, listed, all_blocks, lane);
   const UnitOffsets<kR, Sh::kWaves> off = unit_offsets<kR, Sh::kWaves>(g, wv, lane);
   const int tb = row_t_base(lane);
@@ -452,13 +465,11 @@ void k_attn_bwd_dkdv(Geo g, BwdArgs a, AttnGrid grid) {
       rsrc(a.ld + bh * g.n_rows * kR * 2, g.n_rows * kR * 8);
   // returns which of the unit's 32 queries exist
   auto load_unit = [&](int u, uint8_t* dst) -> uint32_t {
-    const int pos = u / kUnits;
-    uint32_t org = 0;
-    const uint32_t i = kGen && pos >= listed && !all_blocks
-                           ? (uint32_t)(g.n_tiles + pos - listed)
-                           : ids.at(g, pos, lane, org);
+    uint32_t org;
+    bool full;
+    const uint32_t i = ids.at(g, u / kUnits, lane, org, full);
     const int p = u % kUnits;
-    const uint32_t valid = rows_valid<kGen, kR>(g, i, p, lane);
+    const uint32_t valid = full ? ~0u : rows_valid<kGen, kR>(g, i, p, lane);
     dma_rows<kGen, kR, Sh::kWaves>(dst, qrs, g, i, org, p, wv, lane, valid, off);
     dma_rows<kGen, kR, Sh::kWaves>(dst + kUnitBytes, drs, g, i, org, p, wv, lane, valid, off);
     if (wv == 0 && lane < 16)   // 32 (lse2, D) pairs = 256 B
