@@ -29,7 +29,7 @@
 // come from the same token rows in LDS through the transposing reads
 // (ds_read_b64_tr_b16), so nothing is copied to a dim-major layout first.
 // Both kernels run two waves per SIMD.  Every streamed unit (token rows
-// gathered from token-major memory and the per-query (lse*log2 e, D) pairs)
+// gathered from token-major memory and the per-query lse*log2 e and D values)
 // goes straight into LDS with buffer_load_dwordx4 ... lds into a ring of
 // slots (two in k_attn_bwd_dq, three in k_attn_bwd_dkdv), as in the forward
 // kernel.
@@ -103,6 +103,13 @@ __device__ __forceinline__ bf16x8 row_t_operand(const uint8_t* unit, int tb, int
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(unit + o0));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(unit + o1));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// (lse * log2 e, D) of query r of block row `row` (R queries per block):
+// each group of 32 queries holds their 32 lse values, then their 32 D values,
+// so a dK/dV wave reads only the half it uses.
+__device__ __forceinline__ int64_t ld_index(int64_t row, int r, int R) {
+  return row * 2 * R + (r >> 5) * 64 + (r & 31);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
@@ -284,8 +291,8 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, AttnGrid grid) {
   bf16x8 qf[8], df[8];
   load_row_operand(qf, static_cast<const uint16_t*>(a.q) + qtok * kHeadDim, hl);
   load_row_operand(df, static_cast<const uint16_t*>(a.dout) + qtok * kHeadDim, hl);
-  const float lse2 = a.ld[(row * kR + qrow) * 2];
-  const float dq_d = a.ld[(row * kR + qrow) * 2 + 1];
+  const float lse2 = a.ld[ld_index(row, qrow, kR)];
+  const float dq_d = a.ld[ld_index(row, qrow, kR) + 32];
   const float c = a.scale_log2;
 
   f32x16 acc[4];
@@ -388,14 +395,14 @@ void k_attn_bwd_dq(Geo g, BwdArgs a, AttnGrid grid) {
 // Each wave thus needs one accumulator and one operand block, so two waves
 // share a SIMD, and each does 16 of the 32 products of a unit.  Iteration u:
 // the V waves take unit u, the K waves unit u-1, and unit u+1 is loading:
-// three slots of Q rows, dO rows and the units' (lse*log2 e, D) pairs, plus
+// three slots of Q rows, dO rows and the units' lse*log2 e and D values, plus
 // two P buffers.  The arithmetic (products, their order, the roundings) is
 // the same as one wave doing both, so the gradients are too.
 template <int kR>
 struct DkdvShape {
   static constexpr int kGroups = kR / 32;             // 32-key groups per block
   static constexpr int kWaves = 2 * kGroups;
-  static constexpr int kSlot = 2 * kUnitBytes + 256;  // Q rows | dO rows | 32 pairs
+  static constexpr int kSlot = 2 * kUnitBytes + 256;  // Q rows | dO rows | 32 lse2 | 32 D
   static constexpr int kPBuf = kGroups * 64 * 64;     // 16 fp32 per lane per group
   static constexpr int kLds = 3 * kSlot + 2 * kPBuf;
 };
@@ -472,7 +479,7 @@ void k_attn_bwd_dkdv(Geo g, BwdArgs a, AttnGrid grid) {
     const uint32_t valid = full ? ~0u : rows_valid<kGen, kR>(g, i, p, lane);
     dma_rows<kGen, kR, Sh::kWaves>(dst, qrs, g, i, org, p, wv, lane, valid, off);
     dma_rows<kGen, kR, Sh::kWaves>(dst + kUnitBytes, drs, g, i, org, p, wv, lane, valid, off);
-    if (wv == 0 && lane < 16)   // 32 (lse2, D) pairs = 256 B
+    if (wv == 0 && lane < 16)   // the unit's 32 lse2 and 32 D values = 256 B
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           lrs, (lds_u8*)(dst + 2 * kUnitBytes), 16, (uint32_t)lane * 16,
           (i * (uint32_t)kR + 32u * p) * 8u, 0, 0);
@@ -516,13 +523,15 @@ void k_attn_bwd_dkdv(Geo g, BwdArgs a, AttnGrid grid) {
       const int n = st + kAhead;
       if (n < 8) ra[st % kAhead] = *reinterpret_cast<const bf16x8*>(sA + swz_row(kperm, 2 * n + hl));
     }
-    // (lse2, D) of the lane's 16 queries 16*ks + 8*hl + e, in pairs
-    const f32x4* sL = reinterpret_cast<const f32x4*>(sQ + 2 * kUnitBytes);
-    f32x4 lv[8];
+    // lse2 (V wave) or D (K wave) of the lane's 16 queries 16*ks + 8*hl + e:
+    // lv[2*ks + e/4][e%4], from the unit's 32 lse2 values or the 32 D values
+    // after them
+    const f32x4* sL = reinterpret_cast<const f32x4*>(sQ + 2 * kUnitBytes) + (vwave ? 0 : 8);
+    f32x4 lv[4];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int x = 0; x < 4; ++x) lv[4 * ks + x] = sL[(16 * ks + 8 * hl) / 2 + x];
+      for (int x = 0; x < 2; ++x) lv[2 * ks + x] = sL[4 * ks + 2 * hl + x];
     const uint32_t valid = vwave ? v_cur : v_prev;
     bf16x8 bo[2];   // P (V wave) or dS (K wave) as the B operand of k-step ks
     if (vwave) {
@@ -532,8 +541,8 @@ void k_attn_bwd_dkdv(Geo g, BwdArgs a, AttnGrid grid) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ks = r >> 3, e = r & 7;
-        const f32x4 l2 = lv[4 * ks + (e >> 1)];
-        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c, -l2[(e & 1) * 2]));
+        const float pr =
+            __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c, -lv[2 * ks + (e >> 2)][e & 3]));
         pv[r >> 2][r & 3] = pr;
         bo[ks][e] = (__bf16)pr;
       }
@@ -556,8 +565,7 @@ void k_attn_bwd_dkdv(Geo g, BwdArgs a, AttnGrid grid) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ks = r >> 3, e = r & 7;
-        const f32x4 l2 = lv[4 * ks + (e >> 1)];
-        bo[ks][e] = (__bf16)(pv[r >> 2][r & 3] * (sc[r] - l2[(e & 1) * 2 + 1]));
+        bo[ks][e] = (__bf16)(pv[r >> 2][r & 3] * (sc[r] - lv[2 * ks + (e >> 2)][e & 3]));
       }
       if (kGen && valid != ~0u)
 #pragma unroll
@@ -598,9 +606,8 @@ __global__ __launch_bounds__(256) void k_attn_bwd_prep(Geo g, const uint16_t* __
       text ? (tile - g.n_tiles) * g.R + r < g.L : (ext.full || pos_exists(g, ext, r));
   if (!exists) {
     if (half == 0) {
-      const int64_t qi = blk * g.R + r;
-      ld[qi * 2] = lse[blk * g.R] * kLog2e;
-      ld[qi * 2 + 1] = 0.0f;
+      ld[ld_index(blk, r, g.R)] = lse[blk * g.R] * kLog2e;
+      ld[ld_index(blk, r, g.R) + 32] = 0.0f;
     }
     return;
   }
@@ -619,9 +626,8 @@ __global__ __launch_bounds__(256) void k_attn_bwd_prep(Geo g, const uint16_t* __
   }
   acc += __shfl_xor(acc, 1);
   if (half == 0) {
-    const int64_t qi = blk * g.R + r;
-    ld[qi * 2] = lse[qi] * kLog2e;
-    ld[qi * 2 + 1] = acc;
+    ld[ld_index(blk, r, g.R)] = lse[blk * g.R + r] * kLog2e;
+    ld[ld_index(blk, r, g.R) + 32] = acc;
   }
 }
 
