@@ -203,6 +203,28 @@ def test_dense_equals_all_kept():
     assert torch.equal(sparse.lse, dense.lse)
 
 
+def test_t64_dense_equals_all_kept():
+    """64-token blocks with top-k covering every block: the sparse run over
+    full kept lists, the dense run (no lists) and the oracle's dense attention
+    agree -- bit for bit between the two runs, within the bars against the
+    oracle on every row."""
+    base = si.ALL["t64-grid"]
+    wl = base.with_(name="t64-grid-all", topk=base.n_tiles)
+    q, k, v = si.make_qkv(wl)
+    sel = oracle.select(wl, q, k)
+    assert np.all(sel["kv_cnt"] == wl.n_tiles)
+    sparse = _plan(wl)
+    dense = _plan(wl, dense=True)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    sparse.run(qd, kd, vd)
+    dense.run(qd, kd, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(sparse.o, dense.o)
+    assert torch.equal(sparse.lse, dense.lse)
+    rows = np.arange(wl.batch * wl.heads * wl.n_rows, dtype=np.int64)
+    _check_attention(wl, q, k, v, sel, dense, rows)
+
+
 def test_deterministic():
     wl, q, k, v, sel = _case("dup-ties")
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
@@ -215,10 +237,10 @@ def test_deterministic():
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("name", ["grid32-w1-k2", "t64-grid"])
 @pytest.mark.parametrize("flags", [oracle.COMBINE_AND, oracle.TOPK_EXCLUDE_WINDOW,
                                    oracle.COMBINE_AND | oracle.TOPK_EXCLUDE_WINDOW])
-def test_flag_variants(flags):
-    name = "grid32-w1-k2"
+def test_flag_variants(name, flags):
     wl, q, k, v, sel = _case(name, flags)
     plan = _plan(wl, flags)
     plan.run(to_dev(q), to_dev(k), to_dev(v))
