@@ -46,8 +46,9 @@
 // and taken out with v_readlane, so no per-unit global load sits on the
 // critical path.
 // LDS operand reads are issued ahead of their products (up to 8 for K, the
-// first 8 V operands before the softmax), held in place by scheduling
-// fences; waves raise their issue priority around the matrix-core sections.
+// first 8 V operands before the softmax; with 64-token blocks from one asm
+// block, see v_operands_tile), held in place by scheduling fences; waves
+// raise their issue priority around the matrix-core sections.
 // Softmax: the running max m is raised only when the probabilities formed
 // with the current m would exceed 2^32 on some lane (always on a row's first
 // unit), so most units need neither a max reduction nor an O rescale; the
@@ -142,6 +143,52 @@ __device__ __forceinline__ bf16x8 v_operand(const uint8_t* sV, int t, int ks, in
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 1024));
   const auto w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, w);
+}
+
+// The 8 V operands of one 32-key tile t of a token-major V slot (operand i:
+// ks = i/4, db = i%4, the addresses of v_operand), read by one asm block that
+// waits for its own reads before it ends.  With the builtin the compiler,
+// which cannot tell a transposing read's LDS address from the target of the
+// next unit's direct loads, first waits for those loads to land (vmcnt(0));
+// the slot read here is never a load target while it is read.  Used by the
+// 64-token instance, whose waves run only 8 products between the unit's
+// barrier and these reads, so the drain cost it 3% of its time; with 128-token
+// blocks the same drain measured as free.
+__device__ __forceinline__ void v_operands_tile(const uint8_t* sV, int t, int vofs, bf16x8* vr) {
+  uint32_t b[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    b[db] = (uint32_t)(uintptr_t)(const lds_u8*)(sV + (vofs ^ (db << 6)) + 32 * t * 256);
+  long r[16];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %2, %17\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %4, %18\n\t"
+      "ds_read_b64_tr_b16 %5, %18 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %6, %19\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %9, %16 offset:5120\n\t"
+      "ds_read_b64_tr_b16 %10, %17 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %11, %17 offset:5120\n\t"
+      "ds_read_b64_tr_b16 %12, %18 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %13, %18 offset:5120\n\t"
+      "ds_read_b64_tr_b16 %14, %19 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %15, %19 offset:5120\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
+        "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+      : "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3])
+      : "memory");
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const s16x4 lo = __builtin_bit_cast(s16x4, r[2 * i]);
+    const s16x4 hi = __builtin_bit_cast(s16x4, r[2 * i + 1]);
+    vr[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
 }
 
 __device__ __forceinline__ float max3f(float a, float b, float c) {
@@ -508,9 +555,13 @@ void k_attn_fwd(Geo g, AttnArgs a, AttnGrid grid) {
     constexpr int kVAhead = 8;
     constexpr int kVProducts = 8 * kT;
     bf16x8 vr[kVAhead];
+    if (kTok && kSplit) {
+      v_operands_tile(sV, tile(0), vofs, vr);
+    } else {
 #pragma unroll
-    for (int i = 0; i < kVAhead; ++i)
-      vr[i] = v_operand<kTok>(sV, tile(i >> 3), (i >> 2) & 1, i & 3, l32, hl, vofs);
+      for (int i = 0; i < kVAhead; ++i)
+        vr[i] = v_operand<kTok>(sV, tile(i >> 3), (i >> 2) & 1, i & 3, l32, hl, vofs);
+    }
 
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(kFenceKeepDs);
